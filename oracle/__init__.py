@@ -1,0 +1,193 @@
+"""Sequential CPU oracle for the device-wide prefix scan.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The GPU library never calls it, and
+the two share no code: the arithmetic lives in ``scan_oracle.c`` (plain C, one
+left-to-right loop per definition, float sums in double), loaded here through
+ctypes and wrapped for numpy arrays.
+
+Pages cited:
+  [L7]    "Lecture 7: 并行模式五 —— 前缀和 / 扫描：双缓冲与层次化算法"
+          (UIUC ECE408 course notes, runguoli.com)
+  [PMPP9] "第9章并行模式：前缀和 - Scan算法" (PMPP chapter 9 notes, bittern.cn)
+  [YLY]   "CUDA编程并行前缀和扫描详解" (tutorial, m.youleyou.com)
+
+Definitions: inclusive and exclusive scan [L7 concept 1; PMPP9 §9.1; YLY §2.1,
+§2.2]; identities [PMPP9 §9.1 identity table]; compaction by an exclusive scan
+of predicate flags [L7 concept 2; PMPP9 §9.6]; segmented scan [L7 concept 2,
+radix-sort remark].  Every function here has a pin in tests/test_oracle.py
+(worked examples printed on the pages, closed forms, invariants, brute force
+on tiny inputs and special cases that reduce to numpy routines).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "scan_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+OPS = {"add": 0, "max": 1, "min": 2}
+
+_lib = None
+
+
+def build() -> str:
+    """Compile scan_oracle.c with gcc into oracle/liboracle.so (always rebuilds)."""
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fPIC", "-shared",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    L = ctypes.c_int64
+    sigs = {
+        "oracle_scan_i32": [I, I, P, P, L],
+        "oracle_scan_u32": [I, I, P, P, L],
+        "oracle_scan_f32_add": [I, P, P, P, L],
+        "oracle_scan_f32_minmax": [I, I, P, P, L],
+        "oracle_scan_affine": [I, P, P, L],
+        "oracle_segscan_i32": [I, I, P, P, P, L],
+        "oracle_segscan_u32": [I, I, P, P, P, L],
+        "oracle_segscan_f32_add": [I, P, P, P, P, L],
+        "oracle_segscan_f32_minmax": [I, I, P, P, P, L],
+        "oracle_compact_i32": [P, P, P, L],
+        "oracle_compact_u32": [P, P, P, L],
+        "oracle_compact_f32": [P, P, P, L],
+    }
+    for name, argtypes in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = argtypes
+        fn.restype = L if name.startswith("oracle_compact") else None
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _contig(x: np.ndarray, dtype) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype != dtype:
+        raise TypeError("expected %s, got %s" % (np.dtype(dtype), x.dtype))
+    return np.ascontiguousarray(x)
+
+
+def scan(op: str, x: np.ndarray, exclusive: bool = False):
+    """Inclusive (default) or exclusive scan of a 1-D int32/uint32/float32 array.
+
+    Returns y in the input dtype, except for float32 add, which returns the
+    pair (y, s) of float64 arrays: y is the prefix sum accumulated in double
+    and s the prefix sum of |x| over the same range (the tolerance scale).
+    """
+    lib = _load()
+    x = np.asarray(x)
+    n = x.shape[0]
+    ex = 1 if exclusive else 0
+    if x.dtype == np.int32:
+        y = np.empty(n, np.int32)
+        lib.oracle_scan_i32(OPS[op], ex, _ptr(_contig(x, np.int32)), _ptr(y), n)
+        return y
+    if x.dtype == np.uint32:
+        y = np.empty(n, np.uint32)
+        lib.oracle_scan_u32(OPS[op], ex, _ptr(_contig(x, np.uint32)), _ptr(y), n)
+        return y
+    if x.dtype == np.float32:
+        xc = _contig(x, np.float32)
+        if op == "add":
+            y = np.empty(n, np.float64)
+            s = np.empty(n, np.float64)
+            lib.oracle_scan_f32_add(ex, _ptr(xc), _ptr(y), _ptr(s), n)
+            return y, s
+        y = np.empty(n, np.float32)
+        lib.oracle_scan_f32_minmax(OPS[op], ex, _ptr(xc), _ptr(y), n)
+        return y
+    raise TypeError("unsupported dtype %s" % x.dtype)
+
+
+def scan_affine(ab: np.ndarray, exclusive: bool = False) -> np.ndarray:
+    """Scan of affine maps; ab is an (n, 2) uint32 array of (a, b) pairs.
+
+    Element i of an inclusive result is the composition of maps 0..i, the
+    later map applied after the earlier: (a2,b2) o (a1,b1) = (a2*a1, a2*b1+b2)
+    mod 2^32.  Its b component is the recurrence y_i = a_i*y_{i-1} + b_i.
+    """
+    lib = _load()
+    ab = _contig(ab, np.uint32)
+    if ab.ndim != 2 or ab.shape[1] != 2:
+        raise ValueError("ab must have shape (n, 2)")
+    n = ab.shape[0]
+    y = np.empty((n, 2), np.uint32)
+    lib.oracle_scan_affine(1 if exclusive else 0, _ptr(ab), _ptr(y), n)
+    return y
+
+
+def segmented_scan(op: str, x: np.ndarray, heads: np.ndarray, exclusive: bool = False):
+    """Segmented scan; heads is a uint8 array, nonzero starts a segment.
+
+    Index 0 always starts a segment.  float32 add returns (y, s) in float64
+    as scan() does, with s restarted at every head.
+    """
+    lib = _load()
+    x = np.asarray(x)
+    n = x.shape[0]
+    h = _contig(heads, np.uint8)
+    if h.shape[0] != n:
+        raise ValueError("heads must have the length of x")
+    ex = 1 if exclusive else 0
+    if x.dtype == np.int32:
+        y = np.empty(n, np.int32)
+        lib.oracle_segscan_i32(OPS[op], ex, _ptr(_contig(x, np.int32)), _ptr(h), _ptr(y), n)
+        return y
+    if x.dtype == np.uint32:
+        y = np.empty(n, np.uint32)
+        lib.oracle_segscan_u32(OPS[op], ex, _ptr(_contig(x, np.uint32)), _ptr(h), _ptr(y), n)
+        return y
+    if x.dtype == np.float32:
+        xc = _contig(x, np.float32)
+        if op == "add":
+            y = np.empty(n, np.float64)
+            s = np.empty(n, np.float64)
+            lib.oracle_segscan_f32_add(ex, _ptr(xc), _ptr(h), _ptr(y), _ptr(s), n)
+            return y, s
+        y = np.empty(n, np.float32)
+        lib.oracle_segscan_f32_minmax(OPS[op], ex, _ptr(xc), _ptr(h), _ptr(y), n)
+        return y
+    raise TypeError("unsupported dtype %s" % x.dtype)
+
+
+def compact(x: np.ndarray):
+    """Order-preserving compaction of the elements x > 0.
+
+    Returns (out, count, pos): out holds the kept elements in input order,
+    count their number, pos the exclusive scan of the 0/1 predicate flags.
+    """
+    lib = _load()
+    x = np.asarray(x)
+    n = x.shape[0]
+    out = np.empty(n, x.dtype)
+    pos = np.empty(n, np.uint32)
+    fn = {np.dtype(np.int32): lib.oracle_compact_i32,
+          np.dtype(np.uint32): lib.oracle_compact_u32,
+          np.dtype(np.float32): lib.oracle_compact_f32}.get(x.dtype)
+    if fn is None:
+        raise TypeError("unsupported dtype %s" % x.dtype)
+    xc = np.ascontiguousarray(x)
+    count = int(fn(_ptr(xc), _ptr(out), _ptr(pos), n))
+    return out[:count].copy(), count, pos

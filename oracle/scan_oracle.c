@@ -1,0 +1,283 @@
+/*
+ * scan_oracle.c -- the plain, sequential CPU oracle for the device-wide
+ * prefix scan.  TEST INFRASTRUCTURE ONLY: it is built and called by the
+ * tests, by the smoke check and by the CPU-baseline leg of the benchmark,
+ * never by the GPU library, and it shares no code, header or table with it.
+ *
+ * Every routine is the textbook definition written out as one left-to-right
+ * loop: no blocking, no reordering, no parallelism.  Floating-point sums are
+ * accumulated in double.  Integers wrap modulo 2^32.
+ *
+ * Pages cited (by title and section):
+ *   [L7]    "Lecture 7: 并行模式五 —— 前缀和 / 扫描：双缓冲与层次化算法"
+ *           (UIUC ECE408 course notes, runguoli.com)
+ *   [YLY]   "CUDA编程并行前缀和扫描详解" (tutorial, m.youleyou.com)
+ *   [PMPP9] "第9章并行模式：前缀和 - Scan算法 (Parallel Patterns: Prefix Sum -
+ *           Scan Algorithms)" (PMPP chapter 9 notes, bittern.cn)
+ *
+ * Definitions followed:
+ *   inclusive  y[i] = x[0] (+) ... (+) x[i]
+ *              [L7 concept 1 "inclusive 与 exclusive"; PMPP9 §9.1; YLY §2.1]
+ *   exclusive  y[0] = identity, y[i] = x[0] (+) ... (+) x[i-1]
+ *              [L7 concept 1; PMPP9 §9.1; YLY §2.2]
+ *   The operator only has to be associative; the order of the operands is
+ *   kept, earlier element on the left [L7 concept 1, operator generalisation].
+ *   Identities: + -> 0, max -> -inf, min -> +inf [PMPP9 §9.1 identity table];
+ *   for 32-bit integers -inf/+inf read as the smallest/largest value of the
+ *   type, and the identity of the affine map is (a, b) = (1, 0).
+ *   A recurrence out[j] = out[j-1] (+) f(j) is a scan [L7 concept 1]; the
+ *   affine recurrence y_i = a_i * y_{i-1} + b_i composes maps
+ *   (a2,b2) o (a1,b1) = (a2*a1, a2*b1 + b2), applied after the earlier one.
+ *   Stream compaction keeps x > 0 in order, at the positions given by an
+ *   exclusive scan of the 0/1 flags [L7 concept 2 "扫描的典型应用";
+ *   PMPP9 §9.6 array compaction; YLY §2.2 flag/pos example].
+ *   Segmented scan restarts the fold at every head flag [L7 concept 2, radix
+ *   sort remark]; index 0 always starts a segment.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#define OP_ADD 0
+#define OP_MAX 1
+#define OP_MIN 2
+
+/* ------------------------------------------------------------------ */
+/* int32: add wraps modulo 2^32 (two's complement); max/min as usual.  */
+/* ------------------------------------------------------------------ */
+static int32_t i32_identity(int op)
+{
+    if (op == OP_MAX) return INT32_MIN;
+    if (op == OP_MIN) return INT32_MAX;
+    return 0;
+}
+
+static int32_t i32_combine(int op, int32_t earlier, int32_t later)
+{
+    if (op == OP_MAX) return (later > earlier) ? later : earlier;
+    if (op == OP_MIN) return (later < earlier) ? later : earlier;
+    return (int32_t)((uint32_t)earlier + (uint32_t)later);
+}
+
+void oracle_scan_i32(int op, int exclusive, const int32_t *x, int32_t *y, int64_t n)
+{
+    int32_t acc = i32_identity(op);
+    for (int64_t i = 0; i < n; ++i) {
+        if (exclusive) {
+            y[i] = acc;
+            acc = i32_combine(op, acc, x[i]);
+        } else {
+            acc = i32_combine(op, acc, x[i]);
+            y[i] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* uint32                                                              */
+/* ------------------------------------------------------------------ */
+static uint32_t u32_identity(int op)
+{
+    if (op == OP_MIN) return UINT32_MAX;
+    return 0; /* add: 0, max: smallest value 0 */
+}
+
+static uint32_t u32_combine(int op, uint32_t earlier, uint32_t later)
+{
+    if (op == OP_MAX) return (later > earlier) ? later : earlier;
+    if (op == OP_MIN) return (later < earlier) ? later : earlier;
+    return earlier + later;
+}
+
+void oracle_scan_u32(int op, int exclusive, const uint32_t *x, uint32_t *y, int64_t n)
+{
+    uint32_t acc = u32_identity(op);
+    for (int64_t i = 0; i < n; ++i) {
+        if (exclusive) {
+            y[i] = acc;
+            acc = u32_combine(op, acc, x[i]);
+        } else {
+            acc = u32_combine(op, acc, x[i]);
+            y[i] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* float32 add: the reference value is accumulated in double, as the    */
+/* pages' CPU references do; s[i] is the matching prefix of |x|, which  */
+/* sets the tolerance of a float32 result.                              */
+/* ------------------------------------------------------------------ */
+void oracle_scan_f32_add(int exclusive, const float *x, double *y, double *s, int64_t n)
+{
+    double acc = 0.0, abs_acc = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (exclusive) {
+            y[i] = acc;
+            s[i] = abs_acc;
+            acc += (double)x[i];
+            abs_acc += fabs((double)x[i]);
+        } else {
+            acc += (double)x[i];
+            abs_acc += fabs((double)x[i]);
+            y[i] = acc;
+            s[i] = abs_acc;
+        }
+    }
+}
+
+/* float32 max/min: a later value replaces the running one only when it is
+ * strictly greater (smaller), so the earlier value wins ties (+0 vs -0).  */
+void oracle_scan_f32_minmax(int op, int exclusive, const float *x, float *y, int64_t n)
+{
+    float acc = (op == OP_MAX) ? -INFINITY : INFINITY;
+    for (int64_t i = 0; i < n; ++i) {
+        float next;
+        if (op == OP_MAX) next = (x[i] > acc) ? x[i] : acc;
+        else              next = (x[i] < acc) ? x[i] : acc;
+        if (exclusive) {
+            y[i] = acc;
+            acc = next;
+        } else {
+            acc = next;
+            y[i] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Affine-map composition over uint32 pairs stored as (a0,b0,a1,b1,...).  */
+/* y_i = a_i * y_{i-1} + b_i with y_{-1} = 0 is the b component; the a    */
+/* component is the running product of the multipliers.  All mod 2^32.   */
+/* ------------------------------------------------------------------ */
+void oracle_scan_affine(int exclusive, const uint32_t *ab, uint32_t *y, int64_t n)
+{
+    uint32_t A = 1u, B = 0u;
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t a = ab[2 * i], b = ab[2 * i + 1];
+        if (exclusive) {
+            y[2 * i] = A;
+            y[2 * i + 1] = B;
+        }
+        B = a * B + b;
+        A = a * A;
+        if (!exclusive) {
+            y[2 * i] = A;
+            y[2 * i + 1] = B;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Segmented scans: head[i] != 0 (or i == 0) starts a new segment; the  */
+/* exclusive form puts the identity at every head.                      */
+/* ------------------------------------------------------------------ */
+void oracle_segscan_i32(int op, int exclusive, const int32_t *x, const uint8_t *head,
+                        int32_t *y, int64_t n)
+{
+    int32_t acc = i32_identity(op);
+    for (int64_t i = 0; i < n; ++i) {
+        if (i == 0 || head[i]) acc = i32_identity(op);
+        if (exclusive) {
+            y[i] = acc;
+            acc = i32_combine(op, acc, x[i]);
+        } else {
+            acc = i32_combine(op, acc, x[i]);
+            y[i] = acc;
+        }
+    }
+}
+
+void oracle_segscan_u32(int op, int exclusive, const uint32_t *x, const uint8_t *head,
+                        uint32_t *y, int64_t n)
+{
+    uint32_t acc = u32_identity(op);
+    for (int64_t i = 0; i < n; ++i) {
+        if (i == 0 || head[i]) acc = u32_identity(op);
+        if (exclusive) {
+            y[i] = acc;
+            acc = u32_combine(op, acc, x[i]);
+        } else {
+            acc = u32_combine(op, acc, x[i]);
+            y[i] = acc;
+        }
+    }
+}
+
+void oracle_segscan_f32_add(int exclusive, const float *x, const uint8_t *head,
+                            double *y, double *s, int64_t n)
+{
+    double acc = 0.0, abs_acc = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (i == 0 || head[i]) {
+            acc = 0.0;
+            abs_acc = 0.0;
+        }
+        if (exclusive) {
+            y[i] = acc;
+            s[i] = abs_acc;
+            acc += (double)x[i];
+            abs_acc += fabs((double)x[i]);
+        } else {
+            acc += (double)x[i];
+            abs_acc += fabs((double)x[i]);
+            y[i] = acc;
+            s[i] = abs_acc;
+        }
+    }
+}
+
+void oracle_segscan_f32_minmax(int op, int exclusive, const float *x, const uint8_t *head,
+                               float *y, int64_t n)
+{
+    const float ident = (op == OP_MAX) ? -INFINITY : INFINITY;
+    float acc = ident;
+    for (int64_t i = 0; i < n; ++i) {
+        float next;
+        if (i == 0 || head[i]) acc = ident;
+        if (op == OP_MAX) next = (x[i] > acc) ? x[i] : acc;
+        else              next = (x[i] < acc) ? x[i] : acc;
+        if (exclusive) {
+            y[i] = acc;
+            acc = next;
+        } else {
+            acc = next;
+            y[i] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Stream compaction, predicate x > 0.  pos[i] is the exclusive scan of  */
+/* the 0/1 flags (the write index of element i when it is kept); kept    */
+/* elements go to out[pos[i]] in input order; returns the count.         */
+/* ------------------------------------------------------------------ */
+int64_t oracle_compact_i32(const int32_t *x, int32_t *out, uint32_t *pos, int64_t n)
+{
+    uint32_t c = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        pos[i] = c;
+        if (x[i] > 0) out[c++] = x[i];
+    }
+    return (int64_t)c;
+}
+
+int64_t oracle_compact_u32(const uint32_t *x, uint32_t *out, uint32_t *pos, int64_t n)
+{
+    uint32_t c = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        pos[i] = c;
+        if (x[i] > 0u) out[c++] = x[i];
+    }
+    return (int64_t)c;
+}
+
+int64_t oracle_compact_f32(const float *x, float *out, uint32_t *pos, int64_t n)
+{
+    uint32_t c = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        pos[i] = c;
+        if (x[i] > 0.0f) out[c++] = x[i];
+    }
+    return (int64_t)c;
+}

@@ -1,0 +1,346 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself:
+  * worked examples printed on the pages (tests/golden/, each file cites its page);
+  * closed forms (all-ones float sums are exact integers; the page's compaction
+    program on x[i] = i % 10 - 5 keeps 400 values 1 2 3 4 ...);
+  * brute force on tiny inputs: every y[i] recomputed from scratch with Python
+    integers, math.fsum, builtin max/min, 2x2 matrix products and per-segment folds;
+  * invariants (last inclusive element = total, exclusive = inclusive shifted
+    right with the identity, compaction keeps order and count);
+  * special cases that reduce to numpy routines (cumsum, maximum.accumulate,
+    cumprod) at larger sizes.
+"""
+import math
+import struct
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+import golden_fixtures
+
+U32 = 1 << 32
+IDENT = {
+    ("add", np.int32): 0, ("max", np.int32): -(1 << 31), ("min", np.int32): (1 << 31) - 1,
+    ("add", np.uint32): 0, ("max", np.uint32): 0, ("min", np.uint32): U32 - 1,
+    ("max", np.float32): -math.inf, ("min", np.float32): math.inf,
+}
+
+
+# --------------------------------------------------------------------------
+# worked examples from the pages
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("rec", golden_fixtures.all_examples("scan"), ids=lambda r: r["path"].split("/")[-1])
+def test_golden_scan(rec):
+    x = rec["input"]
+    for dt in {rec["dtype"], np.int32, np.float32}:
+        xx = x.astype(dt)
+        if "inclusive" in rec:
+            y = oracle.scan(rec["op"], xx)
+            y = y[0] if isinstance(y, tuple) else y
+            np.testing.assert_array_equal(np.asarray(y, np.float64), rec["inclusive"].astype(np.float64))
+        if "exclusive" in rec:
+            y = oracle.scan(rec["op"], xx, exclusive=True)
+            y = y[0] if isinstance(y, tuple) else y
+            np.testing.assert_array_equal(np.asarray(y, np.float64), rec["exclusive"].astype(np.float64))
+    if "remaining" in rec:
+        incl = oracle.scan("add", x.astype(np.int32))
+        assert int(rec["total_length"]) - int(incl[-1]) == int(rec["remaining"])
+
+
+@pytest.mark.parametrize("rec", golden_fixtures.all_examples("compact"), ids=lambda r: r["path"].split("/")[-1])
+def test_golden_compact(rec):
+    for dt in {rec["dtype"], np.int32, np.float32}:
+        x = rec["input"].astype(dt)
+        out, count, pos = oracle.compact(x)
+        np.testing.assert_array_equal(pos, rec["positions"])
+        np.testing.assert_array_equal(out.astype(np.float64), rec["output"].astype(np.float64))
+        assert count == int(rec["flags"].sum()) == len(rec["output"])
+        # the flag scan itself is an exclusive add-scan of the printed flags
+        np.testing.assert_array_equal(oracle.scan("add", rec["flags"], exclusive=True), rec["positions"])
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+def test_all_ones_float_is_exact_index():
+    # every partial sum of ones is an integer <= 2^24, exact in float and double
+    n = 1 << 20
+    x = np.ones(n, np.float32)
+    y, s = oracle.scan("add", x, exclusive=True)
+    np.testing.assert_array_equal(y, np.arange(n, dtype=np.float64))
+    np.testing.assert_array_equal(s, np.arange(n, dtype=np.float64))
+    y, s = oracle.scan("add", x)
+    np.testing.assert_array_equal(y, np.arange(1, n + 1, dtype=np.float64))
+
+
+def test_page_compaction_program_closed_form():
+    # x[i] = i % 10 - 5 over 1000 elements, keep x > 0: i % 10 in {6,7,8,9}
+    x = np.array([(i % 10) - 5 for i in range(1000)], np.float32)
+    out, count, pos = oracle.compact(x)
+    assert count == 400
+    np.testing.assert_array_equal(out, np.tile(np.array([1, 2, 3, 4], np.float32), 100))
+    assert pos[-1] + (1 if x[-1] > 0 else 0) == count
+
+
+def test_int32_add_wraps():
+    x = np.array([2**31 - 1, 1, -1, 5], np.int32)
+    np.testing.assert_array_equal(oracle.scan("add", x),
+                                  np.array([2**31 - 1, -(2**31), 2**31 - 1, -(2**31) + 4], np.int32))
+
+
+def test_affine_known_recurrence():
+    # y_i = a_i * y_{i-1} + b_i with y_{-1} = 0; a = 2, b = 1 gives 1, 3, 7, 15 (= 2^(i+1) - 1)
+    ab = np.array([[2, 1]] * 6, np.uint32)
+    y = oracle.scan_affine(ab)
+    np.testing.assert_array_equal(y[:, 1], np.array([1, 3, 7, 15, 31, 63], np.uint32))
+    np.testing.assert_array_equal(y[:, 0], np.array([2, 4, 8, 16, 32, 64], np.uint32))
+    ye = oracle.scan_affine(ab, exclusive=True)
+    np.testing.assert_array_equal(ye[0], [1, 0])
+    np.testing.assert_array_equal(ye[1:], y[:-1])
+
+
+def test_affine_non_commutative_order():
+    # applying (3,5) after (2,7): x -> 3*(2x+7)+5 = 6x + 26, not 2*(3x+5)+7 = 6x + 17
+    ab = np.array([[2, 7], [3, 5]], np.uint32)
+    np.testing.assert_array_equal(oracle.scan_affine(ab)[1], [6, 26])
+
+
+def test_float_max_ties_keep_earlier():
+    # reading: a later value replaces the running one only when strictly greater
+    x = np.array([0.0, -0.0, 1.0, 1.0], np.float32)
+    y = oracle.scan("max", x)
+    assert struct.pack("<f", y[1]) == struct.pack("<f", 0.0)  # +0 kept over -0
+    y = oracle.scan("min", np.array([-0.0, 0.0], np.float32))
+    assert struct.pack("<f", y[1]) == struct.pack("<f", -0.0)
+    ye = oracle.scan("max", x, exclusive=True)
+    assert ye[0] == -np.inf
+
+
+# --------------------------------------------------------------------------
+# brute force on tiny inputs: each y[i] from scratch
+# --------------------------------------------------------------------------
+def _tiny(dtype, n, rng):
+    if dtype == np.int32:
+        return rng.integers(-(2**31), 2**31, n, dtype=np.int64).astype(np.int32)
+    if dtype == np.uint32:
+        return rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)
+    return (rng.integers(-(2**23), 2**23, n) * 2.0**-23).astype(np.float32)
+
+
+def _bf_fold(op, dtype, vals):
+    """Fold a prefix from scratch with Python builtins."""
+    vals = [v.item() for v in vals]
+    if not vals:
+        return IDENT[(op, dtype)] if (op, dtype) in IDENT else 0
+    if op == "add":
+        if dtype == np.float32:
+            return math.fsum(vals)
+        t = sum(vals) % U32
+        return t - U32 if (dtype == np.int32 and t >= 2**31) else t
+    return max(vals) if op == "max" else min(vals)
+
+
+@pytest.mark.parametrize("dtype", [np.int32, np.uint32, np.float32])
+@pytest.mark.parametrize("op", ["add", "max", "min"])
+@pytest.mark.parametrize("exclusive", [False, True])
+def test_bruteforce_scan(op, dtype, exclusive):
+    rng = np.random.default_rng(11)
+    for n in list(range(0, 34)) + [63, 64, 65]:
+        x = _tiny(dtype, n, rng)
+        y = oracle.scan(op, x, exclusive=exclusive)
+        y = y[0] if isinstance(y, tuple) else y
+        for i in range(n):
+            want = _bf_fold(op, dtype, x[:i] if exclusive else x[:i + 1])
+            assert float(y[i]) == float(want), (op, dtype, exclusive, n, i)
+
+
+def test_bruteforce_exercise_input():
+    # exercise array of the PMPP chapter-9 notes (§八 "Scan定义"); the page prints no answer
+    x = np.array([3, 1, 4, 1, 5, 9, 2, 6], np.int32)
+    want_incl = [sum(x[:i + 1].tolist()) for i in range(8)]
+    want_excl = [sum(x[:i].tolist()) for i in range(8)]
+    np.testing.assert_array_equal(oracle.scan("add", x), want_incl)
+    np.testing.assert_array_equal(oracle.scan("add", x, exclusive=True), want_excl)
+    assert want_incl == [3, 4, 8, 9, 14, 23, 25, 31]
+
+
+def _mat_affine(pairs):
+    """Compose x -> a x + b maps as 2x2 matrices [[a, b], [0, 1]], later on the left."""
+    m = [[1, 0], [0, 1]]
+    for a, b in pairs:
+        a, b = int(a), int(b)
+        m = [[(a * m[0][0]) % U32, (a * m[0][1] + b * m[1][1]) % U32], [0, 1]]
+    return m[0][0], m[0][1]
+
+
+def _closed_affine(pairs):
+    """A_i = prod a_k; B_i = sum_j b_j * prod_{k>j} a_k (mod 2^32)."""
+    A = 1
+    for a, _ in pairs:
+        A = (A * int(a)) % U32
+    B = 0
+    for j, (_, b) in enumerate(pairs):
+        p = int(b)
+        for a, _ in pairs[j + 1:]:
+            p = (p * int(a)) % U32
+        B = (B + p) % U32
+    return A, B
+
+
+@pytest.mark.parametrize("exclusive", [False, True])
+def test_bruteforce_affine(exclusive):
+    rng = np.random.default_rng(5)
+    for n in list(range(0, 20)) + [40]:
+        ab = rng.integers(0, 2**32, (n, 2), dtype=np.uint64).astype(np.uint32)
+        y = oracle.scan_affine(ab, exclusive=exclusive)
+        for i in range(n):
+            pre = [tuple(p) for p in (ab[:i] if exclusive else ab[:i + 1])]
+            assert tuple(int(v) for v in y[i]) == _mat_affine(pre) == _closed_affine(pre)
+
+
+def _bf_segmented(op, dtype, x, heads, exclusive):
+    out = []
+    for i in range(len(x)):
+        s = max(j for j in range(i + 1) if j == 0 or heads[j])
+        out.append(_bf_fold(op, dtype, x[s:i] if exclusive else x[s:i + 1]))
+    return out
+
+
+@pytest.mark.parametrize("dtype", [np.int32, np.uint32, np.float32])
+@pytest.mark.parametrize("op", ["add", "max", "min"])
+@pytest.mark.parametrize("exclusive", [False, True])
+def test_bruteforce_segmented(op, dtype, exclusive):
+    rng = np.random.default_rng(7)
+    for n in list(range(0, 24)) + [50]:
+        x = _tiny(dtype, n, rng)
+        heads = (rng.random(n) < 0.25).astype(np.uint8)
+        if n > 1 and rng.random() < 0.5:
+            heads[0] = 0  # index 0 is a head whatever its flag says
+        y = oracle.segmented_scan(op, x, heads, exclusive=exclusive)
+        y = y[0] if isinstance(y, tuple) else y
+        want = _bf_segmented(op, dtype, x, heads, exclusive)
+        for i in range(n):
+            assert float(y[i]) == float(want[i]), (op, dtype, exclusive, n, i)
+
+
+@pytest.mark.parametrize("dtype", [np.int32, np.uint32, np.float32])
+def test_bruteforce_compact(dtype):
+    rng = np.random.default_rng(9)
+    for n in range(0, 40):
+        x = _tiny(dtype, n, rng)
+        if dtype == np.uint32:
+            x[rng.random(n) < 0.4] = 0
+        out, count, pos = oracle.compact(x)
+        keep = [v for v in x.tolist() if v > 0]
+        assert count == len(keep)
+        assert out.tolist() == keep
+        for i in range(n):
+            assert pos[i] == sum(1 for v in x[:i].tolist() if v > 0)
+
+
+# --------------------------------------------------------------------------
+# invariants and special cases at larger sizes
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [np.int32, np.uint32, np.float32])
+@pytest.mark.parametrize("op", ["add", "max", "min"])
+def test_invariants(op, dtype):
+    n = 100003
+    x = {np.int32: si.int32_full, np.uint32: si.uint32_full, np.float32: si.float32_sym}[dtype](21, n)
+    inc = oracle.scan(op, x)
+    exc = oracle.scan(op, x, exclusive=True)
+    if isinstance(inc, tuple):
+        (inc, s_inc), (exc, s_exc) = inc, exc
+        np.testing.assert_array_equal(s_exc[1:], s_inc[:-1])
+        assert s_exc[0] == 0.0
+        # values on the 2^-23 grid with |prefix| < 2^17: every double partial sum is exact
+        assert inc[-1] == math.fsum(x.astype(np.float64).tolist())
+        assert s_inc[-1] == math.fsum(np.abs(x.astype(np.float64)).tolist())
+        ident = 0.0
+    else:
+        ident = IDENT[(op, dtype)]
+        if op == "add":
+            total = int(x.astype(np.int64).sum()) % U32
+            assert int(inc[-1].astype(np.int64)) % U32 == total
+        elif op == "max":
+            assert inc[-1] == x.max()
+            assert np.all(inc[1:] >= inc[:-1])
+        else:
+            assert inc[-1] == x.min()
+            assert np.all(inc[1:] <= inc[:-1])
+    # exclusive = inclusive shifted right by one with the identity at index 0
+    assert float(exc[0]) == float(ident)
+    np.testing.assert_array_equal(exc[1:], inc[:-1])
+
+
+def test_reduces_to_numpy_routines():
+    n = 200001
+    xi = si.int32_full(3, n)
+    np.testing.assert_array_equal(oracle.scan("add", xi),
+                                  (np.cumsum(xi.astype(np.int64)) % U32).astype(np.uint32).view(np.int32))
+    np.testing.assert_array_equal(oracle.scan("max", xi), np.maximum.accumulate(xi))
+    np.testing.assert_array_equal(oracle.scan("min", xi), np.minimum.accumulate(xi))
+    xu = si.uint32_full(4, n)
+    np.testing.assert_array_equal(oracle.scan("max", xu), np.maximum.accumulate(xu))
+    xf = si.float32_01(2, n)
+    y, s = oracle.scan("add", xf)
+    np.testing.assert_array_equal(y, np.cumsum(xf.astype(np.float64)))
+    np.testing.assert_array_equal(s, np.cumsum(np.abs(xf.astype(np.float64))))
+    np.testing.assert_array_equal(oracle.scan("max", xf), np.maximum.accumulate(xf))
+
+
+def test_affine_special_cases():
+    n = 100000
+    ab = si.affine_pairs(4, n)
+    # all a = 1: the b component is the wrapping add-scan of b
+    ab1 = ab.copy()
+    ab1[:, 0] = 1
+    y = oracle.scan_affine(ab1)
+    np.testing.assert_array_equal(y[:, 0], np.ones(n, np.uint32))
+    np.testing.assert_array_equal(y[:, 1], (np.cumsum(ab1[:, 1].astype(np.uint64)) % U32).astype(np.uint32))
+    # all b = 0: the a component is the running product, b stays 0
+    ab0 = ab.copy()
+    ab0[:, 1] = 0
+    y = oracle.scan_affine(ab0)
+    np.testing.assert_array_equal(y[:, 1], np.zeros(n, np.uint32))
+    np.testing.assert_array_equal(y[:, 0], (np.cumprod(ab0[:, 0].astype(np.uint64)) % U32).astype(np.uint32))
+    # the a component is always the running product of the multipliers
+    y = oracle.scan_affine(ab)
+    np.testing.assert_array_equal(y[:, 0], (np.cumprod(ab[:, 0].astype(np.uint64)) % U32).astype(np.uint32))
+
+
+def test_segmented_special_cases():
+    n = 50000
+    x = si.int32_pm100(5, n)
+    # every element a head: inclusive gives x, exclusive the identity
+    h = np.ones(n, np.uint8)
+    np.testing.assert_array_equal(oracle.segmented_scan("add", x, h), x)
+    np.testing.assert_array_equal(oracle.segmented_scan("add", x, h, exclusive=True), np.zeros(n, np.int32))
+    np.testing.assert_array_equal(oracle.segmented_scan("max", x, h, exclusive=True),
+                                  np.full(n, -(2**31), np.int32))
+    # a single head at 0: the plain scan
+    h = np.zeros(n, np.uint8)
+    for op in ("add", "max", "min"):
+        np.testing.assert_array_equal(oracle.segmented_scan(op, x, h), oracle.scan(op, x))
+        np.testing.assert_array_equal(oracle.segmented_scan(op, x, h, exclusive=True),
+                                      oracle.scan(op, x, exclusive=True))
+    # random heads: each segment's last value is the segment's own sum
+    h = si.segment_heads(5, n, mean_len=100.0)
+    y = oracle.segmented_scan("add", x, h)
+    starts = np.flatnonzero(h)
+    ends = np.append(starts[1:], n) - 1
+    for a, b in zip(starts[:200], ends[:200]):
+        assert y[b] == x[a:b + 1].astype(np.int64).sum()
+
+
+def test_compaction_invariants_large():
+    n = 300000
+    x = si.float32_normal(3, n)
+    out, count, pos = oracle.compact(x)
+    flags = (x > 0)
+    assert count == int(flags.sum())
+    np.testing.assert_array_equal(out, x[flags])
+    assert pos[-1] + int(flags[-1]) == count
+    np.testing.assert_array_equal(pos, oracle.scan("add", flags.astype(np.uint32), exclusive=True))
