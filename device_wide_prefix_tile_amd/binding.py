@@ -1,0 +1,173 @@
+"""Thin ctypes binding of libdwpt_scan.so for torch tensors.
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+the library.  The functions carry the C ABI's names (dwpt_scan.h); they take
+torch tensors on the current CUDA (HIP) device, enqueue on the current torch
+stream and return without synchronising.  There is no CPU fallback: if the
+library cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+SCAN_OK, SCAN_ERR_INVALID, SCAN_ERR_UNSUPPORTED, SCAN_ERR_NOMEM, SCAN_ERR_HIP, SCAN_ERR_TIMEOUT = range(6)
+OPS = {"add": 0, "max": 1, "min": 2, "affine": 3}
+SCAN_I32, SCAN_U32, SCAN_F32, SCAN_U32X2 = range(4)
+_DTYPES = {torch.int32: SCAN_I32, torch.uint32: SCAN_U32, torch.float32: SCAN_F32}
+
+EXPORTS = ("scan_inclusive", "scan_exclusive", "segmented_scan", "compact", "scan_status_string",
+           "scan_get_device_error", "scan_release_workspace", "scan_set_small_n_max",
+           "scan_set_spin_limit", "scan_copy_probe")
+
+_lib = None
+
+
+class ScanError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (built in-tree first if it is not there yet)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB_PATH):
+        _build.build()
+    L = ctypes.CDLL(_build.LIB_PATH)
+    P, S, I, U = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint32
+    sig = {
+        "scan_inclusive": ([I, I, P, P, S, P], I),
+        "scan_exclusive": ([I, I, P, P, S, P], I),
+        "segmented_scan": ([I, I, P, P, P, S, I, P], I),
+        "compact": ([I, P, P, P, S, P], I),
+        "scan_status_string": ([I], ctypes.c_char_p),
+        "scan_get_device_error": ([P], I),
+        "scan_release_workspace": ([], I),
+        "scan_set_small_n_max": ([S], S),
+        "scan_set_spin_limit": ([U], U),
+        "scan_copy_probe": ([P, P, S, P], I),
+    }
+    for name, (argtypes, restype) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().scan_status_string(int(status)).decode()
+
+
+scan_status_string = status_string
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, what: str):
+    if status != SCAN_OK:
+        raise ScanError(status, what)
+
+
+def _dtype_code(x: torch.Tensor, op: str) -> int:
+    if op == "affine":
+        if x.dtype not in (torch.int32, torch.uint32) or x.dim() != 2 or x.shape[1] != 2:
+            raise TypeError("affine scans take an (n, 2) int32/uint32 tensor of (a, b) pairs")
+        return SCAN_U32X2
+    if x.dtype not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % x.dtype)
+    return _DTYPES[x.dtype]
+
+
+def _prep(x: torch.Tensor, out):
+    if not x.is_cuda:
+        raise ValueError("input must be a device tensor")
+    if not x.is_contiguous():
+        raise ValueError("input must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous device tensor shaped like the input")
+    return out
+
+
+def scan_inclusive(x: torch.Tensor, op: str = "add", out: torch.Tensor | None = None, stream=None):
+    """out[i] = x[0] (+) ... (+) x[i]; op in add/max/min (1-D) or affine ((n, 2) pairs)."""
+    dt = _dtype_code(x, op)
+    out = _prep(x, out)
+    _check(lib().scan_inclusive(OPS[op], dt, x.data_ptr(), out.data_ptr(), x.shape[0], _stream(stream)),
+           "scan_inclusive")
+    return out
+
+
+def scan_exclusive(x: torch.Tensor, op: str = "add", out: torch.Tensor | None = None, stream=None):
+    """out[0] = identity, out[i] = x[0] (+) ... (+) x[i-1]."""
+    dt = _dtype_code(x, op)
+    out = _prep(x, out)
+    _check(lib().scan_exclusive(OPS[op], dt, x.data_ptr(), out.data_ptr(), x.shape[0], _stream(stream)),
+           "scan_exclusive")
+    return out
+
+
+def segmented_scan(x: torch.Tensor, heads: torch.Tensor, op: str = "add", exclusive: bool = False,
+                   out: torch.Tensor | None = None, stream=None):
+    """Scan restarted at every nonzero head flag (uint8 tensor); x[0] always starts a segment."""
+    if op not in ("add", "max", "min"):
+        raise ValueError("segmented scans take add, max or min")
+    dt = _dtype_code(x, op)
+    if heads.dtype != torch.uint8 or heads.shape != x.shape or not heads.is_contiguous() or not heads.is_cuda:
+        raise ValueError("heads must be a contiguous uint8 device tensor shaped like x")
+    out = _prep(x, out)
+    _check(lib().segmented_scan(OPS[op], dt, x.data_ptr(), heads.data_ptr(), out.data_ptr(), x.shape[0],
+                                1 if exclusive else 0, _stream(stream)), "segmented_scan")
+    return out
+
+
+def compact(x: torch.Tensor, out: torch.Tensor | None = None, count: torch.Tensor | None = None,
+            stream=None):
+    """Keeps x > 0 in order: returns (out, count) with out[:count] the kept elements.
+
+    count is a 1-element uint32 device tensor; read it after synchronising.
+    """
+    dt = _dtype_code(x, "add")
+    out = _prep(x, out)
+    if count is None:
+        count = torch.zeros(1, dtype=torch.uint32, device=x.device)
+    _check(lib().compact(dt, x.data_ptr(), out.data_ptr(), count.data_ptr(), x.shape[0], _stream(stream)),
+           "compact")
+    return out, count
+
+
+def scan_get_device_error(stream=None) -> int:
+    return int(lib().scan_get_device_error(_stream(stream)))
+
+
+def scan_release_workspace():
+    _check(lib().scan_release_workspace(), "scan_release_workspace")
+
+
+def scan_set_small_n_max(n_max: int) -> int:
+    return int(lib().scan_set_small_n_max(int(n_max)))
+
+
+def scan_set_spin_limit(polls: int) -> int:
+    return int(lib().scan_set_spin_limit(int(polls)))
+
+
+def scan_copy_probe(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check(lib().scan_copy_probe(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream)), "scan_copy_probe")
+    return dst

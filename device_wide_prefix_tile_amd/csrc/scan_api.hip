@@ -1,0 +1,387 @@
+// scan_api.hip -- C ABI of libdwpt_scan.so: argument checks, the
+// (op, dtype, variant) dispatch table, workspace management and launches.
+// The kernels are in tile_scan.hpp; the ABI is documented in dwpt_scan.h.
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <new>
+#include <utility>
+
+#include "dwpt_scan.h"
+#include "tile_scan.hpp"
+
+using namespace dwpt;
+
+namespace {
+
+// ------------------------------------------------------------ tile shapes
+// 256 threads (4 wavefronts); 16 four-byte or 8 eight-byte elements per
+// thread, i.e. 16 KiB tiles.
+template <class Op>
+struct Shape {
+    static constexpr int BLOCK = 256;
+    static constexpr int ITEMS = sizeof(typename Op::elem_t) == 8 ? 8 : 16;
+    static constexpr int TILE = BLOCK * ITEMS;
+};
+
+// ------------------------------------------------------------ settings
+std::mutex g_mu;
+size_t g_small_n_max = 4096;          // n at or below: single-workgroup path
+uint32_t g_spin_limit = 1u << 20;     // look-back polls before giving up (about a second)
+
+// ------------------------------------------------------------ workspaces
+struct Workspace {
+    void* mem = nullptr;
+    size_t status_words = 0;  // capacity in 64-bit status words
+    uint64_t* status = nullptr;
+    uint32_t* ctr = nullptr;
+    uint32_t* err = nullptr;
+    uint32_t ctr_base = 0;
+    uint32_t epoch = 0;
+};
+std::map<std::pair<int, void*>, Workspace> g_ws;
+constexpr size_t kHeaderBytes = 256;  // err word, tile counter, padding
+
+__global__ void zero_words_kernel(uint64_t* p, size_t nwords)
+{
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < nwords;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+hipError_t zero_async(void* p, size_t bytes, hipStream_t s)
+{
+    const size_t nwords = bytes / 8;
+    unsigned grid = (unsigned)((nwords + 255) / 256);
+    if (grid > 1024) grid = 1024;
+    if (grid == 0) grid = 1;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(grid), dim3(256), 0, s, static_cast<uint64_t*>(p), nwords);
+    return hipGetLastError();
+}
+
+// Called with g_mu held.  Makes sure the (device, stream) workspace holds at
+// least `words` status words and advances its epoch for a new call.
+scan_status_t acquire_workspace(hipStream_t s, size_t words, Workspace** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SCAN_ERR_HIP;
+    Workspace& ws = g_ws[std::make_pair(dev, (void*)s)];
+    if (ws.status_words < words) {
+        size_t cap = ws.status_words ? ws.status_words * 2 : (size_t)1 << 16;
+        while (cap < words) cap *= 2;
+        if (ws.mem) {
+            if (hipStreamSynchronize(s) != hipSuccess) return SCAN_ERR_HIP;
+            (void)hipFree(ws.mem);
+            ws = Workspace();
+        }
+        void* mem = nullptr;
+        const size_t bytes = kHeaderBytes + cap * 8;
+        if (hipMalloc(&mem, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return SCAN_ERR_NOMEM;
+        }
+        if (zero_async(mem, bytes, s) != hipSuccess) {
+            (void)hipFree(mem);
+            return SCAN_ERR_HIP;
+        }
+        ws.mem = mem;
+        ws.status_words = cap;
+        ws.err = static_cast<uint32_t*>(mem);
+        ws.ctr = static_cast<uint32_t*>(mem) + 1;
+        ws.status = reinterpret_cast<uint64_t*>(static_cast<char*>(mem) + kHeaderBytes);
+        ws.ctr_base = 0;
+        ws.epoch = 0;
+    }
+    ws.epoch += 1;
+    if (ws.epoch >= (1u << kEpochBits)) {
+        // every tag of the array could now alias the new epoch: clear it
+        if (zero_async(ws.status, ws.status_words * 8, s) != hipSuccess) return SCAN_ERR_HIP;
+        ws.epoch = 1;
+    }
+    *out = &ws;
+    return SCAN_OK;
+}
+
+// ------------------------------------------------------------ launches
+struct Call {
+    const void* in;
+    void* out;
+    const uint8_t* heads;
+    uint32_t* count;
+    size_t n;
+    hipStream_t stream;
+};
+
+bool is_aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Fills params and launches either the single-workgroup or the multi-tile
+// kernel.  KS / KM are the two kernel instances, TILE the tile size and
+// kWords the status words per tile.
+template <int BLOCK, int TILE, int kWords>
+scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), const Call& c, bool vec_ok)
+{
+    ScanParams p{};
+    p.in = c.in;
+    p.out = c.out;
+    p.heads = c.heads;
+    p.count = c.count;
+    p.n = c.n;
+    const uint64_t tiles = (c.n + TILE - 1) / TILE;
+    if (tiles > 0xFFFFFFFFull) return SCAN_ERR_INVALID;
+    p.num_tiles = (uint32_t)tiles;
+    p.vec_ok = vec_ok ? 1 : 0;
+
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (c.n <= g_small_n_max) {
+        hipLaunchKernelGGL(ks, dim3(1), dim3(BLOCK), 0, c.stream, p);
+        return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+    }
+    Workspace* ws = nullptr;
+    const scan_status_t st = acquire_workspace(c.stream, (size_t)tiles * kWords, &ws);
+    if (st != SCAN_OK) return st;
+    p.tile_ctr = ws->ctr;
+    p.ctr_base = ws->ctr_base;
+    p.lb.status = ws->status;
+    p.lb.err = ws->err;
+    p.lb.epoch = ws->epoch;
+    p.lb.spin_limit = g_spin_limit;
+    hipLaunchKernelGGL(km, dim3(p.num_tiles), dim3(BLOCK), 0, c.stream, p);
+    if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+    ws->ctr_base += p.num_tiles;  // every workgroup takes exactly one tile number
+    return SCAN_OK;
+}
+
+template <class Op, bool EXCL>
+scan_status_t run_scan(const Call& c, bool vec_ok)
+{
+    using S = Shape<Op>;
+    return launch<S::BLOCK, S::TILE, Op::kWords>(tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, true>,
+                                                 tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, false>, c,
+                                                 vec_ok);
+}
+
+template <typename T>
+scan_status_t run_compact(const Call& c, bool vec_ok)
+{
+    constexpr int BLOCK = 256, ITEMS = 16;
+    return launch<BLOCK, BLOCK * ITEMS, 1>(compact_kernel<T, BLOCK, ITEMS, true>,
+                                           compact_kernel<T, BLOCK, ITEMS, false>, c, vec_ok);
+}
+
+typedef scan_status_t (*Runner)(const Call&, bool);
+
+// Dispatch tables: [op][dtype] for plain scans (inclusive, exclusive) and
+// segmented scans (inclusive, exclusive); nullptr = unsupported.
+template <bool EXCL>
+Runner plain_runner(int op, int dt)
+{
+    static const Runner table[4][4] = {
+        {run_scan<OpAdd<int32_t>, EXCL>, run_scan<OpAdd<uint32_t>, EXCL>, run_scan<OpAdd<float>, EXCL>, nullptr},
+        {run_scan<OpMax<int32_t>, EXCL>, run_scan<OpMax<uint32_t>, EXCL>, run_scan<OpMax<float>, EXCL>, nullptr},
+        {run_scan<OpMin<int32_t>, EXCL>, run_scan<OpMin<uint32_t>, EXCL>, run_scan<OpMin<float>, EXCL>, nullptr},
+        {nullptr, nullptr, nullptr, run_scan<OpAffine, EXCL>},
+    };
+    return table[op][dt];
+}
+
+template <bool EXCL>
+Runner seg_runner(int op, int dt)
+{
+    static const Runner table[3][3] = {
+        {run_scan<OpSeg<OpAdd<int32_t>>, EXCL>, run_scan<OpSeg<OpAdd<uint32_t>>, EXCL>,
+         run_scan<OpSeg<OpAdd<float>>, EXCL>},
+        {run_scan<OpSeg<OpMax<int32_t>>, EXCL>, run_scan<OpSeg<OpMax<uint32_t>>, EXCL>,
+         run_scan<OpSeg<OpMax<float>>, EXCL>},
+        {run_scan<OpSeg<OpMin<int32_t>>, EXCL>, run_scan<OpSeg<OpMin<uint32_t>>, EXCL>,
+         run_scan<OpSeg<OpMin<float>>, EXCL>},
+    };
+    return table[op][dt];
+}
+
+size_t elem_size(int dt) { return dt == SCAN_U32X2 ? 8 : 4; }
+
+bool ranges_partially_overlap(const void* a, const void* b, size_t bytes_a, size_t bytes_b)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    if (a0 == b0) return false;
+    return a0 < b0 + bytes_b && b0 < a0 + bytes_a;
+}
+
+scan_status_t plain_scan(bool excl, scan_op_t op, scan_dtype_t dt, const void* in, void* out, size_t n,
+                         void* stream)
+{
+    if ((unsigned)op > SCAN_OP_AFFINE || (unsigned)dt > SCAN_U32X2) return SCAN_ERR_UNSUPPORTED;
+    const Runner r = excl ? plain_runner<true>(op, dt) : plain_runner<false>(op, dt);
+    if (!r) return SCAN_ERR_UNSUPPORTED;
+    if (n == 0) return SCAN_OK;
+    const size_t es = elem_size(dt);
+    if (!in || !out) return SCAN_ERR_INVALID;
+    if (!is_aligned(in, es) || !is_aligned(out, es)) return SCAN_ERR_INVALID;
+    if (n > ((size_t)1 << 40)) return SCAN_ERR_INVALID;
+    if (ranges_partially_overlap(in, out, n * es, n * es)) return SCAN_ERR_INVALID;
+    const Call c{in, out, nullptr, nullptr, n, static_cast<hipStream_t>(stream)};
+    return r(c, is_aligned(in, 16) && is_aligned(out, 16));
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+scan_status_t scan_inclusive(scan_op_t op, scan_dtype_t dtype, const void* in, void* out, size_t n,
+                             void* stream)
+{
+    try {
+        return plain_scan(false, op, dtype, in, out, n, stream);
+    } catch (const std::bad_alloc&) {
+        return SCAN_ERR_NOMEM;
+    }
+}
+
+scan_status_t scan_exclusive(scan_op_t op, scan_dtype_t dtype, const void* in, void* out, size_t n,
+                             void* stream)
+{
+    try {
+        return plain_scan(true, op, dtype, in, out, n, stream);
+    } catch (const std::bad_alloc&) {
+        return SCAN_ERR_NOMEM;
+    }
+}
+
+scan_status_t segmented_scan(scan_op_t op, scan_dtype_t dtype, const void* in, const uint8_t* head_flags,
+                             void* out, size_t n, int exclusive, void* stream)
+{
+    try {
+        if ((unsigned)op > SCAN_OP_MIN || (unsigned)dtype > SCAN_F32) return SCAN_ERR_UNSUPPORTED;
+        const Runner r = exclusive ? seg_runner<true>(op, dtype) : seg_runner<false>(op, dtype);
+        if (n == 0) return SCAN_OK;
+        if (!in || !out || !head_flags) return SCAN_ERR_INVALID;
+        if (!is_aligned(in, 4) || !is_aligned(out, 4)) return SCAN_ERR_INVALID;
+        if (n > ((size_t)1 << 40)) return SCAN_ERR_INVALID;
+        if (ranges_partially_overlap(in, out, n * 4, n * 4)) return SCAN_ERR_INVALID;
+        if (ranges_partially_overlap(head_flags, out, n, n * 4) || (const void*)head_flags == out)
+            return SCAN_ERR_INVALID;
+        const Call c{in, out, head_flags, nullptr, n, static_cast<hipStream_t>(stream)};
+        return r(c, is_aligned(in, 16) && is_aligned(out, 16) && is_aligned(head_flags, 4));
+    } catch (const std::bad_alloc&) {
+        return SCAN_ERR_NOMEM;
+    }
+}
+
+scan_status_t compact(scan_dtype_t dtype, const void* in, void* out, uint32_t* d_count, size_t n, void* stream)
+{
+    try {
+        if ((unsigned)dtype > SCAN_F32) return SCAN_ERR_UNSUPPORTED;
+        if (!d_count || !is_aligned(d_count, 4)) return SCAN_ERR_INVALID;
+        // n == 0 still launches one single-workgroup pass so that *d_count becomes 0
+        if (n > 0 && (!in || !out)) return SCAN_ERR_INVALID;
+        if (n > 0 && (!is_aligned(in, 4) || !is_aligned(out, 4))) return SCAN_ERR_INVALID;
+        if (n >= ((size_t)1 << 32)) return SCAN_ERR_INVALID;
+        if (n > 0 && ranges_partially_overlap(in, out, n * 4, n * 4)) return SCAN_ERR_INVALID;
+        if (ranges_partially_overlap(d_count, out, 4, n * 4) || (void*)d_count == out) return SCAN_ERR_INVALID;
+        const Call c{in, out, nullptr, d_count, n, static_cast<hipStream_t>(stream)};
+        const bool vec_ok = is_aligned(in, 16);
+        switch (dtype) {
+            case SCAN_I32: return run_compact<int32_t>(c, vec_ok);
+            case SCAN_U32: return run_compact<uint32_t>(c, vec_ok);
+            case SCAN_F32: return run_compact<float>(c, vec_ok);
+            default: return SCAN_ERR_UNSUPPORTED;
+        }
+    } catch (const std::bad_alloc&) {
+        return SCAN_ERR_NOMEM;
+    }
+}
+
+const char* scan_status_string(scan_status_t s)
+{
+    switch (s) {
+        case SCAN_OK: return "ok";
+        case SCAN_ERR_INVALID: return "invalid argument";
+        case SCAN_ERR_UNSUPPORTED: return "unsupported op/dtype combination";
+        case SCAN_ERR_NOMEM: return "out of device memory for the workspace";
+        case SCAN_ERR_HIP: return "HIP runtime error";
+        case SCAN_ERR_TIMEOUT: return "look-back wait timed out on the device";
+    }
+    return "unknown status";
+}
+
+scan_status_t scan_get_device_error(void* stream)
+{
+    try {
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        if (hipStreamSynchronize(s) != hipSuccess) return SCAN_ERR_HIP;
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return SCAN_ERR_HIP;
+        std::lock_guard<std::mutex> lock(g_mu);
+        auto it = g_ws.find(std::make_pair(dev, (void*)s));
+        if (it == g_ws.end() || !it->second.mem) return SCAN_OK;
+        uint32_t err = 0;
+        if (hipMemcpy(&err, it->second.err, 4, hipMemcpyDeviceToHost) != hipSuccess) return SCAN_ERR_HIP;
+        if (err) {
+            const uint32_t zero = 0;
+            if (hipMemcpy(it->second.err, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return SCAN_ERR_HIP;
+        }
+        if (err & kErrTimeout) return SCAN_ERR_TIMEOUT;
+        return err ? SCAN_ERR_HIP : SCAN_OK;
+    } catch (const std::bad_alloc&) {
+        return SCAN_ERR_NOMEM;
+    }
+}
+
+scan_status_t scan_release_workspace(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    scan_status_t st = SCAN_OK;
+    for (auto& kv : g_ws) {
+        if (!kv.second.mem) continue;
+        if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
+            hipFree(kv.second.mem) != hipSuccess)
+            st = SCAN_ERR_HIP;
+    }
+    g_ws.clear();
+    (void)hipSetDevice(cur);
+    return st;
+}
+
+size_t scan_set_small_n_max(size_t n_max)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    const size_t old = g_small_n_max;
+    g_small_n_max = n_max;
+    return old;
+}
+
+uint32_t scan_set_spin_limit(uint32_t polls)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    const uint32_t old = g_spin_limit;
+    g_spin_limit = polls;
+    return old;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ copy probe
+namespace {
+__global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4* __restrict__ in, u32x4* __restrict__ out,
+                                                          size_t nvec)
+{
+    for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < nvec; i += (size_t)gridDim.x * 256)
+        out[i] = in[i];
+}
+}  // namespace
+
+extern "C" scan_status_t scan_copy_probe(const void* in, void* out, size_t nbytes, void* stream)
+{
+    if (nbytes == 0) return SCAN_OK;
+    if (!in || !out || nbytes % 16 || !is_aligned(in, 16) || !is_aligned(out, 16)) return SCAN_ERR_INVALID;
+    const size_t nvec = nbytes / 16;
+    size_t grid = (nvec + 255) / 256;
+    if (grid > 65536 * 4) grid = 65536 * 4;
+    hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(in), static_cast<u32x4*>(out), nvec);
+    return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+}

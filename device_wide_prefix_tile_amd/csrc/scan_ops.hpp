@@ -1,0 +1,201 @@
+// scan_ops.hpp -- associative operators of the device-wide scan (gfx950).
+//
+// Pages cited:
+//   [L7]    "Lecture 7: 并行模式五 —— 前缀和 / 扫描：双缓冲与层次化算法"
+//           (UIUC ECE408 course notes, runguoli.com)
+//   [PMPP9] "第9章并行模式：前缀和 - Scan算法" (PMPP chapter 9 notes, bittern.cn)
+//
+// A scan needs only associativity; operand order is fixed, the earlier
+// value is always the left argument [L7 concept 1, operator generalisation].
+// Identities follow the table of [PMPP9 §9.1]: + -> 0, max -> -inf,
+// min -> +inf; for 32-bit integers the extreme values of the type stand for
+// -inf/+inf, and the affine map's identity is (1, 0).
+//
+// Each operator trait exposes:
+//   elem_t            element type in memory
+//   value_t           value scanned inside a tile (registers)
+//   carry_t           inter-tile prefix type (wider for float32 add)
+//   prep_t            a carry made ready to be applied per element
+//   identity(), combine(earlier, later)            on value_t
+//   carry_identity(), to_carry(v), combine_carry(earlier, later)
+//   prepare(carry) -> prep_t, apply(prep, local) -> value_t   (= carry (+) local)
+//   kWords, pack(carry, words, flag), unpack(words, flag)     status-word codec
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dwpt {
+
+struct Affine {
+    uint32_t a, b;
+};
+
+// ---------------------------------------------------------------- helpers
+template <typename V>
+__device__ __forceinline__ void to_words(const V& v, uint32_t* w)
+{
+    static_assert(sizeof(V) % 4 == 0, "32-bit multiple");
+    __builtin_memcpy(w, &v, sizeof(V));
+}
+template <typename V>
+__device__ __forceinline__ V from_words(const uint32_t* w)
+{
+    V v;
+    __builtin_memcpy(&v, w, sizeof(V));
+    return v;
+}
+
+// Common part for operators whose carry is their own value type.
+template <typename T, typename Derived>
+struct SameCarry {
+    using elem_t = T;
+    using value_t = T;
+    using carry_t = T;
+    using prep_t = T;
+    static constexpr int kWords = sizeof(T) / 4;
+    __device__ __forceinline__ static carry_t carry_identity() { return Derived::identity(); }
+    __device__ __forceinline__ static carry_t to_carry(value_t v) { return v; }
+    __device__ __forceinline__ static carry_t combine_carry(carry_t a, carry_t b) { return Derived::combine(a, b); }
+    __device__ __forceinline__ static prep_t prepare(carry_t c) { return c; }
+    __device__ __forceinline__ static value_t apply(prep_t c, value_t local) { return Derived::combine(c, local); }
+    __device__ __forceinline__ static void pack(carry_t c, uint32_t* w, uint32_t& flag) { to_words(c, w); flag = 0; }
+    __device__ __forceinline__ static carry_t unpack(const uint32_t* w, uint32_t) { return from_words<carry_t>(w); }
+};
+
+// ---------------------------------------------------------------- add
+template <typename T> struct OpAdd;
+
+// int32 add wraps modulo 2^32 (done in uint32 to keep it defined).
+template <> struct OpAdd<int32_t> : SameCarry<int32_t, OpAdd<int32_t>> {
+    __device__ __forceinline__ static int32_t identity() { return 0; }
+    __device__ __forceinline__ static int32_t combine(int32_t a, int32_t b)
+    {
+        return (int32_t)((uint32_t)a + (uint32_t)b);
+    }
+};
+
+template <> struct OpAdd<uint32_t> : SameCarry<uint32_t, OpAdd<uint32_t>> {
+    __device__ __forceinline__ static uint32_t identity() { return 0u; }
+    __device__ __forceinline__ static uint32_t combine(uint32_t a, uint32_t b) { return a + b; }
+};
+
+// float32 add: tiles are summed in float32, but the prefix carried from tile
+// to tile is a double, and each output is rounded once from
+// (carry in double) + (in-tile float partial).  The carry is split into a
+// float pair hi + lo once per thread so that the per-element work stays two
+// float32 adds: y = hi + (lo + local).
+struct F32Split {
+    float hi, lo;
+};
+template <> struct OpAdd<float> {
+    using elem_t = float;
+    using value_t = float;
+    using carry_t = double;
+    using prep_t = F32Split;
+    static constexpr int kWords = 2;
+    __device__ __forceinline__ static float identity() { return 0.0f; }
+    __device__ __forceinline__ static float combine(float a, float b) { return a + b; }
+    __device__ __forceinline__ static double carry_identity() { return 0.0; }
+    __device__ __forceinline__ static double to_carry(float v) { return (double)v; }
+    __device__ __forceinline__ static double combine_carry(double a, double b) { return a + b; }
+    __device__ __forceinline__ static F32Split prepare(double c)
+    {
+        float hi = (float)c;
+        float lo = (float)(c - (double)hi);
+        return {hi, lo};
+    }
+    __device__ __forceinline__ static float apply(F32Split c, float local) { return c.hi + (c.lo + local); }
+    __device__ __forceinline__ static void pack(double c, uint32_t* w, uint32_t& flag) { to_words(c, w); flag = 0; }
+    __device__ __forceinline__ static double unpack(const uint32_t* w, uint32_t) { return from_words<double>(w); }
+};
+
+// ---------------------------------------------------------------- max / min
+// A later value replaces the running one only when strictly greater
+// (smaller); the earlier value wins ties, which keeps the operator
+// associative for floats with +0/-0 and makes results bit-exact.
+template <typename T> struct Limits;
+template <> struct Limits<int32_t> {
+    __device__ __forceinline__ static int32_t lowest() { return INT32_MIN; }
+    __device__ __forceinline__ static int32_t highest() { return INT32_MAX; }
+};
+template <> struct Limits<uint32_t> {
+    __device__ __forceinline__ static uint32_t lowest() { return 0u; }
+    __device__ __forceinline__ static uint32_t highest() { return UINT32_MAX; }
+};
+template <> struct Limits<float> {
+    __device__ __forceinline__ static float lowest() { return -__builtin_inff(); }
+    __device__ __forceinline__ static float highest() { return __builtin_inff(); }
+};
+
+template <typename T> struct OpMax : SameCarry<T, OpMax<T>> {
+    __device__ __forceinline__ static T identity() { return Limits<T>::lowest(); }
+    __device__ __forceinline__ static T combine(T a, T b) { return (b > a) ? b : a; }
+};
+template <typename T> struct OpMin : SameCarry<T, OpMin<T>> {
+    __device__ __forceinline__ static T identity() { return Limits<T>::highest(); }
+    __device__ __forceinline__ static T combine(T a, T b) { return (b < a) ? b : a; }
+};
+
+// ---------------------------------------------------------------- affine
+// Composition of maps x -> a*x + b over uint32 (mod 2^32).  The later map is
+// applied after the earlier one: (a2,b2) o (a1,b1) = (a2*a1, a2*b1 + b2).
+// This is the matrix-product case of a non-commutative scan operator.
+struct OpAffine : SameCarry<Affine, OpAffine> {
+    __device__ __forceinline__ static Affine identity() { return {1u, 0u}; }
+    __device__ __forceinline__ static Affine combine(Affine e, Affine l)
+    {
+        return {l.a * e.a, l.a * e.b + l.b};
+    }
+};
+
+// ---------------------------------------------------------------- segmented
+// Segmented scan as a scan of (flag, value) pairs: a set flag marks that the
+// span contains a segment head, and a head discards everything before it:
+//   (f1, v1) (+) (f2, v2) = (f1 | f2, f2 ? v2 : v1 (+) v2).
+// The pair operator is associative and not commutative.
+template <typename V>
+struct SegPair {
+    uint32_t f;
+    V v;
+};
+
+template <class Base>
+struct OpSeg {
+    using elem_t = typename Base::elem_t;
+    using bvalue_t = typename Base::value_t;
+    using bcarry_t = typename Base::carry_t;
+    using value_t = SegPair<bvalue_t>;
+    using carry_t = SegPair<bcarry_t>;
+    using prep_t = typename Base::prep_t;
+    static constexpr int kWords = Base::kWords;
+    __device__ __forceinline__ static value_t identity() { return {0u, Base::identity()}; }
+    __device__ __forceinline__ static value_t combine(value_t a, value_t b)
+    {
+        return {a.f | b.f, b.f ? b.v : Base::combine(a.v, b.v)};
+    }
+    __device__ __forceinline__ static carry_t carry_identity() { return {0u, Base::carry_identity()}; }
+    __device__ __forceinline__ static carry_t to_carry(value_t v) { return {v.f, Base::to_carry(v.v)}; }
+    __device__ __forceinline__ static carry_t combine_carry(carry_t a, carry_t b)
+    {
+        return {a.f | b.f, b.f ? b.v : Base::combine_carry(a.v, b.v)};
+    }
+    // The carry's flag never matters when it is applied: only the local flag does.
+    __device__ __forceinline__ static prep_t prepare(carry_t c) { return Base::prepare(c.v); }
+    __device__ __forceinline__ static value_t apply(prep_t c, value_t local)
+    {
+        return {local.f, local.f ? local.v : Base::apply(c, local.v)};
+    }
+    __device__ __forceinline__ static void pack(carry_t c, uint32_t* w, uint32_t& flag)
+    {
+        uint32_t unused;
+        Base::pack(c.v, w, unused);
+        flag = c.f ? 1u : 0u;
+    }
+    __device__ __forceinline__ static carry_t unpack(const uint32_t* w, uint32_t flag)
+    {
+        return {flag, Base::unpack(w, 0u)};
+    }
+};
+
+}  // namespace dwpt

@@ -1,0 +1,162 @@
+/*
+ * dwpt_scan.h -- C ABI of the MI355X (gfx950) device-wide prefix scan library
+ * (libdwpt_scan.so).
+ *
+ * Pages cited:
+ *   [L7]    "Lecture 7: 并行模式五 —— 前缀和 / 扫描：双缓冲与层次化算法"
+ *           (UIUC ECE408 course notes, runguoli.com)
+ *   [PMPP9] "第9章并行模式：前缀和 - Scan算法" (PMPP chapter 9 notes, bittern.cn)
+ *   [YLY]   "CUDA编程并行前缀和扫描详解" (tutorial, m.youleyou.com)
+ *
+ * Conventions shared by every entry point:
+ *   - `in`, `out`, `head_flags` and `d_count` are DEVICE pointers owned by the
+ *     caller (hipMalloc'd or torch CUDA tensors on the current device).  The
+ *     library never frees or keeps them past the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work: they return before the GPU has finished, and
+ *     results (and device-side errors, see scan_get_device_error) are visible
+ *     after the stream is synchronised.
+ *   - n is an element count (pairs for the affine dtype).  n == 0 returns
+ *     SCAN_OK and launches nothing.
+ *   - Pointers must be aligned to the element size; 16-byte alignment selects
+ *     the vector path, anything else a slower scalar path with the same
+ *     results.  `out` may equal `in` (in-place); partial overlap is rejected.
+ *   - Errors are returned, never raised: argument errors (null pointer with
+ *     n > 0, misalignment, partial overlap, n too large) give
+ *     SCAN_ERR_INVALID before anything is launched; an op/dtype pair outside
+ *     the table below gives SCAN_ERR_UNSUPPORTED; a failed HIP call gives
+ *     SCAN_ERR_HIP (hipGetLastError has the HIP code); failure to get
+ *     workspace memory gives SCAN_ERR_NOMEM.
+ *   - Workspace: the multi-tile path keeps a small status array (8 or 16 bytes
+ *     per tile of 2-4 K elements) and a tile counter per (device, stream),
+ *     allocated on first use, grown when needed and reused across calls
+ *     without clearing.  Calls on one stream are serialised by the stream;
+ *     calls on different streams use different workspaces.
+ *
+ * Valid combinations:
+ *   scan_inclusive / scan_exclusive: ADD, MAX, MIN with I32, U32, F32;
+ *                                    AFFINE with U32X2.
+ *   segmented_scan:                  ADD, MAX, MIN with I32, U32, F32.
+ *   compact:                         I32, U32, F32.
+ * Integer ADD wraps modulo 2^32.  F32 ADD results may differ from an exact
+ * sum by rounding (any association is allowed); the prefix carried between
+ * tiles is kept in double so the error stays well inside
+ * 1e-5 * sum_{k<=i} |x_k| + 1e-6.  MAX/MIN keep the earlier value on ties.
+ */
+#ifndef DWPT_SCAN_H
+#define DWPT_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SCAN_OK = 0,
+    SCAN_ERR_INVALID = 1,
+    SCAN_ERR_UNSUPPORTED = 2,
+    SCAN_ERR_NOMEM = 3,
+    SCAN_ERR_HIP = 4,
+    SCAN_ERR_TIMEOUT = 5
+} scan_status_t;
+
+typedef enum {
+    SCAN_OP_ADD = 0,
+    SCAN_OP_MAX = 1,
+    SCAN_OP_MIN = 2,
+    SCAN_OP_AFFINE = 3 /* x -> a*x + b maps composed, later map applied after */
+} scan_op_t;
+
+typedef enum {
+    SCAN_I32 = 0,
+    SCAN_U32 = 1,
+    SCAN_F32 = 2,
+    SCAN_U32X2 = 3 /* (a, b) pairs of uint32, 8 bytes per element */
+} scan_dtype_t;
+
+/*
+ * Inclusive scan: out[i] = in[0] (+) in[1] (+) ... (+) in[i].
+ * [L7 concept 1 "扫描（Scan / Prefix Sum）：inclusive 与 exclusive";
+ *  PMPP9 §9.1; YLY §2.1]  The operator must be associative; operand order is
+ * kept (earlier element on the left), commutativity is never assumed.
+ * For AFFINE, element i of the result is the composition of maps 0..i:
+ * (a2,b2) o (a1,b1) = (a2*a1, a2*b1 + b2) mod 2^32, i.e. its b component is
+ * the recurrence y_i = a_i*y_{i-1} + b_i with y_{-1} = 0 [L7 concept 1,
+ * recurrences as scans].
+ */
+scan_status_t scan_inclusive(scan_op_t op, scan_dtype_t dtype, const void* in, void* out,
+                             size_t n, void* stream);
+
+/*
+ * Exclusive scan: out[0] = identity, out[i] = in[0] (+) ... (+) in[i-1].
+ * [L7 concept 1; PMPP9 §9.1 (identity table); YLY §2.2]  Identities: ADD 0,
+ * MAX the type's lowest value (-inf for F32), MIN its highest (+inf),
+ * AFFINE (1, 0).
+ */
+scan_status_t scan_exclusive(scan_op_t op, scan_dtype_t dtype, const void* in, void* out,
+                             size_t n, void* stream);
+
+/*
+ * Segmented scan: the scan restarts at every element whose head flag is
+ * nonzero; element 0 always starts a segment whatever its flag.
+ * `head_flags` is a device array of n bytes.  Inclusive (exclusive == 0):
+ * out[i] = fold of in[s..i]; exclusive: out[i] = fold of in[s..i-1], the
+ * identity at every head, where s is the head of i's segment.
+ * [L7 concept 2 "扫描的典型应用", radix-sort placement as a segmented scan]
+ */
+scan_status_t segmented_scan(scan_op_t op, scan_dtype_t dtype, const void* in,
+                             const uint8_t* head_flags, void* out, size_t n, int exclusive,
+                             void* stream);
+
+/*
+ * Stream compaction: writes the elements with in[i] > 0, in input order, to
+ * out[0 .. count) and the count (uint32) to *d_count (device memory).
+ * out[count .. n) is left untouched.  The write position of a kept element
+ * is the exclusive scan of the 0/1 predicate flags [L7 concept 2 compaction
+ * figure; PMPP9 §9.6 array compaction; YLY §2.2 flag/pos example].  -0.0
+ * and NaN are not kept.  Requires n < 2^32.
+ */
+scan_status_t compact(scan_dtype_t dtype, const void* in, void* out, uint32_t* d_count, size_t n,
+                      void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* scan_status_string(scan_status_t s);
+
+/*
+ * Synchronises `stream`, then reads and clears the device error word of its
+ * workspace: SCAN_ERR_TIMEOUT if a look-back wait gave up since the last
+ * check (the results of that call are then wrong), SCAN_ERR_HIP if a
+ * workgroup found the tile counter out of step with its launch (it then
+ * skipped its tile), SCAN_OK otherwise.
+ */
+scan_status_t scan_get_device_error(void* stream);
+
+/* Frees every workspace of the calling process (synchronises the device). */
+scan_status_t scan_release_workspace(void);
+
+/*
+ * Tuning and test knobs (process-wide, thread-safe; each returns the old value).
+ * scan_set_small_n_max: inputs with n at or below this size run on one
+ *   workgroup that walks the tiles in order (no workspace, no atomics); larger
+ *   inputs use the multi-tile look-back kernel.  Default 4096.
+ * scan_set_spin_limit: number of look-back polls after which a waiting tile
+ *   gives up, records SCAN_ERR_TIMEOUT (see scan_get_device_error) and
+ *   finishes with a wrong prefix instead of waiting forever.  Default 2^20.
+ */
+size_t scan_set_small_n_max(size_t n_max);
+uint32_t scan_set_spin_limit(uint32_t polls);
+
+/*
+ * Measurement helper, not part of the scan: copies nbytes (a multiple of 16,
+ * 16-byte aligned pointers) from in to out with a plain streaming kernel, to
+ * calibrate achievable HBM bandwidth and the traffic counters.
+ */
+scan_status_t scan_copy_probe(const void* in, void* out, size_t nbytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DWPT_SCAN_H */

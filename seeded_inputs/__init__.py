@@ -24,12 +24,28 @@ Workload recipes (the shapes and value distributions of the scan workloads):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 _CHUNK = 1 << 22
+_THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+def _parallel(n: int, work) -> None:
+    """Run work(c0, c1) over [0, n) in chunks on a thread pool (numpy releases the GIL)."""
+    spans = [(c0, min(n, c0 + _CHUNK)) for c0 in range(0, n, _CHUNK)]
+    if len(spans) <= 1:
+        for c0, c1 in spans:
+            work(c0, c1)
+        return
+    with ThreadPoolExecutor(_THREADS) as ex:
+        for f in [ex.submit(work, c0, c1) for c0, c1 in spans]:
+            f.result()
 
 
 def _mix(z: np.ndarray) -> np.ndarray:
@@ -47,24 +63,31 @@ def _stream_seed(seed: int, stream: int) -> np.uint64:
     return _mix(s)[0]
 
 
+def _draws_span(s: np.uint64, start: int, count: int) -> np.ndarray:
+    ctr = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    ctr *= GAMMA
+    ctr += s
+    return _mix(ctr)
+
+
 def draws(seed: int, n: int, stream: int = 0, start: int = 0) -> np.ndarray:
     """n consecutive 64-bit SplitMix64 draws (counter start..start+n-1)."""
     s = _stream_seed(seed, stream)
     out = np.empty(n, np.uint64)
-    for c0 in range(0, n, _CHUNK):
-        c1 = min(n, c0 + _CHUNK)
-        ctr = np.arange(start + c0 + 1, start + c1 + 1, dtype=np.uint64)
-        ctr *= GAMMA
-        ctr += s
-        out[c0:c1] = _mix(ctr)
+
+    def work(c0, c1):
+        out[c0:c1] = _draws_span(s, start + c0, c1 - c0)
+    _parallel(n, work)
     return out
 
 
 def _map_chunks(seed: int, n: int, stream: int, dtype, fn) -> np.ndarray:
+    s = _stream_seed(seed, stream)
     out = np.empty(n, dtype)
-    for c0 in range(0, n, _CHUNK):
-        c1 = min(n, c0 + _CHUNK)
-        out[c0:c1] = fn(draws(seed, c1 - c0, stream, c0))
+
+    def work(c0, c1):
+        out[c0:c1] = fn(_draws_span(s, c0, c1 - c0))
+    _parallel(n, work)
     return out
 
 
@@ -81,28 +104,30 @@ def float32_01(seed: int, n: int) -> np.ndarray:
 
 def float32_normal(seed: int, n: int) -> np.ndarray:
     """float32 ~ N(0,1), Box-Muller on two independent uniform streams."""
-    def fn_pair(c0, c1):
-        u1 = ((draws(seed, c1 - c0, 1, c0) >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0**-53
-        u2 = (draws(seed, c1 - c0, 2, c0) >> np.uint64(11)).astype(np.float64) * 2.0**-53
-        return (np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)).astype(np.float32)
+    s1, s2 = _stream_seed(seed, 1), _stream_seed(seed, 2)
     out = np.empty(n, np.float32)
-    for c0 in range(0, n, _CHUNK):
-        c1 = min(n, c0 + _CHUNK)
-        out[c0:c1] = fn_pair(c0, c1)
+
+    def work(c0, c1):
+        u1 = ((_draws_span(s1, c0, c1 - c0) >> np.uint64(11)).astype(np.float64) + 0.5) * 2.0**-53
+        u2 = (_draws_span(s2, c0, c1 - c0) >> np.uint64(11)).astype(np.float64) * 2.0**-53
+        out[c0:c1] = (np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)).astype(np.float32)
+    _parallel(n, work)
     return out
 
 
 def affine_pairs(seed: int, n: int, odd_a: bool = False) -> np.ndarray:
     """(n, 2) uint32 pairs (a, b); with odd_a the multipliers are forced odd."""
+    s = _stream_seed(seed, 0)
     out = np.empty((n, 2), np.uint32)
-    for c0 in range(0, n, _CHUNK):
-        c1 = min(n, c0 + _CHUNK)
-        u = draws(seed, c1 - c0, 0, c0)
+
+    def work(c0, c1):
+        u = _draws_span(s, c0, c1 - c0)
         a = (u & np.uint64(0xFFFFFFFF)).astype(np.uint32)
         if odd_a:
             a |= np.uint32(1)
         out[c0:c1, 0] = a
         out[c0:c1, 1] = (u >> np.uint64(32)).astype(np.uint32)
+    _parallel(n, work)
     return out
 
 

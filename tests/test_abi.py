@@ -1,0 +1,86 @@
+"""The C-ABI library loads and exports what include/*.h declares; host-side checks (no GPU).
+
+Nothing here launches a kernel: only calls that are rejected (or are no-ops)
+before the library touches the HIP runtime are made.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from device_wide_prefix_tile_amd import binding
+from device_wide_prefix_tile_amd import build as dbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M):
+            if m.group(1) not in ("if", "while", "for", "return", "sizeof"):
+                names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_scan_calls():
+    names = declared_functions()
+    for n in ("scan_inclusive", "scan_exclusive", "segmented_scan", "compact"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    names = declared_functions()
+    assert names
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert set(binding.EXPORTS) == names
+
+
+def test_library_is_built_for_gfx950():
+    blob = open(dbuild.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_status_strings():
+    for s in range(6):
+        assert binding.status_string(s)
+    assert binding.status_string(99) == "unknown status"
+
+
+def test_argument_checks_before_any_launch():
+    L = binding.lib()
+    ADD, MAX, AFF = 0, 1, 3
+    I32, U32, F32, PAIR = 0, 1, 2, 3
+    # n == 0 is a no-op
+    assert L.scan_inclusive(ADD, F32, None, None, 0, None) == 0
+    assert L.scan_exclusive(MAX, I32, None, None, 0, None) == 0
+    assert L.segmented_scan(ADD, I32, None, None, None, 0, 0, None) == 0
+    # unsupported combinations
+    assert L.scan_inclusive(AFF, F32, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(ADD, PAIR, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(9, I32, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.segmented_scan(AFF, PAIR, 1024, 4096, 2048, 10, 0, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.compact(PAIR, 1024, 2048, 4096, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    # invalid pointers, alignment and overlap
+    assert L.scan_inclusive(ADD, I32, None, 2048, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.scan_inclusive(ADD, I32, 1025, 4096, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.scan_inclusive(AFF, PAIR, 1028, 8192, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.scan_inclusive(ADD, I32, 1024, 1028, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.segmented_scan(ADD, I32, 1024, None, 8192, 10, 0, None) == binding.SCAN_ERR_INVALID
+    assert L.segmented_scan(ADD, I32, 1024, 8192, 8192, 10, 0, None) == binding.SCAN_ERR_INVALID
+    assert L.compact(F32, 1024, 8192, None, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.compact(F32, 1024, 8192, 1 << 20, 1 << 32, None) == binding.SCAN_ERR_INVALID
+    assert L.scan_copy_probe(1024, 2048, 10, None) == binding.SCAN_ERR_INVALID
+
+
+def test_tuning_knobs_round_trip():
+    old = binding.scan_set_small_n_max(12345)
+    assert binding.scan_set_small_n_max(old) == 12345
+    old = binding.scan_set_spin_limit(77)
+    assert binding.scan_set_spin_limit(old) == 77

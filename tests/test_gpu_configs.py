@@ -1,0 +1,88 @@
+"""The five scan workloads at full size, in the launch configuration the benchmark times.
+
+Every output element is compared with the oracle (the C oracle finishes even
+2^30 elements in seconds):
+  1. int32 exclusive add, n = 2^20, values in [0, 15], plus the 8-element
+     worked example of the pages;
+  2. float32 inclusive add, n = 2^28, values in [0, 1), within
+     1e-5 * prefix|x| + 1e-6 of the double-accumulated oracle;
+  3. compaction of float32 N(0,1), n = 2^28, keep x > 0: count and contents
+     bit-exact;
+  4. uint32 affine-map composition, n = 2^26 pairs, inclusive, bit-exact
+     (and the odd-multiplier variant, where no prefix collapses to zero);
+  5. segmented int32 inclusive add, n = 2^27, values in [-100, 100], heads with
+     geometric segment lengths of mean 1000; and an int32 max-scan over
+     n = 2^10 .. 2^30 (powers of 4).
+"""
+import numpy as np
+import pytest
+import torch
+
+import device_wide_prefix_tile_amd as dw
+import oracle
+import seeded_inputs as si
+from parity_helpers import assert_equal, assert_f32_close, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def fresh():
+    yield
+    torch.cuda.empty_cache()
+
+
+def test_config1_int32_exclusive_add_2p20():
+    n = 1 << 20
+    x = si.int32_0_15(1, n)
+    y = from_dev(dw.scan_exclusive(to_dev(x), "add"))
+    assert_equal(y, oracle.scan("add", x, exclusive=True), "config1")
+    ex = np.array([3, 1, 7, 0, 4, 1, 6, 3], np.int32)
+    np.testing.assert_array_equal(from_dev(dw.scan_exclusive(to_dev(ex), "add")), [0, 3, 4, 11, 11, 15, 16, 22])
+    np.testing.assert_array_equal(from_dev(dw.scan_inclusive(to_dev(ex), "add")), [3, 4, 11, 11, 15, 16, 22, 25])
+
+
+def test_config2_f32_inclusive_add_2p28():
+    n = 1 << 28
+    x = si.float32_01(2, n)
+    xd = to_dev(x)
+    y = from_dev(dw.scan_inclusive(xd, "add"))
+    del xd
+    ref, s = oracle.scan("add", x)
+    worst = assert_f32_close(y, ref, s, "config2")
+    print("config2 worst error/tolerance = %.4f" % worst)
+    assert dw.scan_get_device_error() == 0
+
+
+def test_config3_compact_2p28():
+    n = 1 << 28
+    x = si.float32_normal(3, n)
+    out, cnt = dw.compact(to_dev(x))
+    out, cnt = from_dev(out), int(from_dev(cnt)[0])
+    ref, rc, _ = oracle.compact(x)
+    assert cnt == rc
+    assert_equal(out[:cnt], ref, "config3")
+
+
+@pytest.mark.parametrize("odd", [False, True], ids=["any_a", "odd_a"])
+def test_config4_affine_2p26(odd):
+    n = 1 << 26
+    ab = si.affine_pairs(40 if odd else 4, n, odd_a=odd)
+    y = from_dev(dw.scan_inclusive(to_dev(ab), "affine"))
+    assert_equal(y, oracle.scan_affine(ab), "config4 odd=%s" % odd)
+
+
+def test_config5_segmented_add_2p27():
+    n = 1 << 27
+    x = si.int32_pm100(5, n)
+    h = si.segment_heads(5, n, 1000.0)
+    y = from_dev(dw.segmented_scan(to_dev(x), to_dev(h), "add"))
+    assert_equal(y, oracle.segmented_scan("add", x, h), "config5 segmented")
+
+
+@pytest.mark.parametrize("k", range(5, 16))
+def test_config5_max_sweep(k):
+    n = 4 ** k
+    x = si.int32_full(6, n)
+    y = from_dev(dw.scan_inclusive(to_dev(x), "max"))
+    assert_equal(y, oracle.scan("max", x), "config5 max sweep n=4^%d" % k)

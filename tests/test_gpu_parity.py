@@ -1,0 +1,284 @@
+"""GPU parity: the HIP library against the sequential oracle, element by element.
+
+Integer, max/min, affine and compaction results must be bit-exact; float32
+add results must satisfy |y_gpu - y_ref| <= 1e-5 * sum_{k<=i}|x_k| + 1e-6 with
+y_ref accumulated in double.  Sizes span one or several 4096-element tiles
+with ragged tails; each test runs the multi-tile look-back path, and small
+inputs also the single-workgroup path (forced through the small-n knob).
+"""
+import numpy as np
+import pytest
+import torch
+
+import device_wide_prefix_tile_amd as dw
+import golden_fixtures
+import oracle
+import seeded_inputs as si
+from parity_helpers import assert_equal, assert_f32_close, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TILE = 4096
+SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1000, TILE - 1, TILE, TILE + 1, 3 * TILE + 17,
+         65536 + 1, 250001, 1000003]
+NP = {"i32": np.int32, "u32": np.uint32, "f32": np.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    dw.lib()
+    yield
+    dw.scan_set_small_n_max(4096)
+
+
+class Path:
+    """Select the single-workgroup ('single') or look-back ('multi') path, or the default."""
+
+    def __init__(self, which):
+        self.which = which
+
+    def __enter__(self):
+        lim = {"single": 1 << 40, "multi": 0}.get(self.which)
+        self.old = dw.scan_set_small_n_max(lim) if lim is not None else None
+
+    def __exit__(self, *a):
+        if self.old is not None:
+            dw.scan_set_small_n_max(self.old)
+
+
+def paths_for(n):
+    return ["multi", "single"] if n <= 3 * TILE + 17 else ["auto"]
+
+
+def values(dt, n, seed):
+    if dt == "i32":
+        return si.int32_full(seed, n)
+    if dt == "u32":
+        return si.uint32_full(seed, n)
+    return si.float32_sym(seed, n)
+
+
+def check_scan(op, x, y_gpu, exclusive, what):
+    ref = oracle.scan(op, x, exclusive=exclusive)
+    if isinstance(ref, tuple):
+        return assert_f32_close(y_gpu, ref[0], ref[1], what)
+    assert_equal(y_gpu, ref, what)
+
+
+# ---------------------------------------------------------------- worked examples
+@pytest.mark.parametrize("rec", golden_fixtures.all_examples("scan"), ids=lambda r: r["path"].split("/")[-1])
+@pytest.mark.parametrize("path", ["single", "multi"])
+def test_golden_scan_on_gpu(rec, path):
+    for dt in (rec["dtype"], np.int32, np.float32):
+        x = rec["input"].astype(dt)
+        with Path(path):
+            if "inclusive" in rec:
+                y = from_dev(dw.scan_inclusive(to_dev(x), rec["op"]))
+                np.testing.assert_array_equal(y.astype(np.float64), rec["inclusive"].astype(np.float64))
+            if "exclusive" in rec:
+                y = from_dev(dw.scan_exclusive(to_dev(x), rec["op"]))
+                np.testing.assert_array_equal(y.astype(np.float64), rec["exclusive"].astype(np.float64))
+
+
+@pytest.mark.parametrize("rec", golden_fixtures.all_examples("compact"), ids=lambda r: r["path"].split("/")[-1])
+@pytest.mark.parametrize("path", ["single", "multi"])
+def test_golden_compact_on_gpu(rec, path):
+    for dt in (rec["dtype"], np.int32, np.float32):
+        x = rec["input"].astype(dt)
+        with Path(path):
+            out, cnt = dw.compact(to_dev(x))
+            out, cnt = from_dev(out), int(from_dev(cnt)[0])
+        assert cnt == len(rec["output"])
+        np.testing.assert_array_equal(out[:cnt].astype(np.float64), rec["output"].astype(np.float64))
+
+
+# ---------------------------------------------------------------- plain scans
+@pytest.mark.parametrize("dt", ["i32", "u32", "f32"])
+@pytest.mark.parametrize("op", ["add", "max", "min"])
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_scan_parity(op, dt, exclusive):
+    fn = dw.scan_exclusive if exclusive else dw.scan_inclusive
+    for k, n in enumerate(SIZES):
+        x = values(dt, n, 100 + k)
+        xd = to_dev(x)
+        for path in paths_for(n):
+            with Path(path):
+                y = from_dev(fn(xd, op))
+            check_scan(op, x, y, exclusive, "%s %s excl=%s n=%d path=%s" % (op, dt, exclusive, n, path))
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+@pytest.mark.parametrize("odd", [False, True], ids=["any_a", "odd_a"])
+def test_affine_parity(exclusive, odd):
+    fn = dw.scan_exclusive if exclusive else dw.scan_inclusive
+    for k, n in enumerate(SIZES):
+        ab = si.affine_pairs(200 + k, n, odd_a=odd)
+        for path in paths_for(n):
+            with Path(path):
+                y = from_dev(fn(to_dev(ab), "affine"))
+            assert_equal(y, oracle.scan_affine(ab, exclusive=exclusive),
+                         "affine excl=%s odd=%s n=%d path=%s" % (exclusive, odd, n, path))
+
+
+# ---------------------------------------------------------------- segmented scans
+HEAD_MIXES = {
+    "mean1000": lambda s, n: si.segment_heads(s, n, 1000.0),
+    "mean3": lambda s, n: si.segment_heads(s, n, 3.0),
+    "mean5000": lambda s, n: si.segment_heads(s, n, 5000.0),
+    "all": lambda s, n: np.ones(n, np.uint8),
+    "first_only": lambda s, n: np.zeros(n, np.uint8),
+    "tile_starts": lambda s, n: (np.arange(n) % TILE == 0).astype(np.uint8) * 7,
+}
+
+
+@pytest.mark.parametrize("dt", ["i32", "u32", "f32"])
+@pytest.mark.parametrize("op", ["add", "max", "min"])
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_segmented_parity(op, dt, exclusive):
+    for k, n in enumerate([1, 2, 65, TILE - 1, TILE + 1, 3 * TILE + 17, 250001, 1000003]):
+        x = values(dt, n, 300 + k) if dt != "i32" else si.int32_pm100(300 + k, n)
+        for mix, gen in HEAD_MIXES.items():
+            h = gen(400 + k, n)
+            xd, hd = to_dev(x), to_dev(h)
+            for path in paths_for(n):
+                with Path(path):
+                    y = from_dev(dw.segmented_scan(xd, hd, op, exclusive=exclusive))
+                ref = oracle.segmented_scan(op, x, h, exclusive=exclusive)
+                what = "seg %s %s excl=%s n=%d heads=%s path=%s" % (op, dt, exclusive, n, mix, path)
+                if isinstance(ref, tuple):
+                    assert_f32_close(y, ref[0], ref[1], what)
+                else:
+                    assert_equal(y, ref, what)
+
+
+def test_segmented_head_zero_flag_ignored():
+    x = np.arange(1, 10001, dtype=np.int32)
+    h = np.zeros(x.size, np.uint8)
+    h[5000] = 1
+    for path in ("single", "multi"):
+        with Path(path):
+            y = from_dev(dw.segmented_scan(to_dev(x), to_dev(h), "add"))
+        assert_equal(y, oracle.segmented_scan("add", x, h), "head[0]=0 path=%s" % path)
+
+
+# ---------------------------------------------------------------- compaction
+def compact_inputs(dt, n, seed):
+    if dt == "f32":
+        return si.float32_normal(seed, n)
+    if dt == "i32":
+        return si.int32_full(seed, n)
+    u = si.uint32_full(seed, n)
+    u[si.segment_heads(seed, n, 2.0).astype(bool)] = 0
+    return u
+
+
+@pytest.mark.parametrize("dt", ["i32", "u32", "f32"])
+def test_compact_parity(dt):
+    for k, n in enumerate([0] + SIZES):
+        x = compact_inputs(dt, n, 500 + k)
+        xd = to_dev(x) if n else torch.empty(0, dtype={"i32": torch.int32, "u32": torch.uint32,
+                                                         "f32": torch.float32}[dt], device="cuda")
+        for path in paths_for(n):
+            with Path(path):
+                out, cnt = dw.compact(xd)
+                out, cnt = from_dev(out), int(from_dev(cnt)[0])
+            ref, rc, _ = oracle.compact(x)
+            what = "compact %s n=%d path=%s" % (dt, n, path)
+            assert cnt == rc, what
+            assert_equal(out[:cnt], ref, what)
+
+
+def test_compact_special_values():
+    x = np.array([0.0, -0.0, np.nan, 1.0, -1.0, np.inf, -np.inf, 1e-45, -1e-45] * 1000, np.float32)
+    for path in ("single", "multi"):
+        with Path(path):
+            out, cnt = dw.compact(to_dev(x))
+            out, cnt = from_dev(out), int(from_dev(cnt)[0])
+        ref, rc, _ = oracle.compact(x)
+        assert cnt == rc == 3000
+        assert_equal(out[:cnt], ref, "special values path=%s" % path)
+
+
+def test_compact_leaves_tail_untouched():
+    x = si.float32_normal(9, 20000)
+    out = torch.full((20000,), 12345.0, device="cuda")
+    o, cnt = dw.compact(to_dev(x), out=out)
+    o, cnt = from_dev(o), int(from_dev(cnt)[0])
+    assert np.all(o[cnt:] == 12345.0)
+
+
+# ---------------------------------------------------------------- closed forms, layouts
+def test_all_ones_float_is_bit_exact():
+    # every prefix of ones is an integer <= 2^24: exact in float32 under any association
+    n = 1 << 24
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    ye = from_dev(dw.scan_exclusive(x))
+    yi = from_dev(dw.scan_inclusive(x))
+    np.testing.assert_array_equal(ye, np.arange(n, dtype=np.float32))
+    np.testing.assert_array_equal(yi, np.arange(1, n + 1, dtype=np.float32))
+
+
+@pytest.mark.parametrize("n", [5000, 1000003])
+def test_in_place(n):
+    x = si.int32_full(61, n)
+    t = to_dev(x)
+    dw.scan_inclusive(t, "add", out=t)
+    assert_equal(from_dev(t), oracle.scan("add", x), "in-place scan n=%d" % n)
+    h = si.segment_heads(62, n, 50.0)
+    t = to_dev(x)
+    dw.segmented_scan(t, to_dev(h), "max", exclusive=True, out=t)
+    assert_equal(from_dev(t), oracle.segmented_scan("max", x, h, exclusive=True), "in-place seg n=%d" % n)
+    f = si.float32_normal(63, n)
+    t = to_dev(f)
+    _, cnt = dw.compact(t, out=t)
+    ref, rc, _ = oracle.compact(f)
+    cnt = int(from_dev(cnt)[0])
+    assert cnt == rc
+    assert_equal(from_dev(t)[:cnt], ref, "in-place compact n=%d" % n)
+
+
+@pytest.mark.parametrize("n", [4097, 1000003])
+def test_unaligned_views(n):
+    # a view at a 4-byte offset takes the scalar path; results are the same
+    x = si.float32_sym(71, n + 1)
+    xd = to_dev(x)[1:]
+    out = torch.empty(n + 1, dtype=torch.float32, device="cuda")[1:]
+    y = from_dev(dw.scan_inclusive(xd, "add", out=out))
+    ref, s = oracle.scan("add", x[1:])
+    assert_f32_close(y, ref, s, "unaligned add n=%d" % n)
+    xi = si.int32_full(72, n + 1)
+    y = from_dev(dw.scan_exclusive(to_dev(xi)[1:], "min"))
+    assert_equal(y, oracle.scan("min", xi[1:], exclusive=True), "unaligned min n=%d" % n)
+
+
+def test_workspace_reuse_across_calls_and_streams():
+    # status words of earlier calls (other ops, sizes, payload widths) must read as empty
+    xs = [si.int32_full(80 + k, n) for k, n in enumerate([1000003, 70001, 4 * 1000003, 9000])]
+    fs = si.float32_01(85, 2000003)
+    s2 = torch.cuda.Stream()
+    for rep in range(3):
+        for x in xs:
+            assert_equal(from_dev(dw.scan_inclusive(to_dev(x), "add")), oracle.scan("add", x), "reuse add")
+            y, s = oracle.scan("add", fs)
+            assert_f32_close(from_dev(dw.scan_inclusive(to_dev(fs), "add")), y, s, "reuse f32")
+            with torch.cuda.stream(s2):
+                yd = dw.scan_exclusive(to_dev(x), "max")
+            s2.synchronize()
+            assert_equal(from_dev(yd), oracle.scan("max", x, exclusive=True), "reuse max stream2")
+    assert dw.scan_get_device_error() == 0
+
+
+def test_repeat_runs_bit_exact():
+    # one passing run proves little for a protocol with races: repeat and compare
+    n = (1 << 22) + 123
+    x = si.int32_0_15(90, n)
+    ab = si.affine_pairs(91, n // 2, odd_a=True)
+    ref = oracle.scan("add", x, exclusive=True)
+    ref_ab = oracle.scan_affine(ab)
+    xd, abd = to_dev(x), to_dev(ab)
+    for rep in range(20):
+        assert_equal(from_dev(dw.scan_exclusive(xd, "add")), ref, "repeat %d add" % rep)
+        if rep % 4 == 0:
+            assert_equal(from_dev(dw.scan_inclusive(abd, "affine")), ref_ab, "repeat %d affine" % rep)
+    assert dw.scan_get_device_error() == 0
