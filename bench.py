@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the device-wide prefix scan on one MI355X.
+
+Default workload (the headline metric): float32 inclusive add-scan of
+n = 2^28 values uniform in [0, 1) (seed 2), input and output resident in HBM.
+One step is one scan_inclusive call over the whole array (a single
+multi-tile look-back kernel launch).  W untimed warm-up steps, then K timed
+steps between two device synchronisations; each launch is also bracketed by
+HIP events on the stream it runs on, which gives the kernel's average
+duration for the roofline entry.
+
+Prints one JSON line.  value = Gelem/s (n * K / elapsed).  Effective HBM
+traffic counts the minimal 1 read + 1 write per element (8 bytes).
+
+Also reported:
+  roofline      HBM-bound: algorithmic bytes per launch / average launch time
+                against MI355X's 8 TB/s; `traffic` is the counter-measured HBM
+                bytes per launch from the committed rocprofv3 summary, used only
+                while the kernel sources still match the ones it was taken on.
+  cpu_baseline  the sequential oracle on one host core over a bounded sample
+                (the first 2^26 elements of the same input).
+  copy_probe    a plain 16-byte streaming copy of 1 GiB, for the achievable
+                bandwidth on this machine.
+
+--suite FILE additionally times every scan workload (int32 exclusive add at
+2^20 and 2^28, compaction, affine, segmented add, the max-scan size sweep)
+and writes one JSON line per workload to FILE.
+"""
+import argparse
+import hashlib
+import glob
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0
+N_MAIN = 1 << 28
+METRIC = "scan Gelem/s + effective HBM GB/s (% of peak), fp32/int32 n=2^28, 1 MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_f32_inclusive_add_2p28.json")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "device_wide_prefix_tile_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per launch from the committed counter summary, if it matches the sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Run fn() warmup times, then `steps` times between synchronisations.
+
+    Returns (elapsed seconds of the timed region, list of per-launch event ms).
+    """
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    return elapsed, [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(x):
+    import oracle
+    sample = x[: 1 << 26]
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 2 or (time.perf_counter() - t_start < 10.0 and len(times) < 20):
+        t0 = time.perf_counter()
+        y, s = oracle.scan("add", sample)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": round(sample.shape[0] / med / 1e9, 4), "unit": "Gelem/s", "cores": 1, "kind": "oracle",
+            "sample": "first 2^26 of the 2^28 float32 inputs, sequential double-accumulated inclusive add, "
+                      "median of %d runs" % len(times)}, (y, s)
+
+
+def copy_probe(dw, torch, nbytes=1 << 30, reps=20):
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    elapsed, ms = time_launches(lambda: dw.scan_copy_probe(a, b), reps, 3, torch)
+    del a, b
+    return round(2 * nbytes / (statistics.mean(ms) * 1e-3) / 1e9, 1)
+
+
+def suite(dw, torch, si, out_path, steps):
+    """Time each workload at its full size; one JSON line per workload."""
+    import numpy as np
+    lines = []
+
+    def rec(name, n, bytes_per_elem, fn):
+        log("suite: " + name)
+        elapsed, ms = time_launches(fn, steps, 3, torch)
+        t = statistics.median(ms) * 1e-3
+        lines.append({"workload": name, "n": n, "median_us": round(t * 1e6, 2),
+                      "gelem_s": round(n / t / 1e9, 2),
+                      "effective_GBps": round(n * bytes_per_elem / t / 1e9, 1),
+                      "pct_of_peak": round(100 * n * bytes_per_elem / t / 1e9 / PEAK_GBPS, 1)})
+
+    x = torch.from_numpy(si.int32_0_15(1, 1 << 20)).cuda()
+    y = torch.empty_like(x)
+    rec("int32 exclusive add 2^20", 1 << 20, 8, lambda: dw.scan_exclusive(x, "add", out=y))
+    x = torch.from_numpy(si.int32_0_15(1, 1 << 28)).cuda()
+    y = torch.empty_like(x)
+    rec("int32 exclusive add 2^28", 1 << 28, 8, lambda: dw.scan_exclusive(x, "add", out=y))
+    rec("int32 inclusive max 2^28", 1 << 28, 8, lambda: dw.scan_inclusive(x, "max", out=y))
+    del x, y
+    xc = torch.from_numpy(si.float32_normal(3, 1 << 28)).cuda()
+    yc = torch.empty_like(xc)
+    cnt = torch.zeros(1, dtype=torch.uint32, device="cuda")
+    dw.compact(xc, out=yc, count=cnt)
+    torch.cuda.synchronize()
+    kept = int(cnt.cpu().numpy()[0])
+    rec("compaction float32 N(0,1) 2^28 (bytes: read all + write kept)", 1 << 28, 4 + 4 * kept / (1 << 28),
+        lambda: dw.compact(xc, out=yc, count=cnt))
+    del xc, yc
+    ab = torch.from_numpy(si.affine_pairs(4, 1 << 26)).cuda()
+    yab = torch.empty_like(ab)
+    rec("uint32 affine inclusive 2^26 pairs", 1 << 26, 16, lambda: dw.scan_inclusive(ab, "affine", out=yab))
+    del ab, yab
+    xs = torch.from_numpy(si.int32_pm100(5, 1 << 27)).cuda()
+    hs = torch.from_numpy(si.segment_heads(5, 1 << 27, 1000.0)).cuda()
+    ys = torch.empty_like(xs)
+    rec("segmented int32 inclusive add 2^27", 1 << 27, 9, lambda: dw.segmented_scan(xs, hs, "add", out=ys))
+    del xs, hs, ys
+    for k in range(5, 16):
+        n = 4 ** k
+        xm = torch.from_numpy(si.int32_full(6, n)).cuda()
+        ym = torch.empty_like(xm)
+        rec("int32 inclusive max 4^%d" % k, n, 8, lambda: dw.scan_inclusive(xm, "max", out=ym))
+        del xm, ym
+    torch.cuda.empty_cache()
+    with open(out_path, "w") as f:
+        for l in lines:
+            f.write(json.dumps(l) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--suite", metavar="FILE", help="also time every workload, JSON lines to FILE")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (--gpus %d requested); "
+              "the scan is not sharded across GPUs" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import device_wide_prefix_tile_amd as dw
+    import seeded_inputs as si
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dw.lib()
+    log("generating input")
+    x_host = si.float32_01(2, N_MAIN)
+    x = torch.from_numpy(x_host).cuda()
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+
+    log("timing %d steps after %d warm-up steps" % (args.steps, args.warmup))
+    elapsed, ms = time_launches(lambda: dw.scan_inclusive(x, "add", out=y), args.steps, args.warmup, torch)
+    assert dw.scan_get_device_error() == 0, "device reported a look-back timeout"
+    value = N_MAIN * args.steps / elapsed / 1e9
+    bytes_per_launch = 8 * N_MAIN
+    avg_kernel_s = statistics.mean(ms) * 1e-3
+    achieved = bytes_per_launch / avg_kernel_s / 1e9
+    traffic = counter_traffic()
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "Gelem/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "float32 inclusive add-scan, n=2^28, values uniform in [0,1) (seed 2)",
+                   "n": N_MAIN, "op": "add", "variant": "inclusive", "element": "float32",
+                   "kernel": "single-pass tile scan with decoupled look-back, 4096-element tiles"},
+        "effective_GBps": round(bytes_per_launch * args.steps / elapsed / 1e9, 1),
+        "pct_of_peak": round(100 * bytes_per_launch * args.steps / elapsed / 1e9 / PEAK_GBPS, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel_avg_us": round(avg_kernel_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": bytes_per_launch},
+    }
+    log("copy probe")
+    result["copy_probe_GBps"] = copy_probe(dw, torch)
+
+    # output check on the oracle's sample, and the last element against a double sum
+    y_host = y.cpu().numpy()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        base, (ref, s) = cpu_baseline(x_host)
+        result["cpu_baseline"] = base
+        k = ref.shape[0]
+        ok = bool(np.all(np.abs(y_host[:k] - ref) <= 1e-5 * s + 1e-6))
+        result["parity_sample_ok"] = ok
+    total = float(np.sum(x_host, dtype=np.float64))
+    result["parity_last_ok"] = bool(abs(float(y_host[-1]) - total) <= 1e-5 * total + 1e-6)
+    del x, y
+    torch.cuda.empty_cache()
+    if args.suite:
+        suite(dw, torch, si, args.suite, max(10, args.steps // 2))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

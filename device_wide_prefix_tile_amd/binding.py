@@ -22,7 +22,7 @@ _DTYPES = {torch.int32: SCAN_I32, torch.uint32: SCAN_U32, torch.float32: SCAN_F3
 
 EXPORTS = ("scan_inclusive", "scan_exclusive", "segmented_scan", "compact", "scan_status_string",
            "scan_get_device_error", "scan_release_workspace", "scan_set_small_n_max",
-           "scan_set_spin_limit", "scan_copy_probe")
+           "scan_set_spin_limit", "scan_set_multi_tile_mode", "scan_copy_probe")
 
 _lib = None
 
@@ -52,6 +52,7 @@ def lib() -> ctypes.CDLL:
         "scan_release_workspace": ([], I),
         "scan_set_small_n_max": ([S], S),
         "scan_set_spin_limit": ([U], U),
+        "scan_set_multi_tile_mode": ([I], I),
         "scan_copy_probe": ([P, P, S, P], I),
     }
     for name, (argtypes, restype) in sig.items():
@@ -159,6 +160,11 @@ def scan_release_workspace():
 
 def scan_set_small_n_max(n_max: int) -> int:
     return int(lib().scan_set_small_n_max(int(n_max)))
+
+
+def scan_set_multi_tile_mode(mode: int) -> int:
+    """0: persistent pipelined kernel (default); 1: one workgroup per tile."""
+    return int(lib().scan_set_multi_tile_mode(int(mode)))
 
 
 def scan_set_spin_limit(polls: int) -> int:

@@ -3,6 +3,7 @@
 // The kernels are in tile_scan.hpp; the ABI is documented in dwpt_scan.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <new>
@@ -16,19 +17,31 @@ using namespace dwpt;
 namespace {
 
 // ------------------------------------------------------------ tile shapes
-// 256 threads (4 wavefronts); 16 four-byte or 8 eight-byte elements per
-// thread, i.e. 16 KiB tiles.
+// Workgroup size and elements per lane (defaults: 1024 threads = 15 data
+// wavefronts + 1 look-back wavefront, 16 four-byte or 8 eight-byte elements
+// per lane, i.e. 60 KiB tiles); build-time switches so that shapes can be
+// compared by measurement.
+#ifndef DWPT_BLOCK
+#define DWPT_BLOCK 1024
+#endif
+#ifndef DWPT_ITEMS4
+#define DWPT_ITEMS4 16
+#endif
+#ifndef DWPT_ITEMS8
+#define DWPT_ITEMS8 8
+#endif
 template <class Op>
 struct Shape {
-    static constexpr int BLOCK = 256;
-    static constexpr int ITEMS = sizeof(typename Op::elem_t) == 8 ? 8 : 16;
-    static constexpr int TILE = BLOCK * ITEMS;
+    static constexpr int BLOCK = DWPT_BLOCK;
+    static constexpr int ITEMS = sizeof(typename Op::elem_t) == 8 ? DWPT_ITEMS8 : DWPT_ITEMS4;
+    static constexpr int TILE = Geometry<Op, BLOCK, ITEMS>::TILE;
 };
 
 // ------------------------------------------------------------ settings
 std::mutex g_mu;
 size_t g_small_n_max = 4096;          // n at or below: single-workgroup path
 uint32_t g_spin_limit = 1u << 20;     // look-back polls before giving up (about a second)
+int g_multi_mode = 0;                 // 0: persistent pipelined kernel; 1: one tile per workgroup
 
 // ------------------------------------------------------------ workspaces
 struct Workspace {
@@ -115,11 +128,35 @@ struct Call {
 
 bool is_aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Fills params and launches either the single-workgroup or the multi-tile
-// kernel.  KS / KM are the two kernel instances, TILE the tile size and
-// kWords the status words per tile.
+// Resident workgroups of kernel `f` on the current device (cached).
+int resident_capacity(const void* f, int block)
+{
+    static std::map<std::pair<int, const void*>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const auto key = std::make_pair(dev, f);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int per_cu = 0, cus = 0, coop = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, block, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        per_cu = 0;
+    }
+    const int cap = coop ? per_cu * cus : 0;
+    cache[key] = cap;
+    return cap;
+}
+
+// Fills params and launches the single-workgroup kernel (small n), else the
+// persistent pipelined kernel (cooperative launch, every workgroup
+// resident), else -- when a cooperative launch is not possible -- the
+// one-tile-per-workgroup kernel.  TILE is the tile size and kWords the
+// status words per tile.
 template <int BLOCK, int TILE, int kWords>
-scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), const Call& c, bool vec_ok)
+scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(ScanParams), const Call& c,
+                     bool vec_ok)
 {
     ScanParams p{};
     p.in = c.in;
@@ -138,14 +175,29 @@ scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), const Call&
         return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
     }
     Workspace* ws = nullptr;
-    const scan_status_t st = acquire_workspace(c.stream, (size_t)tiles * kWords, &ws);
+    // per tile: its status, and a second word set for group statuses (one-tile-per-workgroup
+    // kernel) or the resolver's published prefixes (persistent kernel)
+    const scan_status_t st = acquire_workspace(c.stream, (size_t)(2 * tiles) * kWords, &ws);
     if (st != SCAN_OK) return st;
     p.tile_ctr = ws->ctr;
     p.ctr_base = ws->ctr_base;
     p.lb.status = ws->status;
+    p.lb.groups = ws->status + (size_t)tiles * kWords;
     p.lb.err = ws->err;
     p.lb.epoch = ws->epoch;
     p.lb.spin_limit = g_spin_limit;
+    if (g_multi_mode == 0) {
+        const int cap = resident_capacity((const void*)kp, BLOCK);
+        if (cap > 1) {
+            // workgroup 0 resolves prefixes; the others scan tiles
+            const unsigned grid = 1u + (unsigned)std::min<uint64_t>((uint64_t)cap - 1, tiles);
+            void* args[] = {&p};
+            if (hipLaunchCooperativeKernel((const void*)kp, dim3(grid), dim3(BLOCK), args, 0, c.stream) ==
+                hipSuccess)
+                return SCAN_OK;
+            (void)hipGetLastError();  // not possible right now: one tile per workgroup instead
+        }
+    }
     hipLaunchKernelGGL(km, dim3(p.num_tiles), dim3(BLOCK), 0, c.stream, p);
     if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
     ws->ctr_base += p.num_tiles;  // every workgroup takes exactly one tile number
@@ -157,16 +209,17 @@ scan_status_t run_scan(const Call& c, bool vec_ok)
 {
     using S = Shape<Op>;
     return launch<S::BLOCK, S::TILE, Op::kWords>(tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, true>,
-                                                 tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, false>, c,
-                                                 vec_ok);
+                                                 tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, false>,
+                                                 tile_scan_persistent<Op, EXCL, S::BLOCK, S::ITEMS>, c, vec_ok);
 }
 
 template <typename T>
 scan_status_t run_compact(const Call& c, bool vec_ok)
 {
-    constexpr int BLOCK = 256, ITEMS = 16;
-    return launch<BLOCK, BLOCK * ITEMS, 1>(compact_kernel<T, BLOCK, ITEMS, true>,
-                                           compact_kernel<T, BLOCK, ITEMS, false>, c, vec_ok);
+    constexpr int BLOCK = DWPT_BLOCK, ITEMS = DWPT_ITEMS4;
+    return launch<BLOCK, Geometry<OpAdd<uint32_t>, BLOCK, ITEMS>::TILE, 1>(
+        compact_kernel<T, BLOCK, ITEMS, true>, compact_kernel<T, BLOCK, ITEMS, false>,
+        compact_persistent<T, BLOCK, ITEMS>, c, vec_ok);
 }
 
 typedef scan_status_t (*Runner)(const Call&, bool);
@@ -351,6 +404,14 @@ size_t scan_set_small_n_max(size_t n_max)
     std::lock_guard<std::mutex> lock(g_mu);
     const size_t old = g_small_n_max;
     g_small_n_max = n_max;
+    return old;
+}
+
+int scan_set_multi_tile_mode(int mode)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    const int old = g_multi_mode;
+    g_multi_mode = mode ? 1 : 0;
     return old;
 }
 

@@ -5,22 +5,25 @@
 //           (UIUC ECE408 course notes, runguoli.com)
 //   [PMPP9] "第9章并行模式：前缀和 - Scan算法" (PMPP chapter 9 notes, bittern.cn)
 //
-// One workgroup scans one tile of TILE = BLOCK * ITEMS elements:
+// One workgroup scans one tile of TILE = ND * 64 * ITEMS elements, with ND =
+// BLOCK/64 - 1 data wavefronts and one look-back wavefront:
 //   1. take the next tile number from a counter (start order, not hardware
 //      order);
-//   2. load the tile with 16-byte loads: wavefront w owns 64 * ITEMS
+//   2. load the tile with 16-byte loads: data wavefront w owns 64 * ITEMS
 //      consecutive elements, in R = ITEMS / VEC rounds of 64 * VEC elements,
 //      lane l holding VEC consecutive elements of each round, so every load
 //      instruction of a wavefront reads 1 KiB of contiguous memory;
 //   3. scan each lane's VEC elements serially in registers (thread
 //      coarsening, [L7 concept 6 and its kernel-2 register array]);
 //   4. scan the lane totals across the wavefront with DPP (wave_ops.hpp);
-//   5. combine the wavefront totals through LDS with one barrier;
-//   6. wavefront 0 publishes the tile total, looks back for the prefix of all
-//      earlier tiles and publishes the tile's inclusive prefix
-//      (lookback.hpp) -- this replaces the hierarchical scan's second and
-//      third kernels [L7 concept 6], so the data cross HBM once each way;
-//   7. apply the prefix and store with 16-byte stores.
+//   5. combine the wavefront totals through LDS: the last data wavefront to
+//      arrive forms the tile total and publishes it;
+//   6. meanwhile the look-back wavefront has been folding the earlier tiles'
+//      published totals (two-level decoupled look-back, lookback.hpp); it
+//      publishes the tile's inclusive prefix -- this replaces the
+//      hierarchical scan's second and third kernels [L7 concept 6], so the
+//      data cross HBM once each way;
+//   7. after one barrier, apply the prefix and store with 16-byte stores.
 // Exclusive scans put the identity at y[0] and use the value before each
 // element [L7 concept 1; PMPP9 §9.1].  The tail tile pads with the identity
 // in registers and never stores the padding.  In SINGLE mode one workgroup
@@ -29,9 +32,9 @@
 //
 // Compaction [L7 concept 2 "扫描的典型应用"; PMPP9 §9.6]: the predicate
 // x > 0 is evaluated in registers, the 0/1 flags are scanned the same way
-// (uint32 count), kept elements are packed in LDS at their rank inside the
-// tile and written out as one contiguous run at the tile's prefix count, so
-// flags and positions never touch HBM.
+// (uint32 count), each wavefront packs its kept elements in LDS in order and
+// writes them out as one contiguous run at the tile's prefix count plus the
+// counts of the earlier wavefronts, so flags and positions never touch HBM.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -80,11 +83,26 @@ __device__ __forceinline__ bool resets(typename Op::value_t v)
     else return false;
 }
 
+// Build-time tuning switches (chosen by measurement; see the defaults).
+#ifndef DWPT_NT_LOADS
+#define DWPT_NT_LOADS 0   // streaming (non-temporal) hint on tile loads
+#endif
+#ifndef DWPT_NT_STORES
+#define DWPT_NT_STORES 0  // streaming (non-temporal) hint on tile stores
+#endif
+#ifndef DWPT_STATIC_TILES
+#define DWPT_STATIC_TILES 0  // 1: tile number = workgroup index instead of a counter
+#endif
+
 template <typename E, int VEC>
 __device__ __forceinline__ void load_vec(const E* p, E (&e)[VEC])
 {
     static_assert(sizeof(E) * VEC == 16, "16-byte vector");
+#if DWPT_NT_LOADS
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
     const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#endif
     __builtin_memcpy(e, &v, 16);
 }
 template <typename E, int VEC>
@@ -92,182 +110,276 @@ __device__ __forceinline__ void store_vec(E* p, const E (&e)[VEC])
 {
     u32x4 v;
     __builtin_memcpy(&v, e, 16);
+#if DWPT_NT_STORES
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+#else
     *reinterpret_cast<u32x4*>(p) = v;
+#endif
+}
+
+// Tile number of this workgroup: taken from a counter in the order
+// workgroups start, so a tile only ever waits on tiles that have started.
+// Returns num_tiles (and records an error) if the counter is out of step.
+__device__ __forceinline__ uint32_t take_tile(const ScanParams& p, uint32_t* s_tile)
+{
+#if DWPT_STATIC_TILES
+    (void)s_tile;
+    __syncthreads();
+    return blockIdx.x;
+#else
+    if (threadIdx.x == 0)
+        *s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - p.ctr_base;
+    __syncthreads();
+    const uint32_t tile = *s_tile;
+    if (tile >= p.num_tiles && threadIdx.x == 0)
+        __hip_atomic_fetch_or(p.lb.err, (uint32_t)kErrCounter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return tile;
+#endif
+}
+
+// ------------------------------------------------------------------ pieces
+// Tile geometry: ND data wavefronts of 64 lanes, each lane holding R rounds
+// of VEC consecutive elements (ITEMS = R * VEC per lane); the last wavefront
+// of the workgroup does the look-back.
+template <class Op, int BLOCK, int ITEMS>
+struct Geometry {
+    using E = typename Op::elem_t;
+    static constexpr int VEC = 16 / (int)sizeof(E);
+    static constexpr int R = ITEMS / VEC;
+    static constexpr int NW = BLOCK / 64;
+    static constexpr int ND = NW - 1;
+    static constexpr int WAVE_ELEMS = 64 * ITEMS;
+    static constexpr int TILE = ND * WAVE_ELEMS;
+    static_assert(ITEMS % VEC == 0 && BLOCK % 64 == 0 && NW >= 2, "tile shape");
+};
+
+// Loads one wavefront's share of a tile (2): 16-byte loads when the whole
+// tile is in range and the pointers are aligned, else element loads with the
+// identity past n.  raw_head[r] bit j: element j of round r is a segment head.
+template <class Op, int R, int VEC>
+__device__ __forceinline__ void load_wave(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
+                                          typename Op::value_t (&x)[R][VEC], uint32_t (&raw_head)[R])
+{
+    using E = typename Op::elem_t;
+    constexpr bool SEG = IsSeg<Op>::value;
+    const E* __restrict__ in = static_cast<const E*>(p.in);
+    if (vec) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
+            E e[VEC];
+            load_vec<E, VEC>(in + i0, e);
+            uint32_t hb = 0;
+            if constexpr (SEG) {
+                const uint32_t h4 = *reinterpret_cast<const uint32_t*>(p.heads + i0);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) hb |= ((h4 >> (8 * j)) & 0xFFu) ? (1u << j) : 0u;
+                if (i0 == 0) hb |= 1u;
+            }
+            raw_head[r] = hb;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) x[r][j] = make_value<Op>(e[j], (hb >> j) & 1u);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
+            uint32_t hb = 0;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const uint64_t i = i0 + j;
+                if (i < p.n) {
+                    uint32_t h = 0;
+                    if constexpr (SEG) h = (i == 0 || p.heads[i]) ? 1u : 0u;
+                    hb |= h << j;
+                    x[r][j] = make_value<Op>(in[i], h);
+                } else {
+                    x[r][j] = Op::identity();
+                }
+            }
+            raw_head[r] = hb;
+        }
+    }
+}
+
+// Serial scan of each lane's elements (3) and wavefront scans of the lane
+// totals (4): afterwards x holds in-lane inclusive prefixes, lane_excl[r]
+// the fold of the lower lanes' round-r totals and round_carry[r] the fold of
+// the wavefront's rounds before r (round_carry[R]: the wavefront total).
+template <class Op, int R, int VEC>
+__device__ __forceinline__ void scan_wave(typename Op::value_t (&x)[R][VEC], typename Op::value_t (&lane_excl)[R],
+                                          typename Op::value_t (&round_carry)[R + 1])
+{
+    using V = typename Op::value_t;
+    const V ident = Op::identity();
+    const auto comb = [](V a, V b) { return Op::combine(a, b); };
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 1; j < VEC; ++j) x[r][j] = Op::combine(x[r][j - 1], x[r][j]);
+    round_carry[0] = ident;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const V incl = wave_inclusive_scan(x[r][VEC - 1], ident, comb);
+        lane_excl[r] = wave_shift_up(incl, ident);
+        round_carry[r + 1] = Op::combine(round_carry[r], read_lane(incl, 63));
+    }
+}
+
+// Applies the prefix of everything before the lane's elements and stores (7).
+template <class Op, bool EXCL, int R, int VEC>
+__device__ __forceinline__ void apply_store(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
+                                            typename Op::carry_t P, typename Op::value_t wave_prefix,
+                                            const typename Op::value_t (&x)[R][VEC],
+                                            const typename Op::value_t (&lane_excl)[R],
+                                            const typename Op::value_t (&round_carry)[R + 1],
+                                            const uint32_t (&raw_head)[R])
+{
+    using E = typename Op::elem_t;
+    using V = typename Op::value_t;
+    constexpr bool SEG = IsSeg<Op>::value;
+    const V ident = Op::identity();
+    E* __restrict__ out = static_cast<E*>(p.out);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const V in_tile = Op::combine(Op::combine(wave_prefix, round_carry[r]), lane_excl[r]);
+        const typename Op::prep_t pc = Op::prepare(Op::combine_carry(P, Op::to_carry(in_tile)));
+        E e[VEC];
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            V y;
+            if constexpr (EXCL) {
+                y = Op::apply(pc, j == 0 ? ident : x[r][j - 1]);
+                if constexpr (SEG)
+                    if ((raw_head[r] >> j) & 1u) y = ident;
+            } else {
+                y = Op::apply(pc, x[r][j]);
+            }
+            e[j] = elem_of<Op>(y);
+        }
+        const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
+        if (vec) {
+            store_vec<E, VEC>(out + i0, e);
+        } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                if (i0 + j < p.n) out[i0 + j] = e[j];
+        }
+    }
+}
+
+// Data wavefront w hands its total over; the last one to arrive combines all
+// totals, publishes the tile's AGGREGATE (or PREFIX, when it is already
+// known) and releases the look-back wavefront.
+template <class Op, int ND>
+__device__ __forceinline__ void hand_over(const ScanParams& p, uint32_t tile, int w, int lane,
+                                          typename Op::value_t wave_total, typename Op::value_t* s_wave,
+                                          TileHandover* h, typename Op::carry_t* s_total, bool* s_known)
+{
+    using V = typename Op::value_t;
+    if (lane == 0) s_wave[w] = wave_total;
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(&h->arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != (uint32_t)(ND - 1)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // every lane sees the other totals
+    V total = Op::identity();
+#pragma unroll
+    for (int k = 0; k < ND; ++k) total = Op::combine(total, s_wave[k]);
+    if (lane == 0) {
+        const bool known = (tile == 0) || resets<Op>(total);
+        const typename Op::carry_t agg = Op::to_carry(total);
+        publish_acked<Op>(p.lb, p.lb.status, tile, agg, known ? kStatePrefix : kStateAggregate);
+        *s_total = agg;
+        *s_known = known;
+        __hip_atomic_store(&h->total_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
 }
 
 // ------------------------------------------------------------------ scan
 template <class Op, bool EXCL, int BLOCK, int ITEMS, bool SINGLE>
 __global__ __launch_bounds__(BLOCK) void tile_scan_kernel(ScanParams p)
 {
-    using E = typename Op::elem_t;
+    using G = Geometry<Op, BLOCK, ITEMS>;
     using V = typename Op::value_t;
     using C = typename Op::carry_t;
-    constexpr bool SEG = IsSeg<Op>::value;
-    constexpr int VEC = 16 / (int)sizeof(E);
-    constexpr int R = ITEMS / VEC;
-    constexpr int NW = BLOCK / 64;
-    constexpr int WAVE_ELEMS = 64 * ITEMS;
-    constexpr int TILE = BLOCK * ITEMS;
-    static_assert(ITEMS % VEC == 0 && BLOCK % 64 == 0, "tile shape");
-    static_assert(!SEG || VEC == 4, "segmented scans use 4-byte elements");
+    constexpr int R = G::R, VEC = G::VEC, ND = G::ND;
+    static_assert(!IsSeg<Op>::value || VEC == 4, "segmented scans use 4-byte elements");
 
-    __shared__ V s_wave[NW];
-    __shared__ C s_prefix;
+    __shared__ V s_wave[ND];
+    __shared__ C s_excl;
+    __shared__ C s_total;
+    __shared__ bool s_known;
+    __shared__ TileHandover s_h;
     __shared__ uint32_t s_tile;
 
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
-    const E* __restrict__ in = static_cast<const E*>(p.in);
-    E* __restrict__ out = static_cast<E*>(p.out);
     const V ident = Op::identity();
-    const auto comb = [](V a, V b) { return Op::combine(a, b); };
 
-    C running = Op::carry_identity();  // SINGLE mode carry
-    const uint32_t tiles_here = SINGLE ? p.num_tiles : 1u;
-
-    for (uint32_t it = 0; it < tiles_here; ++it) {
-        uint32_t tile;
-        if constexpr (SINGLE) {
-            tile = it;
-        } else {
-            if (threadIdx.x == 0)
-                s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                         p.ctr_base;
+    if constexpr (SINGLE) {
+        // Small-n path: one workgroup walks the tiles in order and carries the
+        // prefix in registers; the last wavefront idles.
+        C running = Op::carry_identity();
+        for (uint32_t tile = 0; tile < p.num_tiles; ++tile) {
+            const uint64_t tile_base = (uint64_t)tile * G::TILE;
+            const uint64_t wave_base = tile_base + (uint64_t)w * G::WAVE_ELEMS;
+            const bool vec = p.vec_ok && tile_base + G::TILE <= p.n;
+            V x[R][VEC], lane_excl[R], round_carry[R + 1];
+            uint32_t raw_head[R];
+            if (w < ND) {
+                load_wave<Op, R, VEC>(p, wave_base, vec, lane, x, raw_head);
+                scan_wave<Op, R, VEC>(x, lane_excl, round_carry);
+                if (lane == 0) s_wave[w] = round_carry[R];
+            }
             __syncthreads();
-            tile = s_tile;
-            if (tile >= p.num_tiles) {  // counter out of step with this launch: never index past the grid
-                if (threadIdx.x == 0)
-                    __hip_atomic_fetch_or(p.lb.err, (uint32_t)kErrCounter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                return;
+            V wave_prefix = ident, tile_total = ident;
+#pragma unroll
+            for (int k = 0; k < ND; ++k) {
+                const V a = s_wave[k];
+                if (k < w) wave_prefix = Op::combine(wave_prefix, a);
+                tile_total = Op::combine(tile_total, a);
             }
-        }
-
-        const uint64_t tile_base = (uint64_t)tile * TILE;
-        const uint64_t wave_base = tile_base + (uint64_t)w * WAVE_ELEMS;
-        const bool full = tile_base + TILE <= p.n;
-
-        // ---- load (2)
-        V x[R][VEC];
-        uint32_t raw_head[R];  // bit j: element j of round r is a segment head
-        if (full && p.vec_ok) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
-                E e[VEC];
-                load_vec<E, VEC>(in + i0, e);
-                uint32_t hb = 0;
-                if constexpr (SEG) {
-                    const uint32_t h4 = *reinterpret_cast<const uint32_t*>(p.heads + i0);
-#pragma unroll
-                    for (int j = 0; j < VEC; ++j) hb |= ((h4 >> (8 * j)) & 0xFFu) ? (1u << j) : 0u;
-                    if (i0 == 0) hb |= 1u;
-                }
-                raw_head[r] = hb;
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) x[r][j] = make_value<Op>(e[j], (hb >> j) & 1u);
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
-                uint32_t hb = 0;
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) {
-                    const uint64_t i = i0 + j;
-                    if (i < p.n) {
-                        uint32_t h = 0;
-                        if constexpr (SEG) h = (i == 0 || p.heads[i]) ? 1u : 0u;
-                        hb |= h << j;
-                        x[r][j] = make_value<Op>(in[i], h);
-                    } else {
-                        x[r][j] = ident;
-                    }
-                }
-                raw_head[r] = hb;
-            }
-        }
-
-        // ---- serial scan in registers (3)
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int j = 1; j < VEC; ++j) x[r][j] = Op::combine(x[r][j - 1], x[r][j]);
-
-        // ---- wavefront scans of the lane totals (4)
-        V lane_excl[R];
-        V round_carry[R + 1];
-        round_carry[0] = ident;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const V incl = wave_inclusive_scan(x[r][VEC - 1], ident, comb);
-            lane_excl[r] = wave_shift_up(incl, ident);
-            round_carry[r + 1] = Op::combine(round_carry[r], read_lane(incl, 63));
-        }
-
-        // ---- cross-wavefront combine (5)
-        if (lane == 0) s_wave[w] = round_carry[R];
-        __syncthreads();
-        V wave_prefix = ident, tile_total = ident;
-#pragma unroll
-        for (int k = 0; k < NW; ++k) {
-            const V a = s_wave[k];
-            if (k < w) wave_prefix = Op::combine(wave_prefix, a);
-            tile_total = Op::combine(tile_total, a);
-        }
-
-        // ---- inter-tile prefix (6)
-        C P;
-        if constexpr (SINGLE) {
-            P = running;
+            if (w < ND)
+                apply_store<Op, EXCL, R, VEC>(p, wave_base, vec, lane, running, wave_prefix, x, lane_excl,
+                                              round_carry, raw_head);
             running = Op::combine_carry(running, Op::to_carry(tile_total));
-        } else {
-            if (w == 0) {
-                const C agg = Op::to_carry(tile_total);
-                // A tile with no predecessor, or whose total restarts the
-                // fold (a segment head inside it), already knows its inclusive
-                // prefix: publish it as PREFIX straight away.
-                const bool known = (tile == 0) || resets<Op>(tile_total);
-                if (lane == 0) publish<Op>(p.lb, tile, agg, known ? kStatePrefix : kStateAggregate);
-                C excl = Op::carry_identity();
-                // Elements before the tile's first head still need the prefix.
-                bool need = tile != 0;
-                if constexpr (SEG) need = need && !(__builtin_amdgcn_readfirstlane(raw_head[0]) & 1u);
-                if (need) excl = lookback<Op>(p.lb, tile);
-                if (!known && lane == 0) publish<Op>(p.lb, tile, Op::combine_carry(excl, agg), kStatePrefix);
-                if (lane == 0) s_prefix = excl;
-            }
-            __syncthreads();
-            P = s_prefix;
+            __syncthreads();  // s_wave is rewritten by the next tile
         }
+        return;
+    }
 
-        // ---- apply and store (7)
+    // ---- (1) tile number; reset the hand-over state
+    if (threadIdx.x == 0) {
+        s_h.arrived = 0u;
+        s_h.total_ready = 0u;
+    }
+    const uint32_t tile = take_tile(p, &s_tile);
+    if (tile >= p.num_tiles) return;  // never index past the grid
+    const uint64_t tile_base = (uint64_t)tile * G::TILE;
+    const uint64_t wave_base = tile_base + (uint64_t)w * G::WAVE_ELEMS;
+    const bool vec = p.vec_ok && tile_base + G::TILE <= p.n;
+
+    V x[R][VEC], lane_excl[R], round_carry[R + 1];
+    uint32_t raw_head[R];
+    if (w < ND) {
+        // ---- (2)-(5) data wavefronts: load, scan, hand the total over
+        load_wave<Op, R, VEC>(p, wave_base, vec, lane, x, raw_head);
+        scan_wave<Op, R, VEC>(x, lane_excl, round_carry);
+        hand_over<Op, ND>(p, tile, w, lane, round_carry[R], s_wave, &s_h, &s_total, &s_known);
+    } else {
+        // ---- (6) look-back wavefront, concurrent with the loads
+        const C excl = lookback_wave<Op>(p.lb, tile, &s_h, &s_total, &s_known);
+        if (lane == 0) s_excl = excl;
+    }
+    __syncthreads();
+    if (w < ND) {
+        V wave_prefix = ident;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const V in_tile = Op::combine(Op::combine(wave_prefix, round_carry[r]), lane_excl[r]);
-            const typename Op::prep_t pc = Op::prepare(Op::combine_carry(P, Op::to_carry(in_tile)));
-            E e[VEC];
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                V y;
-                if constexpr (EXCL) {
-                    y = Op::apply(pc, j == 0 ? ident : x[r][j - 1]);
-                    if constexpr (SEG)
-                        if ((raw_head[r] >> j) & 1u) y = ident;
-                } else {
-                    y = Op::apply(pc, x[r][j]);
-                }
-                e[j] = elem_of<Op>(y);
-            }
-            const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
-            if (full && p.vec_ok) {
-                store_vec<E, VEC>(out + i0, e);
-            } else {
-#pragma unroll
-                for (int j = 0; j < VEC; ++j)
-                    if (i0 + j < p.n) out[i0 + j] = e[j];
-            }
-        }
-        if constexpr (SINGLE) __syncthreads();  // s_wave is rewritten by the next tile
+        for (int k = 0; k < ND; ++k)
+            if (k < w) wave_prefix = Op::combine(wave_prefix, s_wave[k]);
+        apply_store<Op, EXCL, R, VEC>(p, wave_base, vec, lane, s_excl, wave_prefix, x, lane_excl, round_carry,
+                                      raw_head);
     }
 }
 
@@ -275,129 +387,482 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_kernel(ScanParams p)
 template <typename T>
 __device__ __forceinline__ bool keep(T x) { return x > T(0); }
 
+// Predicate flags of one wavefront's elements: loads (as load_wave) and
+// returns in kept[r] bit j whether element j of round r is kept.
+template <typename T, int R, int VEC>
+__device__ __forceinline__ void load_flags(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
+                                           T (&x)[R][VEC], uint32_t (&kept)[R])
+{
+    const T* __restrict__ in = static_cast<const T*>(p.in);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
+        uint32_t b = 0;
+        if (vec) {
+            load_vec<T, VEC>(in + i0, x[r]);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) b |= keep(x[r][j]) ? (1u << j) : 0u;
+        } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                x[r][j] = (i0 + j < p.n) ? in[i0 + j] : T(0);
+                b |= (i0 + j < p.n && keep(x[r][j])) ? (1u << j) : 0u;
+            }
+        }
+        kept[r] = b;
+    }
+}
+
+// Packs a wavefront's kept elements, in order, at the start of its own LDS
+// region; returns the wavefront's count.
+template <typename T, int R, int VEC>
+__device__ __forceinline__ uint32_t pack_wave(const T (&x)[R][VEC], const uint32_t (&kept)[R], T* region)
+{
+    const auto add = [](uint32_t a, uint32_t b) { return a + b; };
+    uint32_t base = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t incl = wave_inclusive_scan((uint32_t)__builtin_popcount(kept[r]), 0u, add);
+        uint32_t rank = base + wave_shift_up(incl, 0u);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j)
+            if ((kept[r] >> j) & 1u) region[rank++] = x[r][j];
+        base += read_lane(incl, 63);
+    }
+    return base;
+}
+
 template <typename T, int BLOCK, int ITEMS, bool SINGLE>
 __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 {
     using Cnt = OpAdd<uint32_t>;
-    constexpr int VEC = 16 / (int)sizeof(T);
-    constexpr int R = ITEMS / VEC;
-    constexpr int NW = BLOCK / 64;
-    constexpr int WAVE_ELEMS = 64 * ITEMS;
-    constexpr int TILE = BLOCK * ITEMS;
-    static_assert(ITEMS % VEC == 0 && BLOCK % 64 == 0, "tile shape");
+    using G = Geometry<Cnt, BLOCK, ITEMS>;
+    constexpr int R = G::R, VEC = G::VEC, ND = G::ND;
+    static_assert(sizeof(T) == 4, "4-byte elements");
 
-    __shared__ T s_keep[TILE];
-    __shared__ uint32_t s_wave[NW];
-    __shared__ uint32_t s_prefix;
+    __shared__ T s_keep[G::TILE];  // wavefront w packs into [w * WAVE_ELEMS, ...)
+    __shared__ uint32_t s_wave[ND];
+    __shared__ uint32_t s_excl;
+    __shared__ uint32_t s_total;
+    __shared__ bool s_known;
+    __shared__ TileHandover s_h;
     __shared__ uint32_t s_tile;
 
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
-    const T* __restrict__ in = static_cast<const T*>(p.in);
     T* __restrict__ out = static_cast<T*>(p.out);
-    const auto add = [](uint32_t a, uint32_t b) { return a + b; };
+    T* region = s_keep + w * G::WAVE_ELEMS;
 
-    uint32_t running = 0;
-    const uint32_t tiles_here = SINGLE ? p.num_tiles : 1u;
-    for (uint32_t it = 0; it < tiles_here; ++it) {
-        uint32_t tile;
-        if constexpr (SINGLE) {
-            tile = it;
-        } else {
-            if (threadIdx.x == 0)
-                s_tile = __hip_atomic_fetch_add(p.tile_ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                         p.ctr_base;
-            __syncthreads();
-            tile = s_tile;
-            if (tile >= p.num_tiles) {
-                if (threadIdx.x == 0)
-                    __hip_atomic_fetch_or(p.lb.err, (uint32_t)kErrCounter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                return;
-            }
-        }
-        const uint64_t tile_base = (uint64_t)tile * TILE;
-        const uint64_t wave_base = tile_base + (uint64_t)w * WAVE_ELEMS;
-        const bool full = tile_base + TILE <= p.n;
-
-        T x[R][VEC];
-        uint32_t kept[R];  // bit j: element j of round r passes the predicate
-        if (full && p.vec_ok) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                load_vec<T, VEC>(in + wave_base + (uint64_t)(r * 64 + lane) * VEC, x[r]);
-                uint32_t b = 0;
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) b |= keep(x[r][j]) ? (1u << j) : 0u;
-                kept[r] = b;
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
-                uint32_t b = 0;
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) {
-                    x[r][j] = (i0 + j < p.n) ? in[i0 + j] : T(0);
-                    b |= (i0 + j < p.n && keep(x[r][j])) ? (1u << j) : 0u;
-                }
-                kept[r] = b;
-            }
-        }
-
-        // flag counts: per lane, then across the wavefront, then across wavefronts
-        uint32_t lane_excl[R];
-        uint32_t round_base[R + 1];
-        round_base[0] = 0;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t incl = wave_inclusive_scan((uint32_t)__builtin_popcount(kept[r]), 0u, add);
-            lane_excl[r] = wave_shift_up(incl, 0u);
-            round_base[r + 1] = round_base[r] + read_lane(incl, 63);
-        }
-        if (lane == 0) s_wave[w] = round_base[R];
-        __syncthreads();
-        uint32_t wave_prefix = 0, tile_total = 0;
-#pragma unroll
-        for (int k = 0; k < NW; ++k) {
-            const uint32_t a = s_wave[k];
-            if (k < w) wave_prefix += a;
-            tile_total += a;
-        }
-
-        // pack kept elements at their rank inside the tile
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            uint32_t rank = wave_prefix + round_base[r] + lane_excl[r];
-#pragma unroll
-            for (int j = 0; j < VEC; ++j)
-                if ((kept[r] >> j) & 1u) s_keep[rank++] = x[r][j];
-        }
-
-        uint32_t P;
-        if constexpr (SINGLE) {
-            P = running;
-            running += tile_total;
-            __syncthreads();
-        } else {
-            if (w == 0) {
-                if (lane == 0) publish<Cnt>(p.lb, tile, tile_total, tile == 0 ? kStatePrefix : kStateAggregate);
-                uint32_t excl = 0;
-                if (tile != 0) {
-                    excl = lookback<Cnt>(p.lb, tile);
-                    if (lane == 0) publish<Cnt>(p.lb, tile, excl + tile_total, kStatePrefix);
-                }
-                if (lane == 0) s_prefix = excl;
+    if constexpr (SINGLE) {
+        uint32_t running = 0;
+        for (uint32_t tile = 0; tile < p.num_tiles; ++tile) {
+            const uint64_t tile_base = (uint64_t)tile * G::TILE;
+            const uint64_t wave_base = tile_base + (uint64_t)w * G::WAVE_ELEMS;
+            const bool vec = p.vec_ok && tile_base + G::TILE <= p.n;
+            uint32_t cnt = 0;
+            if (w < ND) {
+                T x[R][VEC];
+                uint32_t kept[R];
+                load_flags<T, R, VEC>(p, wave_base, vec, lane, x, kept);
+                cnt = pack_wave<T, R, VEC>(x, kept, region);
+                if (lane == 0) s_wave[w] = cnt;
             }
             __syncthreads();
-            P = s_prefix;
+            uint32_t wave_prefix = 0, total = 0;
+#pragma unroll
+            for (int k = 0; k < ND; ++k) {
+                if (k < w) wave_prefix += s_wave[k];
+                total += s_wave[k];
+            }
+            if (w < ND)
+                for (uint32_t i = lane; i < cnt; i += 64) out[(uint64_t)running + wave_prefix + i] = region[i];
+            running += total;
+            __syncthreads();
         }
-
-        // one contiguous run out[P .. P + tile_total)
-        for (uint32_t i = threadIdx.x; i < tile_total; i += BLOCK) out[(uint64_t)P + i] = s_keep[i];
-        if (!SINGLE && tile == p.num_tiles - 1 && threadIdx.x == 0) *p.count = P + tile_total;
-        if constexpr (SINGLE) __syncthreads();
+        if (threadIdx.x == 0) *p.count = running;
+        return;
     }
-    if (SINGLE && threadIdx.x == 0) *p.count = running;
+
+    if (threadIdx.x == 0) {
+        s_h.arrived = 0u;
+        s_h.total_ready = 0u;
+    }
+    const uint32_t tile = take_tile(p, &s_tile);
+    if (tile >= p.num_tiles) return;
+    const uint64_t tile_base = (uint64_t)tile * G::TILE;
+    const uint64_t wave_base = tile_base + (uint64_t)w * G::WAVE_ELEMS;
+    const bool vec = p.vec_ok && tile_base + G::TILE <= p.n;
+
+    uint32_t cnt = 0;
+    if (w < ND) {
+        T x[R][VEC];
+        uint32_t kept[R];
+        load_flags<T, R, VEC>(p, wave_base, vec, lane, x, kept);
+        cnt = pack_wave<T, R, VEC>(x, kept, region);
+        hand_over<Cnt, ND>(p, tile, w, lane, cnt, s_wave, &s_h, &s_total, &s_known);
+    } else {
+        const uint32_t excl = lookback_wave<Cnt>(p.lb, tile, &s_h, &s_total, &s_known);
+        if (lane == 0) s_excl = excl;
+    }
+    __syncthreads();
+    if (w < ND) {
+        uint32_t wave_prefix = 0;
+#pragma unroll
+        for (int k = 0; k < ND; ++k)
+            if (k < w) wave_prefix += s_wave[k];
+        // one contiguous run per wavefront at out[prefix of the tile + earlier wavefronts]
+        const uint64_t dst = (uint64_t)s_excl + wave_prefix;
+        for (uint32_t i = lane; i < cnt; i += 64) out[dst + i] = region[i];
+    }
+    if (tile == p.num_tiles - 1 && threadIdx.x == 0) *p.count = s_excl + s_total;
+}
+
+// ============================================================ persistent
+// Persistent, software-pipelined variant of the multi-tile path, launched
+// cooperatively with exactly as many workgroups as can be resident together.
+//
+//  * Workgroup 0 is the resolver: one wavefront that streams through the
+//    tile totals in tile order, scans them 64 * RSPAN at a time and
+//    publishes each tile's exclusive prefix (lookback.hpp, resolve_stream).
+//    It loads no data, so its status reads do not queue behind tile loads,
+//    and each total is read about once.  (A look-back by every tile would
+//    have ~250 tiles in flight each reading ~250 statuses of the same
+//    region per round; measured, those reads queued behind the tile data on
+//    every CU and hammered the same cache lines.)
+//  * Workgroups 1 .. G-1 scan tiles dealt round-robin: workgroup b takes
+//    tiles b-1, b-1 + (G-1), ...  Every data wavefront keeps three of its
+//    tiles in flight as raw elements in registers: while it waits for the
+//    prefix of tile k, the total of tile k+1 is already published and the
+//    loads of tile k+2 are on their way.  So totals go out as soon as the
+//    data arrives, and the wait for a prefix overlaps memory traffic.  The
+//    in-register scan is cheap, so a tile is reduced once for its total and
+//    scanned again when its prefix arrives.  The last wavefront of the
+//    workgroup only fetches the prefixes the resolver publishes, one word
+//    per tile.
+//  * Data and prefix wavefronts meet through a four-slot ring in LDS
+//    (iteration k uses slot k & 3) with sequence numbers instead of
+//    barriers: a slot is rewritten only after every wavefront has passed the
+//    prefix wait of the iteration two before, so four slots are enough.
+//  * Progress: every workgroup is resident; the resolver only waits for
+//    totals, which a data workgroup publishes before it waits for any
+//    prefix of a later tile; waits are bounded by the spin limit.
+constexpr int kPipeSlots = 4;
+#ifndef DWPT_RESOLVE_SPAN
+#define DWPT_RESOLVE_SPAN 4  // tiles per lane of the resolver's window
+#endif
+
+template <class V, class C, int ND>
+struct PipeSlot {
+    uint32_t arrived;     // data-wavefront arrivals, counted over all uses of the slot
+    uint32_t prefix_seq;  // k + 1 once the exclusive prefix of iteration k is here
+    C prefix;
+    V wave_total[ND];
+};
+
+template <class Op>
+__device__ __forceinline__ typename Op::elem_t elem_identity()
+{
+    if constexpr (IsSeg<Op>::value) return Op::identity().v;
+    else return Op::identity();
+}
+
+// Issues one wavefront's loads of a tile into raw registers (the data is not
+// used here, so nothing waits for it).  Out-of-range elements read as the
+// identity; h4[r] holds the head-flag bytes of round r.
+template <class Op, int R, int VEC>
+__device__ __forceinline__ void issue_loads(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
+                                            typename Op::elem_t (&e)[R][VEC], uint32_t (&h4)[R])
+{
+    using E = typename Op::elem_t;
+    constexpr bool SEG = IsSeg<Op>::value;
+    const E* __restrict__ in = static_cast<const E*>(p.in);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
+        h4[r] = 0;
+        if (vec) {
+            load_vec<E, VEC>(in + i0, e[r]);
+            if constexpr (SEG) h4[r] = *reinterpret_cast<const uint32_t*>(p.heads + i0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const uint64_t i = i0 + j;
+                e[r][j] = (i < p.n) ? in[i] : elem_identity<Op>();
+                if constexpr (SEG)
+                    if (i < p.n && p.heads[i]) h4[r] |= 0xFFu << (8 * j);
+            }
+        }
+    }
+}
+
+// Raw elements -> scan values and head bits (element 0 of the input is a head).
+template <class Op, int R, int VEC>
+__device__ __forceinline__ void to_values(uint64_t wave_base, int lane, const typename Op::elem_t (&e)[R][VEC],
+                                          const uint32_t (&h4)[R], typename Op::value_t (&x)[R][VEC],
+                                          uint32_t (&raw_head)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        uint32_t hb = 0;
+        if constexpr (IsSeg<Op>::value) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) hb |= ((h4[r] >> (8 * j)) & 0xFFu) ? (1u << j) : 0u;
+            if (wave_base + (uint64_t)(r * 64 + lane) * VEC == 0) hb |= 1u;
+        }
+        raw_head[r] = hb;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) x[r][j] = make_value<Op>(e[r][j], (hb >> j) & 1u);
+    }
+}
+
+// Fold of one wavefront's share of a tile, in element order.
+template <class Op, int R, int VEC>
+__device__ __forceinline__ typename Op::value_t reduce_wave(uint64_t wave_base, int lane,
+                                                            const typename Op::elem_t (&e)[R][VEC],
+                                                            const uint32_t (&h4)[R])
+{
+    using V = typename Op::value_t;
+    const V ident = Op::identity();
+    const auto comb = [](V a, V b) { return Op::combine(a, b); };
+    V x[R][VEC];
+    uint32_t raw_head[R];
+    to_values<Op, R, VEC>(wave_base, lane, e, h4, x, raw_head);
+    V total = ident;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        V t = x[r][0];
+#pragma unroll
+        for (int j = 1; j < VEC; ++j) t = Op::combine(t, x[r][j]);
+        total = Op::combine(total, read_lane(wave_inclusive_scan(t, ident, comb), 63));
+    }
+    return total;
+}
+
+// Data wavefront w hands its total over; the last one of the workgroup to
+// arrive for this tile publishes the tile total.
+template <class Op, class Slot, int ND>
+__device__ __forceinline__ void hand_over_slot(const ScanParams& p, uint32_t tile, uint32_t k, int w, int lane,
+                                               typename Op::value_t wave_total, Slot* slot)
+{
+    using V = typename Op::value_t;
+    if (lane == 0) slot->wave_total[w] = wave_total;
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(&slot->arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != (k / kPipeSlots) * ND + (ND - 1)) return;  // not the last data wavefront of this use
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    V total = Op::identity();
+#pragma unroll
+    for (int q = 0; q < ND; ++q) total = Op::combine(total, slot->wave_total[q]);
+    if (lane == 0) publish<Op>(p.lb, p.lb.status, tile, Op::to_carry(total), kStateAggregate);
+}
+
+__device__ __forceinline__ void wait_seq(uint32_t* seq, uint32_t want)
+{
+    while (__hip_atomic_load(seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < want)
+        __builtin_amdgcn_s_sleep(1);
+}
+
+template <class Slot>
+__device__ __forceinline__ void init_slots(Slot* s)
+{
+    if (threadIdx.x < kPipeSlots) {
+        s[threadIdx.x].arrived = 0u;
+        s[threadIdx.x].prefix_seq = 0u;
+    }
+    __syncthreads();
+}
+
+// Prefix wavefront of a data workgroup: fetches the prefix of each of the
+// workgroup's tiles, in order, into the slot ring.
+template <class Op, class Slot>
+__device__ __forceinline__ void fetch_prefixes(const ScanParams& p, uint32_t first, uint32_t stride, Slot* slots)
+{
+    uint32_t k = 0;
+    for (uint32_t tile = first; tile < p.num_tiles; tile += stride, ++k) {
+        const typename Op::carry_t excl = wait_excl<Op>(p.lb, p.lb.groups, tile);
+        Slot* slot = &slots[k % kPipeSlots];
+        if (lane_id() == 0) {
+            slot->prefix = excl;
+            __hip_atomic_store(&slot->prefix_seq, k + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+}
+
+// Position of a data wavefront's share of a tile.
+template <class G>
+struct WaveTile {
+    uint32_t tile;
+    uint64_t base;  // first element of the wavefront's share
+    bool vec;       // whole tile in range and aligned: 16-byte accesses
+    __device__ __forceinline__ void set(const ScanParams& p, uint32_t t, int w)
+    {
+        tile = t;
+        base = (uint64_t)t * G::TILE + (uint64_t)w * G::WAVE_ELEMS;
+        vec = p.vec_ok && (uint64_t)t * G::TILE + G::TILE <= p.n;
+    }
+};
+
+template <class Op, bool EXCL, int BLOCK, int ITEMS>
+__global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
+{
+    using G = Geometry<Op, BLOCK, ITEMS>;
+    using E = typename Op::elem_t;
+    using V = typename Op::value_t;
+    using C = typename Op::carry_t;
+    using Slot = PipeSlot<V, C, G::ND>;
+    constexpr int R = G::R, VEC = G::VEC, ND = G::ND;
+    static_assert(!IsSeg<Op>::value || VEC == 4, "segmented scans use 4-byte elements");
+
+    __shared__ Slot s_slot[kPipeSlots];
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    if (blockIdx.x == 0) {
+        if (w == 0) (void)resolve_stream<Op, DWPT_RESOLVE_SPAN>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
+        return;
+    }
+    init_slots(s_slot);
+    const uint32_t stride = gridDim.x - 1;
+    const uint32_t first = blockIdx.x - 1;
+    if (w == ND) {
+        fetch_prefixes<Op>(p, first, stride, s_slot);
+        return;
+    }
+
+    // three tiles per data wavefront: a (waiting for its prefix), b (total
+    // published), c (loads in flight)
+    E ea[R][VEC], eb[R][VEC], ec[R][VEC];
+    uint32_t ha[R], hb[R], hc[R];
+    WaveTile<G> ta, tb, tc;
+    ta.set(p, first, w);
+    tb.set(p, first + stride, w);
+    issue_loads<Op, R, VEC>(p, ta.base, ta.vec, lane, ea, ha);
+    if (tb.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, tb.base, tb.vec, lane, eb, hb);
+    hand_over_slot<Op, Slot, ND>(p, ta.tile, 0, w, lane, reduce_wave<Op, R, VEC>(ta.base, lane, ea, ha),
+                                 &s_slot[0]);
+    for (uint32_t k = 0; ta.tile < p.num_tiles; ++k) {
+        tc.set(p, tb.tile + stride, w);
+        if (tc.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, tc.base, tc.vec, lane, ec, hc);
+        if (tb.tile < p.num_tiles)
+            hand_over_slot<Op, Slot, ND>(p, tb.tile, k + 1, w, lane, reduce_wave<Op, R, VEC>(tb.base, lane, eb, hb),
+                                         &s_slot[(k + 1) % kPipeSlots]);
+
+        Slot* slot = &s_slot[k % kPipeSlots];
+        wait_seq(&slot->prefix_seq, k + 1);
+        {
+            V x[R][VEC], lane_excl[R], round_carry[R + 1];
+            uint32_t raw_head[R];
+            to_values<Op, R, VEC>(ta.base, lane, ea, ha, x, raw_head);
+            scan_wave<Op, R, VEC>(x, lane_excl, round_carry);
+            V wave_prefix = Op::identity();
+#pragma unroll
+            for (int q = 0; q < ND; ++q)
+                if (q < w) wave_prefix = Op::combine(wave_prefix, slot->wave_total[q]);
+            apply_store<Op, EXCL, R, VEC>(p, ta.base, ta.vec, lane, slot->prefix, wave_prefix, x, lane_excl,
+                                          round_carry, raw_head);
+        }
+        // rotate: b -> a, c -> b
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ha[r] = hb[r];
+            hb[r] = hc[r];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                ea[r][j] = eb[r][j];
+                eb[r][j] = ec[r][j];
+            }
+        }
+        ta = tb;
+        tb = tc;
+    }
+}
+
+template <typename T, int BLOCK, int ITEMS>
+__global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
+{
+    using Cnt = OpAdd<uint32_t>;
+    using Ld = OpMax<T>;  // element loads of T (identity past n: never kept)
+    using G = Geometry<Cnt, BLOCK, ITEMS>;
+    using Slot = PipeSlot<uint32_t, uint32_t, G::ND>;
+    constexpr int R = G::R, VEC = G::VEC, ND = G::ND;
+    static_assert(sizeof(T) == 4, "4-byte elements");
+
+    __shared__ T s_keep[G::TILE];  // wavefront w packs into [w * WAVE_ELEMS, ...)
+    __shared__ Slot s_slot[kPipeSlots];
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    if (blockIdx.x == 0) {
+        if (w == 0) {
+            const uint32_t total = resolve_stream<Cnt, DWPT_RESOLVE_SPAN>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
+            if (lane == 0) *p.count = total;
+        }
+        return;
+    }
+    init_slots(s_slot);
+    const uint32_t stride = gridDim.x - 1;
+    const uint32_t first = blockIdx.x - 1;
+    T* __restrict__ out = static_cast<T*>(p.out);
+    if (w == ND) {
+        fetch_prefixes<Cnt>(p, first, stride, s_slot);
+        return;
+    }
+
+    const auto kept_bits = [&](const T (&e)[R][VEC], uint64_t base, uint32_t (&kept)[R]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint64_t i0 = base + (uint64_t)(r * 64 + lane) * VEC;
+            uint32_t b = 0;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) b |= (keep(e[r][j]) && i0 + j < p.n) ? (1u << j) : 0u;
+            kept[r] = b;
+        }
+    };
+    const auto count_wave = [&](const T (&e)[R][VEC], uint64_t base) {
+        uint32_t kept[R];
+        kept_bits(e, base, kept);
+        uint32_t c = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) c += (uint32_t)__builtin_popcount(kept[r]);
+        const auto add = [](uint32_t a, uint32_t b) { return a + b; };
+        return read_lane(wave_inclusive_scan(c, 0u, add), 63);
+    };
+
+    T* region = s_keep + w * G::WAVE_ELEMS;
+    T ea[R][VEC], eb[R][VEC], ec[R][VEC];
+    uint32_t hu[R];
+    WaveTile<G> ta, tb, tc;
+    ta.set(p, first, w);
+    tb.set(p, first + stride, w);
+    issue_loads<Ld, R, VEC>(p, ta.base, ta.vec, lane, ea, hu);
+    if (tb.tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, tb.base, tb.vec, lane, eb, hu);
+    hand_over_slot<Cnt, Slot, ND>(p, ta.tile, 0, w, lane, count_wave(ea, ta.base), &s_slot[0]);
+    for (uint32_t k = 0; ta.tile < p.num_tiles; ++k) {
+        tc.set(p, tb.tile + stride, w);
+        if (tc.tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, tc.base, tc.vec, lane, ec, hu);
+        if (tb.tile < p.num_tiles)
+            hand_over_slot<Cnt, Slot, ND>(p, tb.tile, k + 1, w, lane, count_wave(eb, tb.base),
+                                          &s_slot[(k + 1) % kPipeSlots]);
+        Slot* slot = &s_slot[k % kPipeSlots];
+        uint32_t kept[R];
+        kept_bits(ea, ta.base, kept);
+        const uint32_t cnt = pack_wave<T, R, VEC>(ea, kept, region);
+        wait_seq(&slot->prefix_seq, k + 1);
+        uint32_t wave_prefix = 0;
+#pragma unroll
+        for (int q = 0; q < ND; ++q)
+            if (q < w) wave_prefix += slot->wave_total[q];
+        const uint64_t dst = (uint64_t)slot->prefix + wave_prefix;
+        for (uint32_t i = lane; i < cnt; i += 64) out[dst + i] = region[i];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                ea[r][j] = eb[r][j];
+                eb[r][j] = ec[r][j];
+            }
+        ta = tb;
+        tb = tc;
+    }
 }
 
 }  // namespace dwpt

@@ -141,11 +141,16 @@ scan_status_t scan_release_workspace(void);
  * scan_set_small_n_max: inputs with n at or below this size run on one
  *   workgroup that walks the tiles in order (no workspace, no atomics); larger
  *   inputs use the multi-tile look-back kernel.  Default 4096.
+ * scan_set_multi_tile_mode: 0 (default) runs large inputs on the persistent
+ *   pipelined kernel (one cooperative launch of as many workgroups as fit on
+ *   the GPU, each scanning every G-th tile); 1 runs one workgroup per tile
+ *   (also the automatic fallback when a cooperative launch is not possible).
  * scan_set_spin_limit: number of look-back polls after which a waiting tile
  *   gives up, records SCAN_ERR_TIMEOUT (see scan_get_device_error) and
  *   finishes with a wrong prefix instead of waiting forever.  Default 2^20.
  */
 size_t scan_set_small_n_max(size_t n_max);
+int scan_set_multi_tile_mode(int mode);
 uint32_t scan_set_spin_limit(uint32_t polls);
 
 /*
