@@ -41,7 +41,19 @@ sys.path.insert(0, ROOT)
 PEAK_GBPS = 8000.0
 N_MAIN = 1 << 28
 METRIC = "scan Gelem/s + effective HBM GB/s (% of peak), fp32/int32 n=2^28, 1 MI355X"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_f32_inclusive_add_2p28.json")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_f32_inclusive_add_2p28.txt")
+STATS_FILE = os.path.join(PROFILES, "kernel_stats_f32_inclusive_add_2p28.txt")
+SCAN_KERNEL = "tile_scan_persistent"
+COPY_KERNEL = "copy_probe_kernel"
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d $OUT/prof_trace -o bench -- "
+             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/prof_fetch -o bench -- "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/prof_write -o bench -- "
+             "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+}
 
 
 def log(msg):
@@ -56,16 +68,103 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def read_kv(path):
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                rec[k.strip()] = v.strip()
+    return rec
+
+
 def counter_traffic():
     """HBM bytes per launch from the committed counter summary, if it matches the sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+        rec = read_kv(TRAFFIC_FILE)
+    except OSError:
         return None
     if rec.get("source_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    try:
+        return int(float(rec["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    rows = []
+    for path in sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _short(name):
+    name = name.replace("(anonymous namespace)::", "").split("(")[0]
+    return name.replace("void dwpt::", "").replace("dwpt::", "")[:110]
+
+
+def summarize_rocprof(trace_dir, fetch_dir, write_dir):
+    """Write the kernel-time and HBM-traffic summaries under profiles/ from rocprofv3 CSV output."""
+    stats = _csv_rows(trace_dir, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel statistics, float32 inclusive add-scan n=2^28 (bench.py workload)",
+             "# command: " + PROFILE_CMDS["trace"],
+             "# kernel | calls | average us | min us | max us | share %"]
+    scan_avg = None
+    for r in stats:
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append("%s | %s | %.2f | %.2f | %.2f | %.1f" % (_short(r["Name"]), r["Calls"], avg,
+                                                           float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                                                           float(r["Percentage"])))
+        if SCAN_KERNEL in r["Name"] and "float" in r["Name"]:
+            scan_avg = avg
+    if scan_avg is not None:
+        lines.append("scan_kernel_average_us: %.2f" % scan_avg)
+        lines.append("scan_kernel_effective_GBps: %.1f" % (8 * N_MAIN / (scan_avg * 1e-6) / 1e9))
+    with open(STATS_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    def per_dispatch(directory, counter):
+        vals = {"scan": [], "copy": []}
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r.get("Kernel_Name", "")
+            v = float(r["Counter_Value"])
+            if SCAN_KERNEL in name and "float" in name:
+                vals["scan"].append(v)
+            elif COPY_KERNEL in name:
+                vals["copy"].append(v)
+        return {k: (sum(v) / len(v) if v else None) for k, v in vals.items()}
+
+    fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = per_dispatch(write_dir, "WRITE_SIZE")
+    copy_kib = (1 << 30) / 1024.0  # the copy probe reads and writes 1 GiB per launch
+    out = ["# HBM traffic of the float32 inclusive add-scan kernel, n=2^28, per launch",
+           "# commands: " + PROFILE_CMDS["fetch"],
+           "#           " + PROFILE_CMDS["write"],
+           "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the same counter",
+           "# reads for the 1 GiB copy probe (1048576 KiB each way) so the figure is in true bytes.",
+           "source_hash: " + kernel_source_hash()]
+    if None not in (fetch["scan"], fetch["copy"], write["scan"], write["copy"]):
+        fs, ws = copy_kib / fetch["copy"], copy_kib / write["copy"]
+        rd = fetch["scan"] * fs * 1024
+        wr = write["scan"] * ws * 1024
+        out += ["copy_fetch_kib: %.0f" % fetch["copy"], "copy_write_kib: %.0f" % write["copy"],
+                "fetch_scale: %.4f" % fs, "write_scale: %.4f" % ws,
+                "scan_fetch_kib: %.0f" % fetch["scan"], "scan_write_kib: %.0f" % write["scan"],
+                "hbm_read_bytes_per_launch: %.0f" % rd, "hbm_write_bytes_per_launch: %.0f" % wr,
+                "hbm_bytes_per_launch: %.0f" % (rd + wr),
+                "algorithmic_bytes_per_launch: %d" % (8 * N_MAIN),
+                "traffic_over_algorithmic: %.4f" % ((rd + wr) / (8 * N_MAIN))]
+    else:
+        out.append("# counters missing: fetch=%r write=%r" % (fetch, write))
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(open(STATS_FILE).read())
+    print(open(TRAFFIC_FILE).read())
 
 
 def time_launches(fn, steps, warmup, torch):
@@ -171,7 +270,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--suite", metavar="FILE", help="also time every workload, JSON lines to FILE")
+    ap.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 CSV output and exit")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(*args.summarize_rocprof)
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (--gpus %d requested); "
               "the scan is not sharded across GPUs" % args.gpus, file=sys.stderr)

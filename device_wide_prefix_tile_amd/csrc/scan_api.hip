@@ -40,7 +40,7 @@ struct Shape {
 // ------------------------------------------------------------ settings
 std::mutex g_mu;
 size_t g_small_n_max = 4096;          // n at or below: single-workgroup path
-uint32_t g_spin_limit = 1u << 20;     // look-back polls before giving up (about a second)
+uint32_t g_spin_limit = 1u << 18;     // look-back polls before giving up (a fraction of a second)
 int g_multi_mode = 0;                 // 0: persistent pipelined kernel; 1: one tile per workgroup
 
 // ------------------------------------------------------------ workspaces

@@ -673,13 +673,21 @@ __device__ __forceinline__ void init_slots(Slot* s)
     __syncthreads();
 }
 
+// k-th tile of data workgroup `first` (0-based) among `stride` of them:
+// tiles are dealt round-robin.
+__device__ __forceinline__ uint32_t tile_of(uint32_t first, uint32_t k, uint32_t stride)
+{
+    return first + k * stride;
+}
+
 // Prefix wavefront of a data workgroup: fetches the prefix of each of the
 // workgroup's tiles, in order, into the slot ring.
 template <class Op, class Slot>
 __device__ __forceinline__ void fetch_prefixes(const ScanParams& p, uint32_t first, uint32_t stride, Slot* slots)
 {
-    uint32_t k = 0;
-    for (uint32_t tile = first; tile < p.num_tiles; tile += stride, ++k) {
+    for (uint32_t k = 0;; ++k) {
+        const uint32_t tile = tile_of(first, k, stride);
+        if (tile >= p.num_tiles) break;
         const typename Op::carry_t excl = wait_excl<Op>(p.lb, p.lb.groups, tile);
         Slot* slot = &slots[k % kPipeSlots];
         if (lane_id() == 0) {
@@ -734,14 +742,14 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     E ea[R][VEC], eb[R][VEC], ec[R][VEC];
     uint32_t ha[R], hb[R], hc[R];
     WaveTile<G> ta, tb, tc;
-    ta.set(p, first, w);
-    tb.set(p, first + stride, w);
+    ta.set(p, tile_of(first, 0, stride), w);
+    tb.set(p, tile_of(first, 1, stride), w);
     issue_loads<Op, R, VEC>(p, ta.base, ta.vec, lane, ea, ha);
     if (tb.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, tb.base, tb.vec, lane, eb, hb);
     hand_over_slot<Op, Slot, ND>(p, ta.tile, 0, w, lane, reduce_wave<Op, R, VEC>(ta.base, lane, ea, ha),
                                  &s_slot[0]);
     for (uint32_t k = 0; ta.tile < p.num_tiles; ++k) {
-        tc.set(p, tb.tile + stride, w);
+        tc.set(p, tile_of(first, k + 2, stride), w);
         if (tc.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, tc.base, tc.vec, lane, ec, hc);
         if (tb.tile < p.num_tiles)
             hand_over_slot<Op, Slot, ND>(p, tb.tile, k + 1, w, lane, reduce_wave<Op, R, VEC>(tb.base, lane, eb, hb),
@@ -831,13 +839,13 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
     T ea[R][VEC], eb[R][VEC], ec[R][VEC];
     uint32_t hu[R];
     WaveTile<G> ta, tb, tc;
-    ta.set(p, first, w);
-    tb.set(p, first + stride, w);
+    ta.set(p, tile_of(first, 0, stride), w);
+    tb.set(p, tile_of(first, 1, stride), w);
     issue_loads<Ld, R, VEC>(p, ta.base, ta.vec, lane, ea, hu);
     if (tb.tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, tb.base, tb.vec, lane, eb, hu);
     hand_over_slot<Cnt, Slot, ND>(p, ta.tile, 0, w, lane, count_wave(ea, ta.base), &s_slot[0]);
     for (uint32_t k = 0; ta.tile < p.num_tiles; ++k) {
-        tc.set(p, tb.tile + stride, w);
+        tc.set(p, tile_of(first, k + 2, stride), w);
         if (tc.tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, tc.base, tc.vec, lane, ec, hu);
         if (tb.tile < p.num_tiles)
             hand_over_slot<Cnt, Slot, ND>(p, tb.tile, k + 1, w, lane, count_wave(eb, tb.base),

@@ -147,7 +147,7 @@ scan_status_t scan_release_workspace(void);
  *   (also the automatic fallback when a cooperative launch is not possible).
  * scan_set_spin_limit: number of look-back polls after which a waiting tile
  *   gives up, records SCAN_ERR_TIMEOUT (see scan_get_device_error) and
- *   finishes with a wrong prefix instead of waiting forever.  Default 2^20.
+ *   finishes with a wrong prefix instead of waiting forever.  Default 2^18.
  */
 size_t scan_set_small_n_max(size_t n_max);
 int scan_set_multi_tile_mode(int mode);

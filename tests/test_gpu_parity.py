@@ -2,9 +2,11 @@
 
 Integer, max/min, affine and compaction results must be bit-exact; float32
 add results must satisfy |y_gpu - y_ref| <= 1e-5 * sum_{k<=i}|x_k| + 1e-6 with
-y_ref accumulated in double.  Sizes span one or several 4096-element tiles
-with ragged tails; each test runs the multi-tile look-back path, and small
-inputs also the single-workgroup path (forced through the small-n knob).
+y_ref accumulated in double.  Sizes span one or several tiles (15360
+four-byte or 7680 eight-byte elements) with ragged tails; every size runs the
+default path and the one-workgroup-per-tile fallback, and small sizes also
+the single-workgroup path and the persistent kernel forced on (through the
+small-n and mode knobs).
 """
 import numpy as np
 import pytest
@@ -18,9 +20,10 @@ from parity_helpers import assert_equal, assert_f32_close, from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TILE = 4096
-SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1000, TILE - 1, TILE, TILE + 1, 3 * TILE + 17,
-         65536 + 1, 250001, 1000003]
+TILE = 15 * 64 * 16   # elements per tile of 4-byte types (15 data wavefronts x 64 lanes x 16)
+TILE8 = 15 * 64 * 8   # pairs per tile of the 8-byte affine type
+SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1000, 4097, TILE8 - 1, TILE8, TILE8 + 1, TILE - 1, TILE,
+         TILE + 1, 3 * TILE + 17, 65536 + 1, 250001, 1000003]
 NP = {"i32": np.int32, "u32": np.uint32, "f32": np.float32}
 
 
@@ -33,22 +36,26 @@ def gpu():
 
 
 class Path:
-    """Select the single-workgroup ('single') or look-back ('multi') path, or the default."""
+    """Select a kernel path: 'single' (one workgroup walks all tiles), 'multi'
+    (the persistent multi-tile kernel, forced even for small n), 'fallback'
+    (one workgroup per tile, forced even for small n) or 'auto' (the default)."""
 
     def __init__(self, which):
         self.which = which
 
     def __enter__(self):
-        lim = {"single": 1 << 40, "multi": 0}.get(self.which)
+        lim = {"single": 1 << 40, "multi": 0, "fallback": 0}.get(self.which)
         self.old = dw.scan_set_small_n_max(lim) if lim is not None else None
+        self.old_mode = dw.scan_set_multi_tile_mode(1 if self.which == "fallback" else 0)
 
     def __exit__(self, *a):
         if self.old is not None:
             dw.scan_set_small_n_max(self.old)
+        dw.scan_set_multi_tile_mode(self.old_mode)
 
 
 def paths_for(n):
-    return ["multi", "single"] if n <= 3 * TILE + 17 else ["auto"]
+    return ["multi", "single", "fallback"] if n <= 3 * TILE + 17 else ["auto", "fallback"]
 
 
 def values(dt, n, seed):
@@ -68,7 +75,7 @@ def check_scan(op, x, y_gpu, exclusive, what):
 
 # ---------------------------------------------------------------- worked examples
 @pytest.mark.parametrize("rec", golden_fixtures.all_examples("scan"), ids=lambda r: r["path"].split("/")[-1])
-@pytest.mark.parametrize("path", ["single", "multi"])
+@pytest.mark.parametrize("path", ["single", "multi", "fallback"])
 def test_golden_scan_on_gpu(rec, path):
     for dt in (rec["dtype"], np.int32, np.float32):
         x = rec["input"].astype(dt)
@@ -82,7 +89,7 @@ def test_golden_scan_on_gpu(rec, path):
 
 
 @pytest.mark.parametrize("rec", golden_fixtures.all_examples("compact"), ids=lambda r: r["path"].split("/")[-1])
-@pytest.mark.parametrize("path", ["single", "multi"])
+@pytest.mark.parametrize("path", ["single", "multi", "fallback"])
 def test_golden_compact_on_gpu(rec, path):
     for dt in (rec["dtype"], np.int32, np.float32):
         x = rec["input"].astype(dt)
@@ -129,6 +136,7 @@ HEAD_MIXES = {
     "all": lambda s, n: np.ones(n, np.uint8),
     "first_only": lambda s, n: np.zeros(n, np.uint8),
     "tile_starts": lambda s, n: (np.arange(n) % TILE == 0).astype(np.uint8) * 7,
+    "tile_ends": lambda s, n: (np.arange(n) % TILE == TILE - 1).astype(np.uint8),
 }
 
 
@@ -156,7 +164,7 @@ def test_segmented_head_zero_flag_ignored():
     x = np.arange(1, 10001, dtype=np.int32)
     h = np.zeros(x.size, np.uint8)
     h[5000] = 1
-    for path in ("single", "multi"):
+    for path in ("single", "multi", "fallback"):
         with Path(path):
             y = from_dev(dw.segmented_scan(to_dev(x), to_dev(h), "add"))
         assert_equal(y, oracle.segmented_scan("add", x, h), "head[0]=0 path=%s" % path)
@@ -191,7 +199,7 @@ def test_compact_parity(dt):
 
 def test_compact_special_values():
     x = np.array([0.0, -0.0, np.nan, 1.0, -1.0, np.inf, -np.inf, 1e-45, -1e-45] * 1000, np.float32)
-    for path in ("single", "multi"):
+    for path in ("single", "multi", "fallback"):
         with Path(path):
             out, cnt = dw.compact(to_dev(x))
             out, cnt = from_dev(out), int(from_dev(cnt)[0])
@@ -282,3 +290,28 @@ def test_repeat_runs_bit_exact():
         if rep % 4 == 0:
             assert_equal(from_dev(dw.scan_inclusive(abd, "affine")), ref_ab, "repeat %d affine" % rep)
     assert dw.scan_get_device_error() == 0
+
+
+def test_bounded_waits_report_timeout_and_recover():
+    # A tiny spin limit makes waits give up at once: the call must still
+    # finish (every wave exits), report SCAN_ERR_TIMEOUT, clear it when read,
+    # and leave later calls correct.
+    n = (1 << 24) + 5
+    x = si.float32_01(93, n)
+    xd = to_dev(x)
+    ref, s = oracle.scan("add", x)
+    for mode in (0, 1):
+        old_mode = dw.scan_set_multi_tile_mode(mode)
+        old = dw.scan_set_spin_limit(0)
+        try:
+            for _ in range(3):
+                dw.scan_inclusive(xd, "add")
+            st = dw.scan_get_device_error()
+        finally:
+            dw.scan_set_spin_limit(old)
+        assert st in (0, 5), st
+        assert dw.scan_get_device_error() == 0
+        y = from_dev(dw.scan_inclusive(xd, "add"))
+        dw.scan_set_multi_tile_mode(old_mode)
+        assert_f32_close(y, ref, s, "after timeout mode=%d" % mode)
+        assert dw.scan_get_device_error() == 0
