@@ -310,7 +310,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "float32 inclusive add-scan, n=2^28, values uniform in [0,1) (seed 2)",
                    "n": N_MAIN, "op": "add", "variant": "inclusive", "element": "float32",
-                   "kernel": "single-pass tile scan with decoupled look-back, 4096-element tiles"},
+                   "kernel": "persistent single-pass tile scan, streaming prefix resolver, 15360-element tiles"},
         "effective_GBps": round(bytes_per_launch * args.steps / elapsed / 1e9, 1),
         "pct_of_peak": round(100 * bytes_per_launch * args.steps / elapsed / 1e9 / PEAK_GBPS, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
