@@ -35,6 +35,8 @@ struct Shape {
     static constexpr int BLOCK = DWPT_BLOCK;
     static constexpr int ITEMS = sizeof(typename Op::elem_t) == 8 ? DWPT_ITEMS8 : DWPT_ITEMS4;
     static constexpr int TILE = Geometry<Op, BLOCK, ITEMS>::TILE;
+    // tiles per data wavefront waiting on their prefix in the persistent kernel
+    static constexpr int WAIT = (IsSeg<Op>::value || sizeof(typename Op::elem_t) == 8) ? 2 : 3;
 };
 
 // ------------------------------------------------------------ settings
@@ -210,7 +212,7 @@ scan_status_t run_scan(const Call& c, bool vec_ok)
     using S = Shape<Op>;
     return launch<S::BLOCK, S::TILE, Op::kWords>(tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, true>,
                                                  tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, false>,
-                                                 tile_scan_persistent<Op, EXCL, S::BLOCK, S::ITEMS>, c, vec_ok);
+                                                 tile_scan_persistent<Op, EXCL, S::BLOCK, S::ITEMS, S::WAIT>, c, vec_ok);
 }
 
 template <typename T>
@@ -219,7 +221,7 @@ scan_status_t run_compact(const Call& c, bool vec_ok)
     constexpr int BLOCK = DWPT_BLOCK, ITEMS = DWPT_ITEMS4;
     return launch<BLOCK, Geometry<OpAdd<uint32_t>, BLOCK, ITEMS>::TILE, 1>(
         compact_kernel<T, BLOCK, ITEMS, true>, compact_kernel<T, BLOCK, ITEMS, false>,
-        compact_persistent<T, BLOCK, ITEMS>, c, vec_ok);
+        compact_persistent<T, BLOCK, ITEMS, 3>, c, vec_ok);
 }
 
 typedef scan_status_t (*Runner)(const Call&, bool);

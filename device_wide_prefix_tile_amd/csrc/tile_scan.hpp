@@ -539,14 +539,18 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //    scanned again when its prefix arrives.  The last wavefront of the
 //    workgroup only fetches the prefixes the resolver publishes, one word
 //    per tile.
-//  * Data and prefix wavefronts meet through a four-slot ring in LDS
-//    (iteration k uses slot k & 3) with sequence numbers instead of
-//    barriers: a slot is rewritten only after every wavefront has passed the
-//    prefix wait of the iteration two before, so four slots are enough.
+//  * Data and prefix wavefronts meet through a ring of LDS slots (tile k of
+//    the workgroup uses slot k mod kPipeSlots) with sequence numbers instead
+//    of barriers.  The total of tile k is handed over kPipeWait - 1
+//    iterations before its prefix is awaited; a wavefront that hands over
+//    tile k + S has passed the prefix wait of tile k + S - kPipeWait, which
+//    needed every wavefront's hand-over of that tile, i.e. every wavefront
+//    has finished tile k when S >= 2 * kPipeWait.  So slots are never
+//    rewritten early.
 //  * Progress: every workgroup is resident; the resolver only waits for
 //    totals, which a data workgroup publishes before it waits for any
 //    prefix of a later tile; waits are bounded by the spin limit.
-constexpr int kPipeSlots = 4;
+constexpr int kPipeSlots = 8;  // >= 2 * WAIT (see the ring note above)
 #ifndef DWPT_RESOLVE_SPAN
 #define DWPT_RESOLVE_SPAN 4  // tiles per lane of the resolver's window
 #endif
@@ -711,9 +715,11 @@ struct WaveTile {
     }
 };
 
-template <class Op, bool EXCL, int BLOCK, int ITEMS>
+template <class Op, bool EXCL, int BLOCK, int ITEMS, int WAIT>
 __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
 {
+    constexpr int kPipeWait = WAIT, kPipeTiles = WAIT + 1;
+    static_assert(kPipeSlots >= 2 * kPipeWait, "slot ring too short for the pipeline depth");
     using G = Geometry<Op, BLOCK, ITEMS>;
     using E = typename Op::elem_t;
     using V = typename Op::value_t;
@@ -737,57 +743,63 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
         return;
     }
 
-    // three tiles per data wavefront: a (waiting for its prefix), b (total
-    // published), c (loads in flight)
-    E ea[R][VEC], eb[R][VEC], ec[R][VEC];
-    uint32_t ha[R], hb[R], hc[R];
-    WaveTile<G> ta, tb, tc;
-    ta.set(p, tile_of(first, 0, stride), w);
-    tb.set(p, tile_of(first, 1, stride), w);
-    issue_loads<Op, R, VEC>(p, ta.base, ta.vec, lane, ea, ha);
-    if (tb.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, tb.base, tb.vec, lane, eb, hb);
-    hand_over_slot<Op, Slot, ND>(p, ta.tile, 0, w, lane, reduce_wave<Op, R, VEC>(ta.base, lane, ea, ha),
-                                 &s_slot[0]);
-    for (uint32_t k = 0; ta.tile < p.num_tiles; ++k) {
-        tc.set(p, tile_of(first, k + 2, stride), w);
-        if (tc.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, tc.base, tc.vec, lane, ec, hc);
-        if (tb.tile < p.num_tiles)
-            hand_over_slot<Op, Slot, ND>(p, tb.tile, k + 1, w, lane, reduce_wave<Op, R, VEC>(tb.base, lane, eb, hb),
-                                         &s_slot[(k + 1) % kPipeSlots]);
+    // WAIT + 1 tiles per data wavefront, oldest first: stage 0 waits for its
+    // prefix, stages 1 .. WAIT-1 have their totals out, the newest loads.
+    E e[kPipeTiles][R][VEC];
+    uint32_t h[kPipeTiles][R];
+    WaveTile<G> t[kPipeTiles];
+#pragma unroll
+    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, tile_of(first, q, stride), w);
+#pragma unroll
+    for (int q = 0; q < kPipeTiles - 1; ++q)
+        if (t[q].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[q].base, t[q].vec, lane, e[q], h[q]);
+#pragma unroll
+    for (int q = 0; q < kPipeWait - 1; ++q)
+        if (t[q].tile < p.num_tiles)
+            hand_over_slot<Op, Slot, ND>(p, t[q].tile, q, w, lane, reduce_wave<Op, R, VEC>(t[q].base, lane, e[q], h[q]),
+                                         &s_slot[q % kPipeSlots]);
+    for (uint32_t k = 0; t[0].tile < p.num_tiles; ++k) {
+        constexpr int NEW = kPipeTiles - 1, PUB = kPipeWait - 1;
+        if (t[NEW].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], h[NEW]);
+        if (t[PUB].tile < p.num_tiles)
+            hand_over_slot<Op, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane,
+                                         reduce_wave<Op, R, VEC>(t[PUB].base, lane, e[PUB], h[PUB]),
+                                         &s_slot[(k + PUB) % kPipeSlots]);
 
         Slot* slot = &s_slot[k % kPipeSlots];
         wait_seq(&slot->prefix_seq, k + 1);
         {
             V x[R][VEC], lane_excl[R], round_carry[R + 1];
             uint32_t raw_head[R];
-            to_values<Op, R, VEC>(ta.base, lane, ea, ha, x, raw_head);
+            to_values<Op, R, VEC>(t[0].base, lane, e[0], h[0], x, raw_head);
             scan_wave<Op, R, VEC>(x, lane_excl, round_carry);
             V wave_prefix = Op::identity();
 #pragma unroll
             for (int q = 0; q < ND; ++q)
                 if (q < w) wave_prefix = Op::combine(wave_prefix, slot->wave_total[q]);
-            apply_store<Op, EXCL, R, VEC>(p, ta.base, ta.vec, lane, slot->prefix, wave_prefix, x, lane_excl,
+            apply_store<Op, EXCL, R, VEC>(p, t[0].base, t[0].vec, lane, slot->prefix, wave_prefix, x, lane_excl,
                                           round_carry, raw_head);
         }
-        // rotate: b -> a, c -> b
+        // shift the stages down; the newest gets the next tile
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            ha[r] = hb[r];
-            hb[r] = hc[r];
+        for (int q = 0; q + 1 < kPipeTiles; ++q) {
+            t[q] = t[q + 1];
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                ea[r][j] = eb[r][j];
-                eb[r][j] = ec[r][j];
+            for (int r = 0; r < R; ++r) {
+                h[q][r] = h[q + 1][r];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) e[q][r][j] = e[q + 1][r][j];
             }
         }
-        ta = tb;
-        tb = tc;
+        t[NEW].set(p, tile_of(first, k + kPipeTiles, stride), w);
     }
 }
 
-template <typename T, int BLOCK, int ITEMS>
+template <typename T, int BLOCK, int ITEMS, int WAIT>
 __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
 {
+    constexpr int kPipeWait = WAIT, kPipeTiles = WAIT + 1;
+    static_assert(kPipeSlots >= 2 * kPipeWait, "slot ring too short for the pipeline depth");
     using Cnt = OpAdd<uint32_t>;
     using Ld = OpMax<T>;  // element loads of T (identity past n: never kept)
     using G = Geometry<Cnt, BLOCK, ITEMS>;
@@ -836,24 +848,28 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
     };
 
     T* region = s_keep + w * G::WAVE_ELEMS;
-    T ea[R][VEC], eb[R][VEC], ec[R][VEC];
+    T e[kPipeTiles][R][VEC];
     uint32_t hu[R];
-    WaveTile<G> ta, tb, tc;
-    ta.set(p, tile_of(first, 0, stride), w);
-    tb.set(p, tile_of(first, 1, stride), w);
-    issue_loads<Ld, R, VEC>(p, ta.base, ta.vec, lane, ea, hu);
-    if (tb.tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, tb.base, tb.vec, lane, eb, hu);
-    hand_over_slot<Cnt, Slot, ND>(p, ta.tile, 0, w, lane, count_wave(ea, ta.base), &s_slot[0]);
-    for (uint32_t k = 0; ta.tile < p.num_tiles; ++k) {
-        tc.set(p, tile_of(first, k + 2, stride), w);
-        if (tc.tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, tc.base, tc.vec, lane, ec, hu);
-        if (tb.tile < p.num_tiles)
-            hand_over_slot<Cnt, Slot, ND>(p, tb.tile, k + 1, w, lane, count_wave(eb, tb.base),
-                                          &s_slot[(k + 1) % kPipeSlots]);
+    WaveTile<G> t[kPipeTiles];
+#pragma unroll
+    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, tile_of(first, q, stride), w);
+#pragma unroll
+    for (int q = 0; q < kPipeTiles - 1; ++q)
+        if (t[q].tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, t[q].base, t[q].vec, lane, e[q], hu);
+#pragma unroll
+    for (int q = 0; q < kPipeWait - 1; ++q)
+        if (t[q].tile < p.num_tiles)
+            hand_over_slot<Cnt, Slot, ND>(p, t[q].tile, q, w, lane, count_wave(e[q], t[q].base), &s_slot[q % kPipeSlots]);
+    for (uint32_t k = 0; t[0].tile < p.num_tiles; ++k) {
+        constexpr int NEW = kPipeTiles - 1, PUB = kPipeWait - 1;
+        if (t[NEW].tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], hu);
+        if (t[PUB].tile < p.num_tiles)
+            hand_over_slot<Cnt, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane, count_wave(e[PUB], t[PUB].base),
+                                          &s_slot[(k + PUB) % kPipeSlots]);
         Slot* slot = &s_slot[k % kPipeSlots];
         uint32_t kept[R];
-        kept_bits(ea, ta.base, kept);
-        const uint32_t cnt = pack_wave<T, R, VEC>(ea, kept, region);
+        kept_bits(e[0], t[0].base, kept);
+        const uint32_t cnt = pack_wave<T, R, VEC>(e[0], kept, region);
         wait_seq(&slot->prefix_seq, k + 1);
         uint32_t wave_prefix = 0;
 #pragma unroll
@@ -862,14 +878,14 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
         const uint64_t dst = (uint64_t)slot->prefix + wave_prefix;
         for (uint32_t i = lane; i < cnt; i += 64) out[dst + i] = region[i];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int q = 0; q + 1 < kPipeTiles; ++q) {
+            t[q] = t[q + 1];
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                ea[r][j] = eb[r][j];
-                eb[r][j] = ec[r][j];
-            }
-        ta = tb;
-        tb = tc;
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) e[q][r][j] = e[q + 1][r][j];
+        }
+        t[NEW].set(p, tile_of(first, k + kPipeTiles, stride), w);
     }
 }
 
