@@ -51,12 +51,13 @@ struct Workspace {
     size_t status_words = 0;  // capacity in 64-bit status words
     uint64_t* status = nullptr;
     uint32_t* ctr = nullptr;
+    uint32_t* pipe_ctr = nullptr;  // persistent kernel's self-resetting counters (3 words)
     uint32_t* err = nullptr;
     uint32_t ctr_base = 0;
     uint32_t epoch = 0;
 };
 std::map<std::pair<int, void*>, Workspace> g_ws;
-constexpr size_t kHeaderBytes = 256;  // err word, tile counter, padding
+constexpr size_t kHeaderBytes = 256;  // err word, tile counter, persistent-kernel counters, padding
 
 __global__ void zero_words_kernel(uint64_t* p, size_t nwords)
 {
@@ -104,6 +105,7 @@ scan_status_t acquire_workspace(hipStream_t s, size_t words, Workspace** out)
         ws.status_words = cap;
         ws.err = static_cast<uint32_t*>(mem);
         ws.ctr = static_cast<uint32_t*>(mem) + 1;
+        ws.pipe_ctr = static_cast<uint32_t*>(mem) + 2;
         ws.status = reinterpret_cast<uint64_t*>(static_cast<char*>(mem) + kHeaderBytes);
         ws.ctr_base = 0;
         ws.epoch = 0;
@@ -139,23 +141,22 @@ int resident_capacity(const void* f, int block)
     const auto key = std::make_pair(dev, f);
     auto it = cache.find(key);
     if (it != cache.end()) return it->second;
-    int per_cu = 0, cus = 0, coop = 0;
+    int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, block, 0) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess) {
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
         (void)hipGetLastError();
         per_cu = 0;
     }
-    const int cap = coop ? per_cu * cus : 0;
+    const int cap = per_cu * cus;
     cache[key] = cap;
     return cap;
 }
 
 // Fills params and launches the single-workgroup kernel (small n), else the
-// persistent pipelined kernel (cooperative launch, every workgroup
-// resident), else -- when a cooperative launch is not possible -- the
-// one-tile-per-workgroup kernel.  TILE is the tile size and kWords the
-// status words per tile.
+// persistent pipelined kernel (as many workgroups as fit, plus none beyond
+// one per tile and the resolver), or the one-tile-per-workgroup kernel when
+// that mode is selected.  TILE is the tile size and kWords the status words
+// per tile.
 template <int BLOCK, int TILE, int kWords>
 scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(ScanParams), const Call& c,
                      bool vec_ok)
@@ -183,6 +184,7 @@ scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(
     if (st != SCAN_OK) return st;
     p.tile_ctr = ws->ctr;
     p.ctr_base = ws->ctr_base;
+    p.pipe_ctr = ws->pipe_ctr;
     p.lb.status = ws->status;
     p.lb.groups = ws->status + (size_t)tiles * kWords;
     p.lb.err = ws->err;
@@ -191,13 +193,10 @@ scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(
     if (g_multi_mode == 0) {
         const int cap = resident_capacity((const void*)kp, BLOCK);
         if (cap > 1) {
-            // workgroup 0 resolves prefixes; the others scan tiles
+            // the first workgroup to start resolves prefixes; the others scan tiles
             const unsigned grid = 1u + (unsigned)std::min<uint64_t>((uint64_t)cap - 1, tiles);
-            void* args[] = {&p};
-            if (hipLaunchCooperativeKernel((const void*)kp, dim3(grid), dim3(BLOCK), args, 0, c.stream) ==
-                hipSuccess)
-                return SCAN_OK;
-            (void)hipGetLastError();  // not possible right now: one tile per workgroup instead
+            hipLaunchKernelGGL(kp, dim3(grid), dim3(BLOCK), 0, c.stream, p);
+            return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
         }
     }
     hipLaunchKernelGGL(km, dim3(p.num_tiles), dim3(BLOCK), 0, c.stream, p);

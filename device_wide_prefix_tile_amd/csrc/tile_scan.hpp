@@ -55,6 +55,7 @@ struct ScanParams {
     uint32_t num_tiles;
     uint32_t ctr_base;     // counter value when this launch started
     uint32_t* tile_ctr;
+    uint32_t* pipe_ctr;    // persistent kernel: [0] next tile, [1] roles taken, [2] workgroups retired
     Lookback lb;
     int vec_ok;            // 16-byte aligned pointers: vector loads/stores
 };
@@ -518,38 +519,46 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 }
 
 // ============================================================ persistent
-// Persistent, software-pipelined variant of the multi-tile path, launched
-// cooperatively with exactly as many workgroups as can be resident together.
+// Persistent, software-pipelined variant of the multi-tile path: a normal
+// launch of as many workgroups as fit on the GPU, each looping over tiles.
 //
-//  * Workgroup 0 is the resolver: one wavefront that streams through the
-//    tile totals in tile order, scans them 64 * RSPAN at a time and
-//    publishes each tile's exclusive prefix (lookback.hpp, resolve_stream).
-//    It loads no data, so its status reads do not queue behind tile loads,
-//    and each total is read about once.  (A look-back by every tile would
-//    have ~250 tiles in flight each reading ~250 statuses of the same
-//    region per round; measured, those reads queued behind the tile data on
-//    every CU and hammered the same cache lines.)
-//  * Workgroups 1 .. G-1 scan tiles dealt round-robin: workgroup b takes
-//    tiles b-1, b-1 + (G-1), ...  Every data wavefront keeps three of its
-//    tiles in flight as raw elements in registers: while it waits for the
-//    prefix of tile k, the total of tile k+1 is already published and the
-//    loads of tile k+2 are on their way.  So totals go out as soon as the
-//    data arrives, and the wait for a prefix overlaps memory traffic.  The
-//    in-register scan is cheap, so a tile is reduced once for its total and
-//    scanned again when its prefix arrives.  The last wavefront of the
-//    workgroup only fetches the prefixes the resolver publishes, one word
-//    per tile.
-//  * Data and prefix wavefronts meet through a ring of LDS slots (tile k of
-//    the workgroup uses slot k mod kPipeSlots) with sequence numbers instead
-//    of barriers.  The total of tile k is handed over kPipeWait - 1
+//  * Roles.  The first workgroup to start becomes the resolver: one
+//    wavefront that streams through the tile totals in tile order, scans
+//    them 64 * RSPAN at a time and publishes each tile's exclusive prefix
+//    (lookback.hpp, resolve_stream).  It loads no data, so its status reads
+//    do not queue behind tile loads, and each total is read about once.  (A
+//    look-back by every tile would have hundreds of tiles in flight reading
+//    the same status words; measured, those reads queued behind the tile
+//    data on every CU.)
+//  * Tiles.  The other workgroups take tile numbers from a counter, in the
+//    order they ask.  A tile therefore only ever waits on tiles already
+//    taken by running workgroups, and the resolver has started before any
+//    tile is taken, so no co-residency guarantee is needed (a cooperative
+//    launch was measured to cost ~17 us per call).  The last workgroup to
+//    retire resets the counters for the next launch on the stream.
+//  * Pipeline.  Every data wavefront keeps WAIT + 1 of its tiles in flight
+//    as raw elements in registers: while it waits for the prefix of its
+//    oldest tile, the totals of the next WAIT - 1 are already published and
+//    the loads of the newest are on their way.  WAIT is 3 for plain 4-byte
+//    scans and compaction (measured: 430 us against 466 us at WAIT = 2 for
+//    the float32 add at 2^28; a second loading stage or WAIT = 4 gave nothing
+//    more) and 2 for the wider segmented and affine values, which would not
+//    fit in 128 registers at 3.  The in-register scan is cheap, so a tile is
+//    reduced once for its total and scanned again when its prefix arrives.
+//    The last wavefront of a data workgroup only fetches the prefixes the
+//    resolver publishes, one word per tile.  Wavefront 0 asks for the next
+//    tile number one iteration before it is needed.
+//  * Rings.  Data and prefix wavefronts meet through rings of LDS slots (the
+//    k-th tile of the workgroup uses slot k mod 8) with sequence numbers
+//    instead of barriers.  The total of the k-th tile is handed over WAIT - 1
 //    iterations before its prefix is awaited; a wavefront that hands over
-//    tile k + S has passed the prefix wait of tile k + S - kPipeWait, which
+//    tile k + S has passed the prefix wait of tile k + S - WAIT, which
 //    needed every wavefront's hand-over of that tile, i.e. every wavefront
-//    has finished tile k when S >= 2 * kPipeWait.  So slots are never
-//    rewritten early.
-//  * Progress: every workgroup is resident; the resolver only waits for
-//    totals, which a data workgroup publishes before it waits for any
-//    prefix of a later tile; waits are bounded by the spin limit.
+//    has finished tile k when S >= 2 * WAIT.  So slots are never rewritten
+//    early; the tile-number ring is safe by the same argument.
+//  * Progress.  Every wait is on lower tiles or on the resolver, which only
+//    waits for totals; a total is published before its workgroup waits for
+//    any later prefix; every wait is bounded by the spin limit.
 constexpr int kPipeSlots = 8;  // >= 2 * WAIT (see the ring note above)
 #ifndef DWPT_RESOLVE_SPAN
 #define DWPT_RESOLVE_SPAN 4  // tiles per lane of the resolver's window
@@ -667,30 +676,103 @@ __device__ __forceinline__ void wait_seq(uint32_t* seq, uint32_t want)
         __builtin_amdgcn_s_sleep(1);
 }
 
-template <class Slot>
-__device__ __forceinline__ void init_slots(Slot* s)
+
+
+// Tile numbers of a data workgroup, in the order it processes them.
+struct TileIdRing {
+    uint32_t id[kPipeSlots];
+    uint32_t seq[kPipeSlots];  // k + 1 once id[k mod 8] holds the k-th tile number
+};
+
+__device__ __forceinline__ void put_id(TileIdRing* r, uint32_t k, uint32_t id)
 {
-    if (threadIdx.x < kPipeSlots) {
-        s[threadIdx.x].arrived = 0u;
-        s[threadIdx.x].prefix_seq = 0u;
-    }
-    __syncthreads();
+    r->id[k % kPipeSlots] = id;
+    __hip_atomic_store(&r->seq[k % kPipeSlots], k + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// k-th tile of data workgroup `first` (0-based) among `stride` of them:
-// tiles are dealt round-robin.
-__device__ __forceinline__ uint32_t tile_of(uint32_t first, uint32_t k, uint32_t stride)
+__device__ __forceinline__ uint32_t get_id(TileIdRing* r, uint32_t k)
 {
-    return first + k * stride;
+    while (__hip_atomic_load(&r->seq[k % kPipeSlots], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < k + 1)
+        __builtin_amdgcn_s_sleep(1);
+    return r->id[k % kPipeSlots];
+}
+
+// Workgroup start: take a role (0 = resolver) and clear the LDS rings.
+template <class Slot>
+__device__ __forceinline__ uint32_t start_workgroup(const ScanParams& p, Slot* slots, TileIdRing* ids,
+                                                    uint32_t* s_role)
+{
+    if (threadIdx.x == 0)
+        *s_role = __hip_atomic_fetch_add(&p.pipe_ctr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < kPipeSlots) {
+        slots[threadIdx.x].arrived = 0u;
+        slots[threadIdx.x].prefix_seq = 0u;
+        ids->seq[threadIdx.x] = 0u;
+    }
+    __syncthreads();
+    return *s_role;
+}
+
+// Called by one lane once its workgroup is done with the counters; the last
+// workgroup of the launch resets them for the next one.
+__device__ __forceinline__ void retire_workgroup(const ScanParams& p)
+{
+    const uint32_t d = __hip_atomic_fetch_add(&p.pipe_ctr[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == gridDim.x - 1) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) __hip_atomic_store(&p.pipe_ctr[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Wavefront 0 of a data workgroup takes its first NT tile numbers one round
+// trip after another, so that they interleave with the other workgroups'
+// requests (about one grid apart, like a round-robin deal).  Taking them in
+// one go would hand a workgroup consecutive tiles, and the total of its last
+// one -- published only after the prefix of its first -- would then hold up
+// every later tile: measured, a serial chain seven times slower.  Returns
+// true once a number past the last tile came back.
+template <int NT>
+__device__ __forceinline__ bool take_first_ids(const ScanParams& p, TileIdRing* ids)
+{
+    bool exhausted = false;
+#pragma unroll
+    for (int q = 0; q < NT; ++q) {
+        uint32_t id = p.num_tiles;
+        if (!exhausted) {
+            if (lane_id() == 0)
+                id = __hip_atomic_fetch_add(&p.pipe_ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            id = (uint32_t)__builtin_amdgcn_readfirstlane((int)id);
+            exhausted = id >= p.num_tiles;
+        }
+        if (lane_id() == 0) put_id(ids, (uint32_t)q, id);
+    }
+    return exhausted;
+}
+
+// Wavefront 0 asks for a tile number one iteration before it is needed: the
+// request goes out at the top of the iteration (lane 0) and its result is
+// used only at the end, so the counter's round trip overlaps the iteration.
+__device__ __forceinline__ uint32_t ask_id(const ScanParams& p, bool exhausted)
+{
+    uint32_t id = p.num_tiles;
+    if (!exhausted && lane_id() == 0)
+        id = __hip_atomic_fetch_add(&p.pipe_ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return id;  // valid in lane 0
+}
+
+__device__ __forceinline__ void post_id(const ScanParams& p, TileIdRing* ids, uint32_t k, uint32_t id, bool& exhausted)
+{
+    if (lane_id() == 0) put_id(ids, k, id);
+    exhausted = exhausted || (uint32_t)__builtin_amdgcn_readfirstlane((int)id) >= p.num_tiles;
 }
 
 // Prefix wavefront of a data workgroup: fetches the prefix of each of the
 // workgroup's tiles, in order, into the slot ring.
 template <class Op, class Slot>
-__device__ __forceinline__ void fetch_prefixes(const ScanParams& p, uint32_t first, uint32_t stride, Slot* slots)
+__device__ __forceinline__ void fetch_prefixes(const ScanParams& p, TileIdRing* ids, Slot* slots)
 {
     for (uint32_t k = 0;; ++k) {
-        const uint32_t tile = tile_of(first, k, stride);
+        const uint32_t tile = get_id(ids, k);
         if (tile >= p.num_tiles) break;
         const typename Op::carry_t excl = wait_excl<Op>(p.lb, p.lb.groups, tile);
         Slot* slot = &slots[k % kPipeSlots];
@@ -729,17 +811,21 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     static_assert(!IsSeg<Op>::value || VEC == 4, "segmented scans use 4-byte elements");
 
     __shared__ Slot s_slot[kPipeSlots];
+    __shared__ TileIdRing s_ids;
+    __shared__ uint32_t s_role;
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
-    if (blockIdx.x == 0) {
-        if (w == 0) (void)resolve_stream<Op, DWPT_RESOLVE_SPAN>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
+    if (start_workgroup(p, s_slot, &s_ids, &s_role) == 0) {
+        if (w == 0) {
+            (void)resolve_stream<Op, DWPT_RESOLVE_SPAN>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
+            if (lane == 0) retire_workgroup(p);
+        }
         return;
     }
-    init_slots(s_slot);
-    const uint32_t stride = gridDim.x - 1;
-    const uint32_t first = blockIdx.x - 1;
+    bool exhausted = false;
+    if (w == 0) exhausted = take_first_ids<kPipeTiles>(p, &s_ids);
     if (w == ND) {
-        fetch_prefixes<Op>(p, first, stride, s_slot);
+        fetch_prefixes<Op>(p, &s_ids, s_slot);
         return;
     }
 
@@ -749,7 +835,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     uint32_t h[kPipeTiles][R];
     WaveTile<G> t[kPipeTiles];
 #pragma unroll
-    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, tile_of(first, q, stride), w);
+    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id(&s_ids, q), w);
 #pragma unroll
     for (int q = 0; q < kPipeTiles - 1; ++q)
         if (t[q].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[q].base, t[q].vec, lane, e[q], h[q]);
@@ -760,6 +846,10 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
                                          &s_slot[q % kPipeSlots]);
     for (uint32_t k = 0; t[0].tile < p.num_tiles; ++k) {
         constexpr int NEW = kPipeTiles - 1, PUB = kPipeWait - 1;
+        // the tile number for the next iteration goes out before this
+        // iteration's loads, so waiting for it never waits for them
+        uint32_t next_id = p.num_tiles;
+        if (w == 0) next_id = ask_id(p, exhausted);
         if (t[NEW].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], h[NEW]);
         if (t[PUB].tile < p.num_tiles)
             hand_over_slot<Op, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane,
@@ -791,8 +881,10 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
                 for (int j = 0; j < VEC; ++j) e[q][r][j] = e[q + 1][r][j];
             }
         }
-        t[NEW].set(p, tile_of(first, k + kPipeTiles, stride), w);
+        if (w == 0) post_id(p, &s_ids, k + kPipeTiles, next_id, exhausted);
+        t[NEW].set(p, get_id(&s_ids, k + kPipeTiles), w);
     }
+    if (w == 0 && lane == 0) retire_workgroup(p);
 }
 
 template <typename T, int BLOCK, int ITEMS, int WAIT>
@@ -809,21 +901,25 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
 
     __shared__ T s_keep[G::TILE];  // wavefront w packs into [w * WAVE_ELEMS, ...)
     __shared__ Slot s_slot[kPipeSlots];
+    __shared__ TileIdRing s_ids;
+    __shared__ uint32_t s_role;
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
-    if (blockIdx.x == 0) {
+    if (start_workgroup(p, s_slot, &s_ids, &s_role) == 0) {
         if (w == 0) {
             const uint32_t total = resolve_stream<Cnt, DWPT_RESOLVE_SPAN>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
-            if (lane == 0) *p.count = total;
+            if (lane == 0) {
+                *p.count = total;
+                retire_workgroup(p);
+            }
         }
         return;
     }
-    init_slots(s_slot);
-    const uint32_t stride = gridDim.x - 1;
-    const uint32_t first = blockIdx.x - 1;
+    bool exhausted = false;
+    if (w == 0) exhausted = take_first_ids<kPipeTiles>(p, &s_ids);
     T* __restrict__ out = static_cast<T*>(p.out);
     if (w == ND) {
-        fetch_prefixes<Cnt>(p, first, stride, s_slot);
+        fetch_prefixes<Cnt>(p, &s_ids, s_slot);
         return;
     }
 
@@ -852,7 +948,7 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
     uint32_t hu[R];
     WaveTile<G> t[kPipeTiles];
 #pragma unroll
-    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, tile_of(first, q, stride), w);
+    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id(&s_ids, q), w);
 #pragma unroll
     for (int q = 0; q < kPipeTiles - 1; ++q)
         if (t[q].tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, t[q].base, t[q].vec, lane, e[q], hu);
@@ -862,6 +958,8 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
             hand_over_slot<Cnt, Slot, ND>(p, t[q].tile, q, w, lane, count_wave(e[q], t[q].base), &s_slot[q % kPipeSlots]);
     for (uint32_t k = 0; t[0].tile < p.num_tiles; ++k) {
         constexpr int NEW = kPipeTiles - 1, PUB = kPipeWait - 1;
+        uint32_t next_id = p.num_tiles;
+        if (w == 0) next_id = ask_id(p, exhausted);
         if (t[NEW].tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], hu);
         if (t[PUB].tile < p.num_tiles)
             hand_over_slot<Cnt, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane, count_wave(e[PUB], t[PUB].base),
@@ -885,8 +983,10 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
 #pragma unroll
                 for (int j = 0; j < VEC; ++j) e[q][r][j] = e[q + 1][r][j];
         }
-        t[NEW].set(p, tile_of(first, k + kPipeTiles, stride), w);
+        if (w == 0) post_id(p, &s_ids, k + kPipeTiles, next_id, exhausted);
+        t[NEW].set(p, get_id(&s_ids, k + kPipeTiles), w);
     }
+    if (w == 0 && lane == 0) retire_workgroup(p);
 }
 
 }  // namespace dwpt

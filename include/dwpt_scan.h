@@ -142,9 +142,9 @@ scan_status_t scan_release_workspace(void);
  *   workgroup that walks the tiles in order (no workspace, no atomics); larger
  *   inputs use the multi-tile look-back kernel.  Default 4096.
  * scan_set_multi_tile_mode: 0 (default) runs large inputs on the persistent
- *   pipelined kernel (one cooperative launch of as many workgroups as fit on
- *   the GPU, each scanning every G-th tile); 1 runs one workgroup per tile
- *   (also the automatic fallback when a cooperative launch is not possible).
+ *   pipelined kernel (one launch of as many workgroups as fit on the GPU,
+ *   each taking tile numbers from a counter until the input is done); 1 runs
+ *   one workgroup per tile.
  * scan_set_spin_limit: number of look-back polls after which a waiting tile
  *   gives up, records SCAN_ERR_TIMEOUT (see scan_get_device_error) and
  *   finishes with a wrong prefix instead of waiting forever.  Default 2^18.
