@@ -17,26 +17,47 @@ using namespace dwpt;
 namespace {
 
 // ------------------------------------------------------------ tile shapes
-// Workgroup size and elements per lane (defaults: 1024 threads = 15 data
-// wavefronts + 1 look-back wavefront, 16 four-byte or 8 eight-byte elements
-// per lane, i.e. 60 KiB tiles); build-time switches so that shapes can be
-// compared by measurement.
+// Workgroup size, elements per lane and pipeline depth per class of scan
+// (defaults: 1024 threads = 15 data wavefronts + 1 prefix wavefront).  ITEMS
+// sets the tile (15 * 64 * ITEMS elements); WAIT is the number of tiles per
+// data wavefront that wait on their prefix in the persistent kernel.  Each
+// class takes the deepest pipeline that fits in 128 registers without
+// spilling, and the measured best tile.  Build-time switches, so that shapes
+// can be compared by measurement.
 #ifndef DWPT_BLOCK
 #define DWPT_BLOCK 1024
 #endif
-#ifndef DWPT_ITEMS4
+#ifndef DWPT_ITEMS4            // plain scans of 4-byte values
 #define DWPT_ITEMS4 16
 #endif
-#ifndef DWPT_ITEMS8
+#ifndef DWPT_WAIT4
+#define DWPT_WAIT4 4
+#endif
+#ifndef DWPT_ITEMS8            // 8-byte values (affine pairs)
 #define DWPT_ITEMS8 8
+#endif
+#ifndef DWPT_WAIT8
+#define DWPT_WAIT8 3
+#endif
+#ifndef DWPT_ITEMS_SEG         // segmented scans (value + head flag)
+#define DWPT_ITEMS_SEG 12
+#endif
+#ifndef DWPT_WAIT_SEG
+#define DWPT_WAIT_SEG 3
+#endif
+#ifndef DWPT_ITEMS_COMPACT     // stream compaction
+#define DWPT_ITEMS_COMPACT 12
+#endif
+#ifndef DWPT_WAIT_COMPACT
+#define DWPT_WAIT_COMPACT 4
 #endif
 template <class Op>
 struct Shape {
+    static constexpr bool SEG = IsSeg<Op>::value, WIDE = sizeof(typename Op::elem_t) == 8;
     static constexpr int BLOCK = DWPT_BLOCK;
-    static constexpr int ITEMS = sizeof(typename Op::elem_t) == 8 ? DWPT_ITEMS8 : DWPT_ITEMS4;
+    static constexpr int ITEMS = SEG ? DWPT_ITEMS_SEG : WIDE ? DWPT_ITEMS8 : DWPT_ITEMS4;
     static constexpr int TILE = Geometry<Op, BLOCK, ITEMS>::TILE;
-    // tiles per data wavefront waiting on their prefix in the persistent kernel
-    static constexpr int WAIT = (IsSeg<Op>::value || sizeof(typename Op::elem_t) == 8) ? 2 : 3;
+    static constexpr int WAIT = SEG ? DWPT_WAIT_SEG : WIDE ? DWPT_WAIT8 : DWPT_WAIT4;
 };
 
 // ------------------------------------------------------------ settings
@@ -217,10 +238,10 @@ scan_status_t run_scan(const Call& c, bool vec_ok)
 template <typename T>
 scan_status_t run_compact(const Call& c, bool vec_ok)
 {
-    constexpr int BLOCK = DWPT_BLOCK, ITEMS = DWPT_ITEMS4;
+    constexpr int BLOCK = DWPT_BLOCK, ITEMS = DWPT_ITEMS_COMPACT;
     return launch<BLOCK, Geometry<OpAdd<uint32_t>, BLOCK, ITEMS>::TILE, 1>(
         compact_kernel<T, BLOCK, ITEMS, true>, compact_kernel<T, BLOCK, ITEMS, false>,
-        compact_persistent<T, BLOCK, ITEMS, 3>, c, vec_ok);
+        compact_persistent<T, BLOCK, ITEMS, DWPT_WAIT_COMPACT>, c, vec_ok);
 }
 
 typedef scan_status_t (*Runner)(const Call&, bool);

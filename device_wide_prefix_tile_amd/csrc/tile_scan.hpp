@@ -86,10 +86,10 @@ __device__ __forceinline__ bool resets(typename Op::value_t v)
 
 // Build-time tuning switches (chosen by measurement; see the defaults).
 #ifndef DWPT_NT_LOADS
-#define DWPT_NT_LOADS 0   // streaming (non-temporal) hint on tile loads
+#define DWPT_NT_LOADS 1   // streaming (non-temporal) hint on tile loads
 #endif
 #ifndef DWPT_NT_STORES
-#define DWPT_NT_STORES 0  // streaming (non-temporal) hint on tile stores
+#define DWPT_NT_STORES 1  // streaming (non-temporal) hint on tile stores
 #endif
 #ifndef DWPT_STATIC_TILES
 #define DWPT_STATIC_TILES 0  // 1: tile number = workgroup index instead of a counter
@@ -549,7 +549,7 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //    resolver publishes, one word per tile.  Wavefront 0 asks for the next
 //    tile number one iteration before it is needed.
 //  * Rings.  Data and prefix wavefronts meet through rings of LDS slots (the
-//    k-th tile of the workgroup uses slot k mod 8) with sequence numbers
+//    k-th tile of the workgroup uses slot k mod 16) with sequence numbers
 //    instead of barriers.  The total of the k-th tile is handed over WAIT - 1
 //    iterations before its prefix is awaited; a wavefront that hands over
 //    tile k + S has passed the prefix wait of tile k + S - WAIT, which
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //  * Progress.  Every wait is on lower tiles or on the resolver, which only
 //    waits for totals; a total is published before its workgroup waits for
 //    any later prefix; every wait is bounded by the spin limit.
-constexpr int kPipeSlots = 8;  // >= 2 * WAIT (see the ring note above)
+constexpr int kPipeSlots = 16;  // >= 2 * WAIT (see the ring note above)
 #ifndef DWPT_RESOLVE_SPAN
 #define DWPT_RESOLVE_SPAN 4  // tiles per lane of the resolver's window
 #endif
@@ -681,7 +681,7 @@ __device__ __forceinline__ void wait_seq(uint32_t* seq, uint32_t want)
 // Tile numbers of a data workgroup, in the order it processes them.
 struct TileIdRing {
     uint32_t id[kPipeSlots];
-    uint32_t seq[kPipeSlots];  // k + 1 once id[k mod 8] holds the k-th tile number
+    uint32_t seq[kPipeSlots];  // k + 1 once id[k mod kPipeSlots] holds the k-th tile number
 };
 
 __device__ __forceinline__ void put_id(TileIdRing* r, uint32_t k, uint32_t id)
