@@ -141,10 +141,13 @@ scan_status_t scan_release_workspace(void);
  * scan_set_small_n_max: inputs with n at or below this size run on one
  *   workgroup that walks the tiles in order (no workspace, no atomics); larger
  *   inputs use the multi-tile look-back kernel.  Default 4096.
- * scan_set_multi_tile_mode: 0 (default) runs large inputs on the persistent
- *   pipelined kernel (one launch of as many workgroups as fit on the GPU,
- *   each taking tile numbers from a counter until the input is done); 1 runs
- *   one workgroup per tile.
+ * scan_set_multi_tile_mode: selects the kernel for inputs above the
+ *   small-n size.  2 runs the persistent pipelined kernel (one launch of as
+ *   many workgroups as fit on the GPU, each taking tile numbers from a
+ *   counter until the input is done); 1 runs one workgroup per tile; 0 (the
+ *   default) takes the persistent kernel from 8 tiles per resident
+ *   workgroup up (about 2^25 four-byte elements on 256 compute units) and
+ *   one workgroup per tile below.  Other values select 0.
  * scan_set_spin_limit: number of look-back polls after which a waiting tile
  *   gives up, records SCAN_ERR_TIMEOUT (see scan_get_device_error) and
  *   finishes with a wrong prefix instead of waiting forever.  Default 2^18.

@@ -32,11 +32,28 @@ def fresh():
     torch.cuda.empty_cache()
 
 
+class Mode:
+    """Force a multi-tile kernel: 1 one workgroup per tile, 2 persistent; 0 by size."""
+
+    def __init__(self, mode):
+        self.mode = mode
+
+    def __enter__(self):
+        self.old = dw.scan_set_multi_tile_mode(self.mode)
+
+    def __exit__(self, *a):
+        dw.scan_set_multi_tile_mode(self.old)
+
+
 def test_config1_int32_exclusive_add_2p20():
     n = 1 << 20
     x = si.int32_0_15(1, n)
-    y = from_dev(dw.scan_exclusive(to_dev(x), "add"))
-    assert_equal(y, oracle.scan("add", x, exclusive=True), "config1")
+    xd = to_dev(x)
+    ref = oracle.scan("add", x, exclusive=True)
+    for mode in (0, 1, 2):
+        with Mode(mode):
+            y = from_dev(dw.scan_exclusive(xd, "add"))
+        assert_equal(y, ref, "config1 mode=%d" % mode)
     ex = np.array([3, 1, 7, 0, 4, 1, 6, 3], np.int32)
     np.testing.assert_array_equal(from_dev(dw.scan_exclusive(to_dev(ex), "add")), [0, 3, 4, 11, 11, 15, 16, 22])
     np.testing.assert_array_equal(from_dev(dw.scan_inclusive(to_dev(ex), "add")), [3, 4, 11, 11, 15, 16, 22, 25])
@@ -84,5 +101,10 @@ def test_config5_segmented_add_2p27():
 def test_config5_max_sweep(k):
     n = 4 ** k
     x = si.int32_full(6, n)
-    y = from_dev(dw.scan_inclusive(to_dev(x), "max"))
-    assert_equal(y, oracle.scan("max", x), "config5 max sweep n=4^%d" % k)
+    xd = to_dev(x)
+    ref = oracle.scan("max", x)
+    # the size-selected kernel, and below 2^30 both multi-tile kernels forced
+    for mode in (0, 1, 2) if k < 15 else (0,):
+        with Mode(mode):
+            y = from_dev(dw.scan_inclusive(xd, "max"))
+        assert_equal(y, ref, "config5 max sweep n=4^%d mode=%d" % (k, mode))
