@@ -19,12 +19,16 @@ Also reported:
                 while the kernel sources still match the ones it was taken on.
   cpu_baseline  the sequential oracle on one host core over a bounded sample
                 (the first 2^26 elements of the same input).
-  copy_probe    a plain 16-byte streaming copy of 1 GiB, for the achievable
-                bandwidth on this machine.
+  copy_probe    a plain 16-byte copy of 1 GiB with streaming hints, for the
+                achievable bandwidth of a one-read-one-write kernel.
 
 --suite FILE additionally times every scan workload (int32 exclusive add at
 2^20 and 2^28, compaction, affine, segmented add, the max-scan size sweep)
 and writes one JSON line per workload to FILE.
+
+--workloads-once K runs each full-size workload K times (for rocprofv3
+counter passes); --summarize-traffic and --summarize-rocprof turn rocprofv3
+CSV output into the summaries under profiles/.
 """
 import argparse
 import hashlib
@@ -44,6 +48,7 @@ METRIC = "scan Gelem/s + effective HBM GB/s (% of peak), fp32/int32 n=2^28, 1 MI
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_f32_inclusive_add_2p28.txt")
 STATS_FILE = os.path.join(PROFILES, "kernel_stats_f32_inclusive_add_2p28.txt")
+TRAFFIC_ALL_FILE = os.path.join(PROFILES, "traffic_all_workloads.txt")
 SCAN_KERNEL = "tile_scan_persistent"
 COPY_KERNEL = "copy_probe_kernel"
 PROFILE_CMDS = {
@@ -53,7 +58,26 @@ PROFILE_CMDS = {
              "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/prof_write -o bench -- "
              "python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "wl_fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/prof_wl_fetch -o wl -- "
+                "python3 bench.py --workloads-once 3",
+    "wl_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/prof_wl_write -o wl -- "
+                "python3 bench.py --workloads-once 3",
 }
+
+# Full-size workloads for per-kernel counter runs: (label, kernel-name fragment,
+# n, algorithmic bytes per launch as a function of n and the kept count).
+WORKLOADS = [
+    ("float32 inclusive add 2^28", "tile_scan_persistent<dwpt::OpAdd<float>, false", 1 << 28,
+     lambda n, kept: 8 * n),
+    ("int32 exclusive add 2^28", "tile_scan_persistent<dwpt::OpAdd<int>, true", 1 << 28, lambda n, kept: 8 * n),
+    ("int32 inclusive max 2^28", "tile_scan_persistent<dwpt::OpMax<int>, false", 1 << 28, lambda n, kept: 8 * n),
+    ("compaction float32 N(0,1) 2^28 (read all, write kept)", "compact_persistent<float", 1 << 28,
+     lambda n, kept: 4 * n + 4 * kept),
+    ("uint32 affine inclusive 2^26 pairs", "tile_scan_persistent<dwpt::OpAffine, false", 1 << 26,
+     lambda n, kept: 16 * n),
+    ("segmented int32 inclusive add 2^27 (values, head bytes, out)",
+     "tile_scan_persistent<dwpt::OpSeg<dwpt::OpAdd<int> >, false", 1 << 27, lambda n, kept: 9 * n),
+]
 
 
 def log(msg):
@@ -167,6 +191,94 @@ def summarize_rocprof(trace_dir, fetch_dir, write_dir):
     print(open(TRAFFIC_FILE).read())
 
 
+def _counter_means(directory, counter, fragments):
+    """Mean counter value per dispatch for each kernel-name fragment (None if absent)."""
+    vals = {f: [] for f in fragments}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r.get("Counter_Name") != counter:
+            continue
+        for f in fragments:
+            if f in r.get("Kernel_Name", ""):
+                vals[f].append(float(r["Counter_Value"]))
+    return {f: (sum(v) / len(v) if v else None) for f, v in vals.items()}
+
+
+def summarize_workload_traffic(fetch_dir, write_dir):
+    """HBM bytes per launch of every full-size workload against its algorithmic bytes."""
+    import numpy as np
+    import seeded_inputs as si
+    frags = [COPY_KERNEL] + [w[1] for w in WORKLOADS]
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE", frags)
+    write = _counter_means(write_dir, "WRITE_SIZE", frags)
+    kept = int(np.count_nonzero(si.float32_normal(3, 1 << 28) > 0))
+    out = ["# HBM traffic per launch of each full-size workload (rocprofv3 counters)",
+           "# commands: " + PROFILE_CMDS["wl_fetch"],
+           "#           " + PROFILE_CMDS["wl_write"],
+           "# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by what the same counter reads for",
+           "# the 1 GiB copy probe; algorithmic bytes = one read of every input byte + one write of",
+           "# every output byte.",
+           "source_hash: " + kernel_source_hash(),
+           "compaction_kept: %d" % kept,
+           "# workload | read MB | write MB | total MB | algorithmic MB | traffic / algorithmic"]
+    if fetch[COPY_KERNEL] and write[COPY_KERNEL]:
+        copy_kib = (1 << 30) / 1024.0
+        fs, ws = copy_kib / fetch[COPY_KERNEL], copy_kib / write[COPY_KERNEL]
+        out.append("fetch_scale: %.4f  write_scale: %.4f" % (fs, ws))
+        for label, frag, n, alg in WORKLOADS:
+            if fetch[frag] is None or write[frag] is None:
+                out.append("%s | counters missing" % label)
+                continue
+            rd, wr, a = fetch[frag] * fs * 1024, write[frag] * ws * 1024, alg(n, kept)
+            out.append("%s | %.1f | %.1f | %.1f | %.1f | %.4f" % (label, rd / 1e6, wr / 1e6, (rd + wr) / 1e6,
+                                                                 a / 1e6, (rd + wr) / a))
+    else:
+        out.append("# copy probe counters missing")
+    with open(TRAFFIC_ALL_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(open(TRAFFIC_ALL_FILE).read())
+
+
+def workloads_once(dw, torch, si, steps):
+    """Each full-size workload `steps` times, one input resident at a time (for counter runs)."""
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(steps):
+        dw.scan_copy_probe(a, b)
+    del a, b
+    x = torch.from_numpy(si.float32_01(2, 1 << 28)).cuda()
+    y = torch.empty_like(x)
+    for _ in range(steps):
+        dw.scan_inclusive(x, "add", out=y)
+    del x, y
+    x = torch.from_numpy(si.int32_0_15(1, 1 << 28)).cuda()
+    y = torch.empty_like(x)
+    for _ in range(steps):
+        dw.scan_exclusive(x, "add", out=y)
+    for _ in range(steps):
+        dw.scan_inclusive(x, "max", out=y)
+    del x, y
+    x = torch.from_numpy(si.float32_normal(3, 1 << 28)).cuda()
+    y = torch.empty_like(x)
+    cnt = torch.zeros(1, dtype=torch.uint32, device="cuda")
+    for _ in range(steps):
+        dw.compact(x, out=y, count=cnt)
+    del x, y
+    ab = torch.from_numpy(si.affine_pairs(4, 1 << 26)).cuda()
+    yab = torch.empty_like(ab)
+    for _ in range(steps):
+        dw.scan_inclusive(ab, "affine", out=yab)
+    del ab, yab
+    xs = torch.from_numpy(si.int32_pm100(5, 1 << 27)).cuda()
+    hs = torch.from_numpy(si.segment_heads(5, 1 << 27, 1000.0)).cuda()
+    ys = torch.empty_like(xs)
+    for _ in range(steps):
+        dw.segmented_scan(xs, hs, "add", out=ys)
+    torch.cuda.synchronize()
+    err = dw.scan_get_device_error()
+    print(json.dumps({"workloads_once": steps, "device_error": err}), flush=True)
+
+
 def time_launches(fn, steps, warmup, torch):
     """Run fn() warmup times, then `steps` times between synchronisations.
 
@@ -218,7 +330,9 @@ def suite(dw, torch, si, out_path, steps):
 
     def rec(name, n, bytes_per_elem, fn):
         log("suite: " + name)
-        elapsed, ms = time_launches(fn, steps, 3, torch)
+        # first launches on freshly allocated buffers run slower (measured up to
+        # 15% for compaction): warm up longer than the default benchmark does
+        elapsed, ms = time_launches(fn, steps, 10, torch)
         t = statistics.median(ms) * 1e-3
         lines.append({"workload": name, "n": n, "median_us": round(t * 1e6, 2),
                       "gelem_s": round(n / t / 1e9, 2),
@@ -272,9 +386,16 @@ def main():
     ap.add_argument("--suite", metavar="FILE", help="also time every workload, JSON lines to FILE")
     ap.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output and exit")
+    ap.add_argument("--workloads-once", type=int, metavar="K",
+                    help="run every full-size workload K times (for counter runs) and exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the per-workload traffic summary under profiles/ and exit")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(*args.summarize_rocprof)
+        return
+    if args.summarize_traffic:
+        summarize_workload_traffic(*args.summarize_traffic)
         return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (--gpus %d requested); "
@@ -289,6 +410,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dw.lib()
+    if args.workloads_once:
+        workloads_once(dw, torch, si, args.workloads_once)
+        return
     log("generating input")
     x_host = si.float32_01(2, N_MAIN)
     x = torch.from_numpy(x_host).cuda()

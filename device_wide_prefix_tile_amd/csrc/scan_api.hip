@@ -456,11 +456,14 @@ uint32_t scan_set_spin_limit(uint32_t polls)
 
 // ------------------------------------------------------------ copy probe
 namespace {
+// One 16-byte vector per lane with streaming hints: the fastest plain copy
+// measured on MI355X (about 6.5 TB/s for 1 GiB each way), i.e. the practical
+// ceiling of a one-read-one-write kernel.
 __global__ __launch_bounds__(256) void copy_probe_kernel(const u32x4* __restrict__ in, u32x4* __restrict__ out,
                                                           size_t nvec)
 {
     for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < nvec; i += (size_t)gridDim.x * 256)
-        out[i] = in[i];
+        __builtin_nontemporal_store(__builtin_nontemporal_load(in + i), out + i);
 }
 }  // namespace
 
