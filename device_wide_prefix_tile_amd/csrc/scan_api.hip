@@ -205,15 +205,16 @@ scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(
         return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
     }
     Workspace* ws = nullptr;
-    // per tile: its status, and a second word set for group statuses (one-tile-per-workgroup
-    // kernel) or the resolver's published prefixes (persistent kernel)
-    const scan_status_t st = acquire_workspace(c.stream, (size_t)(2 * tiles) * kWords, &ws);
+    // per tile: its status (AGG_PAD entries apart), then a second array for group statuses
+    // (one-tile-per-workgroup kernel) or the resolver's published prefixes (persistent
+    // kernel, PREFIX_PAD entries apart: one prefix per 128-byte line)
+    const scan_status_t st = acquire_workspace(c.stream, (size_t)tiles * kWords * (DWPT_AGG_PAD + DWPT_PREFIX_PAD), &ws);
     if (st != SCAN_OK) return st;
     p.tile_ctr = ws->ctr;
     p.ctr_base = ws->ctr_base;
     p.pipe_ctr = ws->pipe_ctr;
     p.lb.status = ws->status;
-    p.lb.groups = ws->status + (size_t)tiles * kWords;
+    p.lb.groups = ws->status + (size_t)tiles * kWords * DWPT_AGG_PAD;
     p.lb.err = ws->err;
     p.lb.epoch = ws->epoch;
     p.lb.spin_limit = g_spin_limit;

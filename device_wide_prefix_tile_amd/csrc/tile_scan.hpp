@@ -667,7 +667,7 @@ __device__ __forceinline__ void hand_over_slot(const ScanParams& p, uint32_t til
     V total = Op::identity();
 #pragma unroll
     for (int q = 0; q < ND; ++q) total = Op::combine(total, slot->wave_total[q]);
-    if (lane == 0) publish<Op>(p.lb, p.lb.status, tile, Op::to_carry(total), kStateAggregate);
+    if (lane == 0) publish<Op>(p.lb, p.lb.status, (uint64_t)tile * DWPT_AGG_PAD, Op::to_carry(total), kStateAggregate);
 }
 
 __device__ __forceinline__ void wait_seq(uint32_t* seq, uint32_t want)
