@@ -78,13 +78,13 @@ struct Workspace {
     size_t status_words = 0;  // capacity in 64-bit status words
     uint64_t* status = nullptr;
     uint32_t* ctr = nullptr;
-    uint32_t* pipe_ctr = nullptr;  // persistent kernel's self-resetting counters (3 words)
+    uint32_t* pipe_ctr = nullptr;  // persistent kernel's self-resetting counters (one 128-byte line each)
     uint32_t* err = nullptr;
     uint32_t ctr_base = 0;
     uint32_t epoch = 0;
 };
 std::map<std::pair<int, void*>, Workspace> g_ws;
-constexpr size_t kHeaderBytes = 256;  // err word, tile counter, persistent-kernel counters, padding
+constexpr size_t kHeaderBytes = 512;  // line 0: err word, tile counter; lines 1-3: persistent-kernel counters
 
 __global__ void zero_words_kernel(uint64_t* p, size_t nwords)
 {
@@ -132,7 +132,7 @@ scan_status_t acquire_workspace(hipStream_t s, size_t words, Workspace** out)
         ws.status_words = cap;
         ws.err = static_cast<uint32_t*>(mem);
         ws.ctr = static_cast<uint32_t*>(mem) + 1;
-        ws.pipe_ctr = static_cast<uint32_t*>(mem) + 2;
+        ws.pipe_ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + 128);
         ws.status = reinterpret_cast<uint64_t*>(static_cast<char*>(mem) + kHeaderBytes);
         ws.ctr_base = 0;
         ws.epoch = 0;

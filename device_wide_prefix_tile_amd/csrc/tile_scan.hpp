@@ -55,7 +55,7 @@ struct ScanParams {
     uint32_t num_tiles;
     uint32_t ctr_base;     // counter value when this launch started
     uint32_t* tile_ctr;
-    uint32_t* pipe_ctr;    // persistent kernel: [0] next tile, [1] roles taken, [2] workgroups retired
+    uint32_t* pipe_ctr;    // persistent kernel: next tile, roles taken, workgroups retired (kCtrStride apart)
     Lookback lb;
     int vec_ok;            // 16-byte aligned pointers: vector loads/stores
 };
@@ -531,11 +531,12 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //    the same status words; measured, those reads queued behind the tile
 //    data on every CU.)
 //  * Tiles.  The other workgroups take tile numbers from a counter, in the
-//    order they ask.  A tile therefore only ever waits on tiles already
-//    taken by running workgroups, and the resolver has started before any
-//    tile is taken, so no co-residency guarantee is needed (a cooperative
-//    launch was measured to cost ~17 us per call).  The last workgroup to
-//    retire resets the counters for the next launch on the stream.
+//    order they ask (the scans first take a batch; see take_first_batch).
+//    A tile therefore only ever waits on tiles already taken by running
+//    workgroups, and the resolver has started before any tile is taken, so
+//    no co-residency guarantee is needed (a cooperative launch was measured
+//    to cost ~17 us per call).  The last workgroup to retire resets the
+//    counters for the next launch on the stream.
 //  * Pipeline.  Every data wavefront keeps WAIT + 1 of its tiles in flight
 //    as raw elements in registers: while it waits for the prefix of its
 //    oldest tile, the totals of the next WAIT - 1 are already published and
@@ -678,6 +679,12 @@ __device__ __forceinline__ void wait_seq(uint32_t* seq, uint32_t want)
 
 
 
+// The persistent kernel's counters, each on its own 128-byte line so that
+// their atomics do not queue behind one another.
+enum : int { kCtrTiles = 0, kCtrRoles = 1, kCtrRetired = 2, kCtrCount = 3 };
+constexpr int kCtrStride = 32;  // words
+__device__ __forceinline__ uint32_t* pipe_counter(const ScanParams& p, int q) { return p.pipe_ctr + q * kCtrStride; }
+
 // Tile numbers of a data workgroup, in the order it processes them.
 struct TileIdRing {
     uint32_t id[kPipeSlots];
@@ -703,7 +710,7 @@ __device__ __forceinline__ uint32_t start_workgroup(const ScanParams& p, Slot* s
                                                     uint32_t* s_role)
 {
     if (threadIdx.x == 0)
-        *s_role = __hip_atomic_fetch_add(&p.pipe_ctr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_role = __hip_atomic_fetch_add(pipe_counter(p, kCtrRoles), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x < kPipeSlots) {
         slots[threadIdx.x].arrived = 0u;
         slots[threadIdx.x].prefix_seq = 0u;
@@ -717,10 +724,10 @@ __device__ __forceinline__ uint32_t start_workgroup(const ScanParams& p, Slot* s
 // workgroup of the launch resets them for the next one.
 __device__ __forceinline__ void retire_workgroup(const ScanParams& p)
 {
-    const uint32_t d = __hip_atomic_fetch_add(&p.pipe_ctr[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t d = __hip_atomic_fetch_add(pipe_counter(p, kCtrRetired), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == gridDim.x - 1) {
 #pragma unroll
-        for (int q = 0; q < 3; ++q) __hip_atomic_store(&p.pipe_ctr[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int q = 0; q < kCtrCount; ++q) __hip_atomic_store(pipe_counter(p, q), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -740,13 +747,35 @@ __device__ __forceinline__ bool take_first_ids(const ScanParams& p, TileIdRing* 
         uint32_t id = p.num_tiles;
         if (!exhausted) {
             if (lane_id() == 0)
-                id = __hip_atomic_fetch_add(&p.pipe_ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                id = __hip_atomic_fetch_add(pipe_counter(p, kCtrTiles), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             id = (uint32_t)__builtin_amdgcn_readfirstlane((int)id);
             exhausted = id >= p.num_tiles;
         }
         if (lane_id() == 0) put_id(ids, (uint32_t)q, id);
     }
     return exhausted;
+}
+
+// The scan kernels' start: the first NT numbers as one consecutive batch,
+// with a single atomic (every lower number is then held by a running
+// workgroup, as with single numbers).  The workgroup publishes the totals of
+// the whole batch before it waits for any prefix, so the batch does not chain
+// the workgroups one after another.  Taken one round trip apart instead, the
+// 255 workgroups' first numbers queue on the counter and the first loads go
+// out ~22 us after the launch (measured; the scans gain ~3%, compaction, which
+// keeps single numbers, does not).  Returns true once a number past the last
+// tile came back.
+template <int NT>
+__device__ __forceinline__ bool take_first_batch(const ScanParams& p, TileIdRing* ids)
+{
+    uint32_t b = p.num_tiles;
+    if (lane_id() == 0)
+        b = __hip_atomic_fetch_add(pipe_counter(p, kCtrTiles), (uint32_t)NT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    b = (uint32_t)__builtin_amdgcn_readfirstlane((int)b);
+    if (lane_id() == 0)
+#pragma unroll
+        for (int q = 0; q < NT; ++q) put_id(ids, (uint32_t)q, (uint64_t)b + q < p.num_tiles ? b + q : p.num_tiles);
+    return (uint64_t)b + NT >= p.num_tiles;
 }
 
 // Wavefront 0 asks for a tile number one iteration before it is needed: the
@@ -756,7 +785,7 @@ __device__ __forceinline__ uint32_t ask_id(const ScanParams& p, bool exhausted)
 {
     uint32_t id = p.num_tiles;
     if (!exhausted && lane_id() == 0)
-        id = __hip_atomic_fetch_add(&p.pipe_ctr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        id = __hip_atomic_fetch_add(pipe_counter(p, kCtrTiles), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return id;  // valid in lane 0
 }
 
@@ -823,7 +852,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
         return;
     }
     bool exhausted = false;
-    if (w == 0) exhausted = take_first_ids<kPipeTiles>(p, &s_ids);
+    if (w == 0) exhausted = take_first_batch<kPipeTiles>(p, &s_ids);
     if (w == ND) {
         fetch_prefixes<Op>(p, &s_ids, s_slot);
         return;
@@ -836,11 +865,12 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     WaveTile<G> t[kPipeTiles];
 #pragma unroll
     for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id(&s_ids, q), w);
+    // the first batch: every tile loaded and its total published up front
 #pragma unroll
-    for (int q = 0; q < kPipeTiles - 1; ++q)
+    for (int q = 0; q < kPipeTiles; ++q)
         if (t[q].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[q].base, t[q].vec, lane, e[q], h[q]);
 #pragma unroll
-    for (int q = 0; q < kPipeWait - 1; ++q)
+    for (int q = 0; q < kPipeTiles; ++q)
         if (t[q].tile < p.num_tiles)
             hand_over_slot<Op, Slot, ND>(p, t[q].tile, q, w, lane, reduce_wave<Op, R, VEC>(t[q].base, lane, e[q], h[q]),
                                          &s_slot[q % kPipeSlots]);
@@ -850,8 +880,9 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
         // iteration's loads, so waiting for it never waits for them
         uint32_t next_id = p.num_tiles;
         if (w == 0) next_id = ask_id(p, exhausted);
-        if (t[NEW].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], h[NEW]);
-        if (t[PUB].tile < p.num_tiles)
+        // stages still holding the first batch were loaded and published above
+        if (k >= 1 && t[NEW].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], h[NEW]);
+        if (k >= 2 && t[PUB].tile < p.num_tiles)
             hand_over_slot<Op, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane,
                                          reduce_wave<Op, R, VEC>(t[PUB].base, lane, e[PUB], h[PUB]),
                                          &s_slot[(k + PUB) % kPipeSlots]);
