@@ -68,9 +68,9 @@ int g_multi_mode = 0;                 // 0: by size; 1: one tile per workgroup; 
 // In the automatic mode the persistent kernel takes inputs of at least this
 // many tiles per resident data workgroup; below, too few tiles per workgroup
 // are left to fill its pipeline and one workgroup per tile is faster
-// (measured on int32 max scans: 42 against 46 us at 2^24 elements, 134
-// against 112 us at 2^26).
-constexpr uint64_t kPersistentTilesPerWorkgroup = 8;
+// (measured on int32 max scans: 26 against 30 us at 2^23 elements, 41
+// against 36 us at 2^24).
+constexpr uint64_t kPersistentTilesPerWorkgroup = 3;
 
 // ------------------------------------------------------------ workspaces
 struct Workspace {

@@ -145,8 +145,8 @@ scan_status_t scan_release_workspace(void);
  *   small-n size.  2 runs the persistent pipelined kernel (one launch of as
  *   many workgroups as fit on the GPU, each taking tile numbers from a
  *   counter until the input is done); 1 runs one workgroup per tile; 0 (the
- *   default) takes the persistent kernel from 8 tiles per resident
- *   workgroup up (about 2^25 four-byte elements on 256 compute units) and
+ *   default) takes the persistent kernel from 3 tiles per resident
+ *   workgroup up (about 1.2e7 four-byte elements on 256 compute units) and
  *   one workgroup per tile below.  Other values select 0.
  * scan_set_spin_limit: number of look-back polls after which a waiting tile
  *   gives up, records SCAN_ERR_TIMEOUT (see scan_get_device_error) and

@@ -57,7 +57,7 @@ class Path:
 
 def paths_for(n):
     # 'auto' picks 'fallback' at these sizes (the persistent kernel starts at
-    # about 2^25 elements); the full-size configurations cover 'auto' there
+    # about 1.2e7 elements); the full-size configurations cover 'auto' there
     return ["multi", "single", "fallback"] if n <= 3 * TILE + 17 else ["auto", "multi"]
 
 
