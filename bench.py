@@ -299,6 +299,20 @@ def time_launches(fn, steps, warmup, torch):
     return elapsed, [a.elapsed_time(b) for a, b in evs]
 
 
+def host_cpu():
+    """CPU model and logical CPU count of the host the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return "%s, %d logical CPUs (oracle uses 1)" % (model, os.cpu_count() or 0)
+
+
 def cpu_baseline(x):
     import oracle
     sample = x[: 1 << 26]
@@ -310,6 +324,7 @@ def cpu_baseline(x):
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     return {"value": round(sample.shape[0] / med / 1e9, 4), "unit": "Gelem/s", "cores": 1, "kind": "oracle",
+            "host": host_cpu(),
             "sample": "first 2^26 of the 2^28 float32 inputs, sequential double-accumulated inclusive add, "
                       "median of %d runs" % len(times)}, (y, s)
 
@@ -327,6 +342,7 @@ def suite(dw, torch, si, out_path, steps):
     """Time each workload at its full size; one JSON line per workload."""
     import numpy as np
     lines = []
+    copy_gbps = copy_probe(dw, torch)
 
     def rec(name, n, bytes_per_elem, fn):
         log("suite: " + name)
@@ -336,7 +352,8 @@ def suite(dw, torch, si, out_path, steps):
         lines.append({"workload": name, "n": n, "median_us": round(t * 1e6, 2),
                       "gelem_s": round(n / t / 1e9, 2),
                       "effective_GBps": round(n * bytes_per_elem / t / 1e9, 1),
-                      "pct_of_peak": round(100 * n * bytes_per_elem / t / 1e9 / PEAK_GBPS, 1)})
+                      "pct_of_peak": round(100 * n * bytes_per_elem / t / 1e9 / PEAK_GBPS, 1),
+                      "pct_of_copy": round(100 * n * bytes_per_elem / t / 1e9 / copy_gbps, 1)})
 
     x = torch.from_numpy(si.int32_0_15(1, 1 << 20)).cuda()
     y = torch.empty_like(x)
@@ -445,6 +462,8 @@ def main():
     }
     log("copy probe")
     result["copy_probe_GBps"] = copy_probe(dw, torch)
+    # the kernel's rate against what a plain one-read-one-write copy reaches here
+    result["roofline"]["frac_of_copy"] = round(achieved / result["copy_probe_GBps"], 4)
 
     # output check on the oracle's sample, and the last element against a double sum
     y_host = y.cpu().numpy()
