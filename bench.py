@@ -386,7 +386,19 @@ def suite(dw, torch, si, out_path, steps):
         xm = torch.from_numpy(si.int32_full(6, n)).cuda()
         ym = torch.empty_like(xm)
         rec("int32 inclusive max 4^%d" % k, n, 8, lambda: dw.scan_inclusive(xm, "max", out=ym))
+        if 9 <= k <= 14:
+            # the reduce-then-scan alternative at the same size (12 B/element of traffic; the
+            # figure below still counts the algorithmic 8)
+            old = dw.scan_set_multi_tile_mode(3)
+            rec("int32 inclusive max 4^%d, reduce-then-scan" % k, n, 8, lambda: dw.scan_inclusive(xm, "max", out=ym))
+            dw.scan_set_multi_tile_mode(old)
         del xm, ym
+    xf = torch.from_numpy(si.float32_01(2, 1 << 28)).cuda()
+    yf = torch.empty_like(xf)
+    old = dw.scan_set_multi_tile_mode(3)
+    rec("float32 inclusive add 2^28, reduce-then-scan", 1 << 28, 8, lambda: dw.scan_inclusive(xf, "add", out=yf))
+    dw.scan_set_multi_tile_mode(old)
+    del xf, yf
     torch.cuda.empty_cache()
     with open(out_path, "w") as f:
         for l in lines:

@@ -163,7 +163,8 @@ def scan_set_small_n_max(n_max: int) -> int:
 
 
 def scan_set_multi_tile_mode(mode: int) -> int:
-    """0: by size (default); 1: one workgroup per tile; 2: persistent pipelined kernel."""
+    """0: by size (default); 1: one workgroup per tile; 2: persistent pipelined kernel;
+    3: reduce-then-scan (three launches)."""
     return int(lib().scan_set_multi_tile_mode(int(mode)))
 
 

@@ -1,6 +1,7 @@
 // scan_api.hip -- C ABI of libdwpt_scan.so: argument checks, the
 // (op, dtype, variant) dispatch table, workspace management and launches.
-// The kernels are in tile_scan.hpp; the ABI is documented in dwpt_scan.h.
+// The kernels are in tile_scan.hpp and reduce_then_scan.hpp; the ABI is
+// documented in dwpt_scan.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -10,6 +11,7 @@
 #include <utility>
 
 #include "dwpt_scan.h"
+#include "reduce_then_scan.hpp"
 #include "tile_scan.hpp"
 
 using namespace dwpt;
@@ -64,7 +66,7 @@ struct Shape {
 std::mutex g_mu;
 size_t g_small_n_max = 4096;          // n at or below: single-workgroup path
 uint32_t g_spin_limit = 1u << 18;     // look-back polls before giving up (a fraction of a second)
-int g_multi_mode = 0;                 // 0: by size; 1: one tile per workgroup; 2: persistent kernel
+int g_multi_mode = 0;  // 0: by size; 1: one tile per workgroup; 2: persistent kernel; 3: reduce-then-scan
 // In the automatic mode the persistent kernel takes inputs of at least this
 // many tiles per resident data workgroup; below, too few tiles per workgroup
 // are left to fill its pipeline and one workgroup per tile is faster
@@ -82,6 +84,11 @@ struct Workspace {
     uint32_t* err = nullptr;
     uint32_t ctr_base = 0;
     uint32_t epoch = 0;
+    // reduce-then-scan's plain carries, in memory of their own: status words
+    // must only ever hold tagged entries, or a stale carry could pass for a
+    // current one
+    void* rts = nullptr;
+    size_t rts_bytes = 0;
 };
 std::map<std::pair<int, void*>, Workspace> g_ws;
 constexpr size_t kHeaderBytes = 512;  // line 0: err word, tile counter; lines 1-3: persistent-kernel counters
@@ -116,7 +123,8 @@ scan_status_t acquire_workspace(hipStream_t s, size_t words, Workspace** out)
         if (ws.mem) {
             if (hipStreamSynchronize(s) != hipSuccess) return SCAN_ERR_HIP;
             (void)hipFree(ws.mem);
-            ws = Workspace();
+            ws.mem = nullptr;
+            ws.status_words = 0;
         }
         void* mem = nullptr;
         const size_t bytes = kHeaderBytes + cap * 8;
@@ -144,6 +152,28 @@ scan_status_t acquire_workspace(hipStream_t s, size_t words, Workspace** out)
         ws.epoch = 1;
     }
     *out = &ws;
+    return SCAN_OK;
+}
+
+// Called with g_mu held, after acquire_workspace: at least `bytes` of
+// reduce-then-scan memory in the workspace.
+scan_status_t acquire_rts(hipStream_t s, Workspace& ws, size_t bytes)
+{
+    if (ws.rts_bytes >= bytes) return SCAN_OK;
+    size_t cap = ws.rts_bytes ? ws.rts_bytes * 2 : (size_t)1 << 16;
+    while (cap < bytes) cap *= 2;
+    if (ws.rts) {
+        if (hipStreamSynchronize(s) != hipSuccess) return SCAN_ERR_HIP;
+        (void)hipFree(ws.rts);
+        ws.rts = nullptr;
+        ws.rts_bytes = 0;
+    }
+    if (hipMalloc(&ws.rts, cap) != hipSuccess) {
+        (void)hipGetLastError();
+        ws.rts = nullptr;
+        return SCAN_ERR_NOMEM;
+    }
+    ws.rts_bytes = cap;
     return SCAN_OK;
 }
 
@@ -179,14 +209,24 @@ int resident_capacity(const void* f, int block)
     return cap;
 }
 
+// The three kernels of the reduce-then-scan variant, for carries of type C.
+template <class C>
+struct RtsKernels {
+    void (*reduce)(ScanParams, C*);
+    void (*carries)(const C*, C*, uint32_t, C*);
+    void (*seeded)(ScanParams, const C*);
+};
+
 // Fills params and launches the single-workgroup kernel (small n), else the
 // persistent pipelined kernel (as many workgroups as fit, plus none beyond
-// one per tile and the resolver) or the one-tile-per-workgroup kernel, as
-// the mode and the number of tiles select.  TILE is the tile size and kWords
-// the status words per tile.
-template <int BLOCK, int TILE, int kWords>
-scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(ScanParams), const Call& c,
-                     bool vec_ok)
+// one per tile and the resolver), the one-tile-per-workgroup kernel or the
+// three reduce-then-scan kernels, as the mode and the number of tiles
+// select.  TILE is the tile size and kWords the status words per tile;
+// `grand` receives the fold of all tiles in reduce-then-scan (compaction's
+// count), or nullptr.
+template <int BLOCK, int TILE, int kWords, class C>
+scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(ScanParams),
+                     const RtsKernels<C>& rts, C* grand, const Call& c, bool vec_ok)
 {
     ScanParams p{};
     p.in = c.in;
@@ -210,6 +250,19 @@ scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(
     // kernel, PREFIX_PAD entries apart: one prefix per 128-byte line)
     const scan_status_t st = acquire_workspace(c.stream, (size_t)tiles * kWords * (DWPT_AGG_PAD + DWPT_PREFIX_PAD), &ws);
     if (st != SCAN_OK) return st;
+    if (g_multi_mode == 3) {
+        // 2T + 1 plain carries: the tile totals, the grand total, the prefixes
+        const scan_status_t sr = acquire_rts(c.stream, *ws, (2 * (size_t)tiles + 1) * sizeof(C));
+        if (sr != SCAN_OK) return sr;
+        C* totals = static_cast<C*>(ws->rts);
+        C* excl = totals + tiles + 1;
+        const uint32_t T = (uint32_t)tiles;
+        hipLaunchKernelGGL(rts.reduce, dim3(T), dim3(BLOCK), 0, c.stream, p, totals);
+        hipLaunchKernelGGL(rts.carries, dim3(1), dim3(BLOCK), 0, c.stream, (const C*)totals, excl, T,
+                           grand ? grand : totals + tiles);
+        hipLaunchKernelGGL(rts.seeded, dim3(T), dim3(BLOCK), 0, c.stream, p, (const C*)excl);
+        return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+    }
     p.tile_ctr = ws->ctr;
     p.ctr_base = ws->ctr_base;
     p.pipe_ctr = ws->pipe_ctr;
@@ -238,18 +291,24 @@ template <class Op, bool EXCL>
 scan_status_t run_scan(const Call& c, bool vec_ok)
 {
     using S = Shape<Op>;
-    return launch<S::BLOCK, S::TILE, Op::kWords>(tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, true>,
-                                                 tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, false>,
-                                                 tile_scan_persistent<Op, EXCL, S::BLOCK, S::ITEMS, S::WAIT>, c, vec_ok);
+    using C = typename Op::carry_t;
+    const RtsKernels<C> rts{tile_reduce_kernel<Op, S::BLOCK, S::ITEMS>, carry_scan_kernel<Op, S::BLOCK>,
+                            tile_scan_seeded_kernel<Op, EXCL, S::BLOCK, S::ITEMS>};
+    return launch<S::BLOCK, S::TILE, Op::kWords, C>(tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, true>,
+                                                    tile_scan_kernel<Op, EXCL, S::BLOCK, S::ITEMS, false>,
+                                                    tile_scan_persistent<Op, EXCL, S::BLOCK, S::ITEMS, S::WAIT>, rts,
+                                                    (C*)nullptr, c, vec_ok);
 }
 
 template <typename T>
 scan_status_t run_compact(const Call& c, bool vec_ok)
 {
     constexpr int BLOCK = DWPT_BLOCK, ITEMS = DWPT_ITEMS_COMPACT;
-    return launch<BLOCK, Geometry<OpAdd<uint32_t>, BLOCK, ITEMS>::TILE, 1>(
+    const RtsKernels<uint32_t> rts{tile_count_kernel<T, BLOCK, ITEMS>, carry_scan_kernel<OpAdd<uint32_t>, BLOCK>,
+                                   compact_seeded_kernel<T, BLOCK, ITEMS>};
+    return launch<BLOCK, Geometry<OpAdd<uint32_t>, BLOCK, ITEMS>::TILE, 1, uint32_t>(
         compact_kernel<T, BLOCK, ITEMS, true>, compact_kernel<T, BLOCK, ITEMS, false>,
-        compact_persistent<T, BLOCK, ITEMS, DWPT_WAIT_COMPACT>, c, vec_ok);
+        compact_persistent<T, BLOCK, ITEMS, DWPT_WAIT_COMPACT>, rts, c.count, c, vec_ok);
 }
 
 typedef scan_status_t (*Runner)(const Call&, bool);
@@ -419,10 +478,11 @@ scan_status_t scan_release_workspace(void)
     (void)hipGetDevice(&cur);
     scan_status_t st = SCAN_OK;
     for (auto& kv : g_ws) {
-        if (!kv.second.mem) continue;
-        if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess ||
-            hipFree(kv.second.mem) != hipSuccess)
+        if (!kv.second.mem && !kv.second.rts) continue;
+        if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
             st = SCAN_ERR_HIP;
+        if (kv.second.mem && hipFree(kv.second.mem) != hipSuccess) st = SCAN_ERR_HIP;
+        if (kv.second.rts && hipFree(kv.second.rts) != hipSuccess) st = SCAN_ERR_HIP;
     }
     g_ws.clear();
     (void)hipSetDevice(cur);
@@ -441,7 +501,7 @@ int scan_set_multi_tile_mode(int mode)
 {
     std::lock_guard<std::mutex> lock(g_mu);
     const int old = g_multi_mode;
-    g_multi_mode = (mode == 1 || mode == 2) ? mode : 0;
+    g_multi_mode = (mode >= 1 && mode <= 3) ? mode : 0;
     return old;
 }
 

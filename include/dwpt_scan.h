@@ -147,7 +147,11 @@ scan_status_t scan_release_workspace(void);
  *   counter until the input is done); 1 runs one workgroup per tile; 0 (the
  *   default) takes the persistent kernel from 3 tiles per resident
  *   workgroup up (about 1.2e7 four-byte elements on 256 compute units) and
- *   one workgroup per tile below.  Other values select 0.
+ *   one workgroup per tile below.  3 runs reduce-then-scan: three launches
+ *   (tile totals, one workgroup scanning them, every tile scanned again
+ *   from its prefix), which reads the input twice but never makes a tile
+ *   wait for another, and fixes the association of float sums by n alone.
+ *   Other values select 0.
  * scan_set_spin_limit: number of look-back polls after which a waiting tile
  *   gives up, records SCAN_ERR_TIMEOUT (see scan_get_device_error) and
  *   finishes with a wrong prefix instead of waiting forever.  Default 2^18.

@@ -85,6 +85,7 @@ def test_tuning_knobs_round_trip():
     old = binding.scan_set_spin_limit(77)
     assert binding.scan_set_spin_limit(old) == 77
     old = binding.scan_set_multi_tile_mode(2)
-    assert binding.scan_set_multi_tile_mode(1) == 2
+    assert binding.scan_set_multi_tile_mode(3) == 2
+    assert binding.scan_set_multi_tile_mode(1) == 3
     assert binding.scan_set_multi_tile_mode(7) == 1
     assert binding.scan_set_multi_tile_mode(old) == 0

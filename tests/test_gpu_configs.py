@@ -33,7 +33,7 @@ def fresh():
 
 
 class Mode:
-    """Force a multi-tile kernel: 1 one workgroup per tile, 2 persistent; 0 by size."""
+    """Force a multi-tile kernel: 1 one workgroup per tile, 2 persistent, 3 reduce-then-scan; 0 by size."""
 
     def __init__(self, mode):
         self.mode = mode
@@ -50,7 +50,7 @@ def test_config1_int32_exclusive_add_2p20():
     x = si.int32_0_15(1, n)
     xd = to_dev(x)
     ref = oracle.scan("add", x, exclusive=True)
-    for mode in (0, 1, 2):
+    for mode in (0, 1, 2, 3):
         with Mode(mode):
             y = from_dev(dw.scan_exclusive(xd, "add"))
         assert_equal(y, ref, "config1 mode=%d" % mode)
@@ -63,38 +63,53 @@ def test_config2_f32_inclusive_add_2p28():
     n = 1 << 28
     x = si.float32_01(2, n)
     xd = to_dev(x)
-    y = from_dev(dw.scan_inclusive(xd, "add"))
+    ys = {}
+    for mode in (0, 3):  # the benchmarked kernel, and reduce-then-scan
+        with Mode(mode):
+            ys[mode] = from_dev(dw.scan_inclusive(xd, "add"))
     del xd
     ref, s = oracle.scan("add", x)
-    worst = assert_f32_close(y, ref, s, "config2")
-    print("config2 worst error/tolerance = %.4f" % worst)
+    for mode, y in ys.items():
+        worst = assert_f32_close(y, ref, s, "config2 mode=%d" % mode)
+        print("config2 mode=%d worst error/tolerance = %.4f" % (mode, worst))
     assert dw.scan_get_device_error() == 0
 
 
 def test_config3_compact_2p28():
     n = 1 << 28
     x = si.float32_normal(3, n)
-    out, cnt = dw.compact(to_dev(x))
-    out, cnt = from_dev(out), int(from_dev(cnt)[0])
+    xd = to_dev(x)
     ref, rc, _ = oracle.compact(x)
-    assert cnt == rc
-    assert_equal(out[:cnt], ref, "config3")
+    for mode in (0, 3):
+        with Mode(mode):
+            out, cnt = dw.compact(xd)
+        out, cnt = from_dev(out), int(from_dev(cnt)[0])
+        assert cnt == rc, "config3 mode=%d" % mode
+        assert_equal(out[:cnt], ref, "config3 mode=%d" % mode)
 
 
 @pytest.mark.parametrize("odd", [False, True], ids=["any_a", "odd_a"])
 def test_config4_affine_2p26(odd):
     n = 1 << 26
     ab = si.affine_pairs(40 if odd else 4, n, odd_a=odd)
-    y = from_dev(dw.scan_inclusive(to_dev(ab), "affine"))
-    assert_equal(y, oracle.scan_affine(ab), "config4 odd=%s" % odd)
+    abd = to_dev(ab)
+    ref = oracle.scan_affine(ab)
+    for mode in (0, 3):
+        with Mode(mode):
+            y = from_dev(dw.scan_inclusive(abd, "affine"))
+        assert_equal(y, ref, "config4 odd=%s mode=%d" % (odd, mode))
 
 
 def test_config5_segmented_add_2p27():
     n = 1 << 27
     x = si.int32_pm100(5, n)
     h = si.segment_heads(5, n, 1000.0)
-    y = from_dev(dw.segmented_scan(to_dev(x), to_dev(h), "add"))
-    assert_equal(y, oracle.segmented_scan("add", x, h), "config5 segmented")
+    xd, hd = to_dev(x), to_dev(h)
+    ref = oracle.segmented_scan("add", x, h)
+    for mode in (0, 3):
+        with Mode(mode):
+            y = from_dev(dw.segmented_scan(xd, hd, "add"))
+        assert_equal(y, ref, "config5 segmented mode=%d" % mode)
 
 
 @pytest.mark.parametrize("k", range(5, 16))
@@ -103,8 +118,8 @@ def test_config5_max_sweep(k):
     x = si.int32_full(6, n)
     xd = to_dev(x)
     ref = oracle.scan("max", x)
-    # the size-selected kernel, and below 2^30 both multi-tile kernels forced
-    for mode in (0, 1, 2) if k < 15 else (0,):
+    # the size-selected kernel, and below 2^30 every multi-tile path forced
+    for mode in (0, 1, 2, 3) if k < 15 else (0,):
         with Mode(mode):
             y = from_dev(dw.scan_inclusive(xd, "max"))
         assert_equal(y, ref, "config5 max sweep n=4^%d mode=%d" % (k, mode))

@@ -39,15 +39,16 @@ def gpu():
 class Path:
     """Select a kernel path: 'single' (one workgroup walks all tiles), 'multi'
     (the persistent multi-tile kernel, forced even for small n), 'fallback'
-    (one workgroup per tile, forced even for small n) or 'auto' (the default)."""
+    (one workgroup per tile, forced even for small n), 'rts' (reduce-then-scan,
+    forced even for small n) or 'auto' (the default)."""
 
     def __init__(self, which):
         self.which = which
 
     def __enter__(self):
-        lim = {"single": 1 << 40, "multi": 0, "fallback": 0}.get(self.which)
+        lim = {"single": 1 << 40, "multi": 0, "fallback": 0, "rts": 0}.get(self.which)
         self.old = dw.scan_set_small_n_max(lim) if lim is not None else None
-        self.old_mode = dw.scan_set_multi_tile_mode({"fallback": 1, "multi": 2}.get(self.which, 0))
+        self.old_mode = dw.scan_set_multi_tile_mode({"fallback": 1, "multi": 2, "rts": 3}.get(self.which, 0))
 
     def __exit__(self, *a):
         if self.old is not None:
@@ -58,7 +59,7 @@ class Path:
 def paths_for(n):
     # 'auto' picks 'fallback' at these sizes (the persistent kernel starts at
     # about 1.2e7 elements); the full-size configurations cover 'auto' there
-    return ["multi", "single", "fallback"] if n <= 3 * TILE + 17 else ["auto", "multi"]
+    return ["multi", "single", "fallback", "rts"] if n <= 3 * TILE + 17 else ["auto", "multi", "rts"]
 
 
 def values(dt, n, seed):
@@ -293,6 +294,42 @@ def test_repeat_runs_bit_exact():
         if rep % 4 == 0:
             assert_equal(from_dev(dw.scan_inclusive(abd, "affine")), ref_ab, "repeat %d affine" % rep)
     assert dw.scan_get_device_error() == 0
+
+
+def test_modes_alternate_on_one_stream():
+    # Every kernel path on one stream, one after another, several rounds.
+    # One 1 per tile makes the exclusive carries between tiles small integers
+    # (t for tile t): the values that would pass for valid status words if
+    # reduce-then-scan's plain carries ever shared memory with them.
+    n = 300 * TILE + 77
+    x = (np.arange(n) % TILE == 0).astype(np.int32)
+    xd = to_dev(x)
+    ref = oracle.scan("add", x, exclusive=True)
+    for rnd in range(4):
+        for path in ("rts", "multi", "fallback", "rts", "multi"):
+            with Path(path):
+                y = from_dev(dw.scan_exclusive(xd, "add"))
+            assert_equal(y, ref, "round %d path=%s" % (rnd, path))
+    assert dw.scan_get_device_error() == 0
+
+
+def test_rts_float_sum_is_reproducible():
+    # Reduce-then-scan fixes the association of a float sum by n alone (tile
+    # totals, then one workgroup folding them in order): repeated calls, also
+    # on another stream, give identical bits.
+    n = 5 * TILE + 12345
+    x = si.float32_sym(94, n)
+    xd = to_dev(x)
+    ref, s = oracle.scan("add", x)
+    with Path("rts"):
+        first = from_dev(dw.scan_inclusive(xd, "add"))
+        assert_f32_close(first, ref, s, "rts float add")
+        side = torch.cuda.Stream()
+        for k in range(5):
+            with torch.cuda.stream(side if k % 2 else torch.cuda.current_stream()):
+                y = dw.scan_inclusive(xd, "add")
+            torch.cuda.synchronize()
+            assert np.array_equal(from_dev(y).view(np.uint32), first.view(np.uint32)), "run %d differs" % k
 
 
 def test_bounded_waits_report_timeout_and_recover():
