@@ -62,6 +62,8 @@ def _load():
         "oracle_scan_f32_add": [I, P, P, P, L],
         "oracle_scan_f32_minmax": [I, I, P, P, L],
         "oracle_scan_affine": [I, P, P, L],
+        "oracle_scan_maxcount": [I, P, P, L],
+        "oracle_scan_mat2": [I, P, P, L],
         "oracle_segscan_i32": [I, I, P, P, P, L],
         "oracle_segscan_u32": [I, I, P, P, P, L],
         "oracle_segscan_f32_add": [I, P, P, P, P, L],
@@ -135,6 +137,40 @@ def scan_affine(ab: np.ndarray, exclusive: bool = False) -> np.ndarray:
     n = ab.shape[0]
     y = np.empty((n, 2), np.uint32)
     lib.oracle_scan_affine(1 if exclusive else 0, _ptr(ab), _ptr(y), n)
+    return y
+
+
+def scan_maxcount(vc: np.ndarray, exclusive: bool = False) -> np.ndarray:
+    """Scan of (value, count) pairs under the (maximum, occurrences) operator.
+
+    vc is an (n, 2) int32 array: int32 values and counts (read as uint32).
+    Element i of an inclusive result is (m, c) with m the largest value among
+    elements 0..i and c the sum, mod 2^32, of the counts of the elements
+    whose value is m.  The empty fold is (INT32_MIN, 0).
+    """
+    lib = _load()
+    vc = _contig(vc.view(np.int32) if vc.dtype == np.uint32 else vc, np.int32)
+    if vc.ndim != 2 or vc.shape[1] != 2:
+        raise ValueError("vc must have shape (n, 2)")
+    n = vc.shape[0]
+    y = np.empty((n, 2), np.int32)
+    lib.oracle_scan_maxcount(1 if exclusive else 0, _ptr(vc), _ptr(y), n)
+    return y
+
+
+def scan_mat2(x: np.ndarray, exclusive: bool = False) -> np.ndarray:
+    """Scan of 2x2 uint32 matrices (rows of 4: a, b, c, d for [[a, b], [c, d]]).
+
+    Element i of an inclusive result is X_i X_{i-1} ... X_0 mod 2^32, the
+    later factor on the left; the empty product is the identity.
+    """
+    lib = _load()
+    x = _contig(x, np.uint32)
+    if x.ndim != 2 or x.shape[1] != 4:
+        raise ValueError("x must have shape (n, 4)")
+    n = x.shape[0]
+    y = np.empty((n, 4), np.uint32)
+    lib.oracle_scan_mat2(1 if exclusive else 0, _ptr(x), _ptr(y), n)
     return y
 
 

@@ -33,6 +33,11 @@
  *   PMPP9 §9.6 array compaction; YLY §2.2 flag/pos example].
  *   Segmented scan restarts the fold at every head flag [L7 concept 2, radix
  *   sort remark]; index 0 always starts a segment.
+ *   Composite and matrix operators [L7 concept 1, operator generalisation,
+ *   which names matrix multiplication and a user-defined "(maximum, number
+ *   of occurrences)" operator]: (v1,c1) (+) (v2,c2) keeps the larger value
+ *   and adds the counts on a tie, empty fold (INT32_MIN, 0); 2x2 matrices
+ *   multiply with the later factor on the left, empty product the identity.
  */
 #include <math.h>
 #include <stdint.h>
@@ -164,6 +169,74 @@ void oracle_scan_affine(int exclusive, const uint32_t *ab, uint32_t *y, int64_t 
         if (!exclusive) {
             y[2 * i] = A;
             y[2 * i + 1] = B;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* The "(maximum, number of occurrences)" composite operator that [L7]  */
+/* concept 1 names among user-defined scan operators, over pairs stored */
+/* as (v0,c0,v1,c1,...) with int32 values and uint32 counts: the fold   */
+/* keeps the largest value seen and adds up the counts of the elements  */
+/* that carry it (mod 2^32).  The empty fold is (INT32_MIN, 0).          */
+/* ------------------------------------------------------------------ */
+void oracle_scan_maxcount(int exclusive, const int32_t *vc, int32_t *y, int64_t n)
+{
+    int32_t M = INT32_MIN;
+    uint32_t C = 0u;
+    for (int64_t i = 0; i < n; ++i) {
+        int32_t v = vc[2 * i];
+        uint32_t c = (uint32_t)vc[2 * i + 1];
+        if (exclusive) {
+            y[2 * i] = M;
+            y[2 * i + 1] = (int32_t)C;
+        }
+        if (v > M) {
+            M = v;
+            C = c;
+        } else if (v == M) {
+            C = C + c;
+        }
+        if (!exclusive) {
+            y[2 * i] = M;
+            y[2 * i + 1] = (int32_t)C;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Products of 2x2 uint32 matrices (row-major a,b,c,d per element), the */
+/* matrix-multiplication operator of [L7] concept 1, mod 2^32: element  */
+/* i of an inclusive result is X_i * X_{i-1} * ... * X_0 (the later     */
+/* factor on the left, as for affine maps, which are the matrices       */
+/* [[a,b],[0,1]]).  The empty product is the identity matrix.           */
+/* ------------------------------------------------------------------ */
+void oracle_scan_mat2(int exclusive, const uint32_t *x, uint32_t *y, int64_t n)
+{
+    uint32_t P[4] = {1u, 0u, 0u, 1u};
+    for (int64_t i = 0; i < n; ++i) {
+        const uint32_t *X = x + 4 * i;
+        uint32_t Q[4];
+        if (exclusive) {
+            y[4 * i + 0] = P[0];
+            y[4 * i + 1] = P[1];
+            y[4 * i + 2] = P[2];
+            y[4 * i + 3] = P[3];
+        }
+        /* Q = X * P */
+        Q[0] = X[0] * P[0] + X[1] * P[2];
+        Q[1] = X[0] * P[1] + X[1] * P[3];
+        Q[2] = X[2] * P[0] + X[3] * P[2];
+        Q[3] = X[2] * P[1] + X[3] * P[3];
+        P[0] = Q[0];
+        P[1] = Q[1];
+        P[2] = Q[2];
+        P[3] = Q[3];
+        if (!exclusive) {
+            y[4 * i + 0] = P[0];
+            y[4 * i + 1] = P[1];
+            y[4 * i + 2] = P[2];
+            y[4 * i + 3] = P[3];
         }
     }
 }

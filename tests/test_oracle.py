@@ -344,3 +344,123 @@ def test_compaction_invariants_large():
     np.testing.assert_array_equal(out, x[flags])
     assert pos[-1] + int(flags[-1]) == count
     np.testing.assert_array_equal(pos, oracle.scan("add", flags.astype(np.uint32), exclusive=True))
+
+
+# ---------------------------------------------------------------- (max, count) and 2x2 matrices
+# The composite "(maximum, number of occurrences)" operator and matrix
+# multiplication are the scan operators "Lecture 7: 并行模式五 —— 前缀和 / 扫描"
+# names beside addition (concept 1); neither has a worked example on the
+# pages, so both are pinned by brute force, closed forms and invariants.
+
+def _maxcount_brute(vc, exclusive):
+    out = []
+    for i in range(len(vc)):
+        pre = vc[:i] if exclusive else vc[:i + 1]
+        if len(pre) == 0:
+            out.append((-(2**31), 0))
+            continue
+        m = max(int(v) for v, _ in pre)
+        c = sum(int(c) & 0xFFFFFFFF for v, c in pre if int(v) == m) % 2**32
+        out.append((m, c))
+    return out
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_bruteforce_maxcount(exclusive):
+    rng = np.random.default_rng(11)
+    for n in (1, 2, 3, 7, 40, 97):
+        v = rng.integers(-3, 4, n).astype(np.int32)  # few values: many ties
+        c = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)  # counts that wrap
+        vc = np.stack([v, c.view(np.int32)], axis=1)
+        y = oracle.scan_maxcount(vc, exclusive=exclusive)
+        want = _maxcount_brute(vc, exclusive)
+        assert [(int(a), int(b) & 0xFFFFFFFF) for a, b in y] == want
+
+
+def test_maxcount_closed_forms():
+    n = 1000
+    # all values equal: the count is the running sum of the counts
+    vc = np.stack([np.full(n, 5, np.int32), np.arange(1, n + 1, dtype=np.int32)], axis=1)
+    y = oracle.scan_maxcount(vc)
+    np.testing.assert_array_equal(y[:, 0], 5)
+    np.testing.assert_array_equal(y[:, 1].astype(np.int64), np.arange(1, n + 1) * np.arange(2, n + 2) // 2)
+    # strictly increasing values with count 1: every element is a new maximum
+    vc = np.stack([np.arange(-n, 0, dtype=np.int32), np.ones(n, np.int32)], axis=1)
+    y = oracle.scan_maxcount(vc)
+    np.testing.assert_array_equal(y, vc)
+    # the empty fold heads every exclusive result
+    y = oracle.scan_maxcount(vc, exclusive=True)
+    assert tuple(y[0]) == (-(2**31), 0)
+    np.testing.assert_array_equal(y[1:], oracle.scan_maxcount(vc)[:-1])
+
+
+def test_maxcount_against_numpy():
+    n = 3000
+    v = (si.int32_full(71, n) % 50).astype(np.int32)
+    vc = np.stack([v, np.ones(n, np.int32)], axis=1)
+    y = oracle.scan_maxcount(vc)
+    m = np.maximum.accumulate(v)
+    np.testing.assert_array_equal(y[:, 0], m)
+    counts = np.array([int((v[:i + 1] == m[i]).sum()) for i in range(n)])
+    np.testing.assert_array_equal(y[:, 1], counts)
+
+
+def _mat_mul(x, y):
+    a, b, c, d = (int(t) for t in x)
+    e, f, g, h = (int(t) for t in y)
+    M = 2**32
+    return ((a * e + b * g) % M, (a * f + b * h) % M, (c * e + d * g) % M, (c * f + d * h) % M)
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_bruteforce_mat2(exclusive):
+    rng = np.random.default_rng(12)
+    for n in (1, 2, 3, 5, 33):
+        x = rng.integers(0, 2**32, (n, 4), dtype=np.uint64).astype(np.uint32)
+        y = oracle.scan_mat2(x, exclusive=exclusive)
+        for i in range(n):
+            P = (1, 0, 0, 1)
+            for k in range(i if exclusive else i + 1):
+                P = _mat_mul(x[k], P)  # the later factor on the left
+            assert tuple(int(t) for t in y[i]) == P, i
+
+
+def test_mat2_fibonacci_powers():
+    # every element [[1, 1], [1, 0]]: the i-th inclusive product is its
+    # (i+1)-th power [[F(i+2), F(i+1)], [F(i+1), F(i)]] (textbook identity),
+    # with the Fibonacci numbers here from their defining recurrence
+    n = 500
+    x = np.tile(np.array([1, 1, 1, 0], np.uint32), (n, 1))
+    y = oracle.scan_mat2(x)
+    F = [0, 1]
+    while len(F) < n + 3:
+        F.append(F[-1] + F[-2])
+    for i in range(n):
+        want = [F[i + 2] % 2**32, F[i + 1] % 2**32, F[i + 1] % 2**32, F[i] % 2**32]
+        assert [int(t) for t in y[i]] == want, i
+
+
+def test_mat2_embeds_affine():
+    # affine maps are the matrices [[a, b], [0, 1]]: the matrix scan must
+    # reproduce the affine scan (pinned above) in its first row
+    n = 2000
+    ab = si.affine_pairs(13, n)
+    x = np.zeros((n, 4), np.uint32)
+    x[:, 0], x[:, 1], x[:, 3] = ab[:, 0], ab[:, 1], 1
+    for exclusive in (False, True):
+        y = oracle.scan_mat2(x, exclusive=exclusive)
+        np.testing.assert_array_equal(y[:, :2], oracle.scan_affine(ab, exclusive=exclusive))
+        np.testing.assert_array_equal(y[:, 2], 0)
+        np.testing.assert_array_equal(y[:, 3], 1)
+
+
+def test_mat2_determinant_is_multiplicative():
+    n = 2000
+    x = si.uint32_full(14, 4 * n).reshape(n, 4)
+    y = oracle.scan_mat2(x)
+    M = 2**32
+    det = lambda t: (int(t[0]) * int(t[3]) - int(t[1]) * int(t[2])) % M
+    acc = 1
+    for i in range(n):
+        acc = acc * det(x[i]) % M
+        assert det(y[i]) == acc, i
