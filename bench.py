@@ -77,6 +77,10 @@ WORKLOADS = [
      lambda n, kept: 16 * n),
     ("segmented int32 inclusive add 2^27 (values, head bytes, out)",
      "tile_scan_persistent<dwpt::OpSeg<dwpt::OpAdd<int> >, false", 1 << 27, lambda n, kept: 9 * n),
+    ("(maximum, count) inclusive 2^27 pairs", "tile_scan_persistent<dwpt::OpMaxCount, false", 1 << 27,
+     lambda n, kept: 16 * n),
+    ("2x2 matrix product inclusive 2^25 matrices", "tile_scan_persistent<dwpt::OpMat2, false", 1 << 25,
+     lambda n, kept: 32 * n),
 ]
 
 
@@ -274,6 +278,16 @@ def workloads_once(dw, torch, si, steps):
     ys = torch.empty_like(xs)
     for _ in range(steps):
         dw.segmented_scan(xs, hs, "add", out=ys)
+    del xs, hs, ys
+    vc = torch.from_numpy(si.maxcount_pairs(8, 1 << 27)).cuda()
+    yvc = torch.empty_like(vc)
+    for _ in range(steps):
+        dw.scan_inclusive(vc, "maxcount", out=yvc)
+    del vc, yvc
+    m = torch.from_numpy(si.mat2_elems(9, 1 << 25)).cuda()
+    ym = torch.empty_like(m)
+    for _ in range(steps):
+        dw.scan_inclusive(m, "mat2", out=ym)
     torch.cuda.synchronize()
     err = dw.scan_get_device_error()
     print(json.dumps({"workloads_once": steps, "device_error": err}), flush=True)
@@ -381,6 +395,15 @@ def suite(dw, torch, si, out_path, steps):
     ys = torch.empty_like(xs)
     rec("segmented int32 inclusive add 2^27", 1 << 27, 9, lambda: dw.segmented_scan(xs, hs, "add", out=ys))
     del xs, hs, ys
+    vc = torch.from_numpy(si.maxcount_pairs(8, 1 << 27)).cuda()
+    yvc = torch.empty_like(vc)
+    rec("(maximum, count) inclusive 2^27 pairs, values in [-1000, 1000]", 1 << 27, 16,
+        lambda: dw.scan_inclusive(vc, "maxcount", out=yvc))
+    del vc, yvc
+    m = torch.from_numpy(si.mat2_elems(9, 1 << 25)).cuda()
+    ym = torch.empty_like(m)
+    rec("2x2 uint32 matrix product inclusive 2^25 matrices", 1 << 25, 32, lambda: dw.scan_inclusive(m, "mat2", out=ym))
+    del m, ym
     for k in range(5, 16):
         n = 4 ** k
         xm = torch.from_numpy(si.int32_full(6, n)).cuda()

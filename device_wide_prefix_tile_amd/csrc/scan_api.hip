@@ -8,6 +8,7 @@
 #include <map>
 #include <mutex>
 #include <new>
+#include <type_traits>
 #include <utility>
 
 #include "dwpt_scan.h"
@@ -41,6 +42,18 @@ namespace {
 #ifndef DWPT_WAIT8
 #define DWPT_WAIT8 3
 #endif
+#ifndef DWPT_ITEMS_MC          // (max, count) pairs
+#define DWPT_ITEMS_MC 6
+#endif
+#ifndef DWPT_WAIT_MC
+#define DWPT_WAIT_MC 3
+#endif
+#ifndef DWPT_ITEMS16           // 16-byte values (2x2 matrices)
+#define DWPT_ITEMS16 2
+#endif
+#ifndef DWPT_WAIT16
+#define DWPT_WAIT16 4
+#endif
 #ifndef DWPT_ITEMS_SEG         // segmented scans (value + head flag)
 #define DWPT_ITEMS_SEG 12
 #endif
@@ -55,11 +68,21 @@ namespace {
 #endif
 template <class Op>
 struct Shape {
-    static constexpr bool SEG = IsSeg<Op>::value, WIDE = sizeof(typename Op::elem_t) == 8;
+    static constexpr bool SEG = IsSeg<Op>::value, WIDE = sizeof(typename Op::elem_t) == 8,
+                          WIDE16 = sizeof(typename Op::elem_t) == 16;
     static constexpr int BLOCK = DWPT_BLOCK;
-    static constexpr int ITEMS = SEG ? DWPT_ITEMS_SEG : WIDE ? DWPT_ITEMS8 : DWPT_ITEMS4;
+    static constexpr bool MC = std::is_same<Op, OpMaxCount>::value;
+    static constexpr int ITEMS = SEG      ? DWPT_ITEMS_SEG
+                                 : MC     ? DWPT_ITEMS_MC
+                                 : WIDE16 ? DWPT_ITEMS16
+                                 : WIDE   ? DWPT_ITEMS8
+                                          : DWPT_ITEMS4;
     static constexpr int TILE = Geometry<Op, BLOCK, ITEMS>::TILE;
-    static constexpr int WAIT = SEG ? DWPT_WAIT_SEG : WIDE ? DWPT_WAIT8 : DWPT_WAIT4;
+    static constexpr int WAIT = SEG      ? DWPT_WAIT_SEG
+                                : MC     ? DWPT_WAIT_MC
+                                : WIDE16 ? DWPT_WAIT16
+                                : WIDE   ? DWPT_WAIT8
+                                         : DWPT_WAIT4;
 };
 
 // ------------------------------------------------------------ settings
@@ -318,13 +341,16 @@ typedef scan_status_t (*Runner)(const Call&, bool);
 template <bool EXCL>
 Runner plain_runner(int op, int dt)
 {
-    static const Runner table[4][4] = {
-        {run_scan<OpAdd<int32_t>, EXCL>, run_scan<OpAdd<uint32_t>, EXCL>, run_scan<OpAdd<float>, EXCL>, nullptr},
-        {run_scan<OpMax<int32_t>, EXCL>, run_scan<OpMax<uint32_t>, EXCL>, run_scan<OpMax<float>, EXCL>, nullptr},
-        {run_scan<OpMin<int32_t>, EXCL>, run_scan<OpMin<uint32_t>, EXCL>, run_scan<OpMin<float>, EXCL>, nullptr},
-        {nullptr, nullptr, nullptr, run_scan<OpAffine, EXCL>},
+    static const Runner table[3][3] = {
+        {run_scan<OpAdd<int32_t>, EXCL>, run_scan<OpAdd<uint32_t>, EXCL>, run_scan<OpAdd<float>, EXCL>},
+        {run_scan<OpMax<int32_t>, EXCL>, run_scan<OpMax<uint32_t>, EXCL>, run_scan<OpMax<float>, EXCL>},
+        {run_scan<OpMin<int32_t>, EXCL>, run_scan<OpMin<uint32_t>, EXCL>, run_scan<OpMin<float>, EXCL>},
     };
-    return table[op][dt];
+    if (op <= SCAN_OP_MIN && dt <= SCAN_F32) return table[op][dt];
+    if (op == SCAN_OP_AFFINE && dt == SCAN_U32X2) return run_scan<OpAffine, EXCL>;
+    if (op == SCAN_OP_MAX_COUNT && dt == SCAN_I32_U32) return run_scan<OpMaxCount, EXCL>;
+    if (op == SCAN_OP_MAT2 && dt == SCAN_U32X4) return run_scan<OpMat2, EXCL>;
+    return nullptr;
 }
 
 template <bool EXCL>
@@ -341,7 +367,16 @@ Runner seg_runner(int op, int dt)
     return table[op][dt];
 }
 
-size_t elem_size(int dt) { return dt == SCAN_U32X2 ? 8 : 4; }
+// Element size, which is also the alignment an array of the type needs.
+size_t elem_size(int dt)
+{
+    switch (dt) {
+        case SCAN_U32X2:
+        case SCAN_I32_U32: return 8;
+        case SCAN_U32X4: return 16;
+        default: return 4;
+    }
+}
 
 bool ranges_partially_overlap(const void* a, const void* b, size_t bytes_a, size_t bytes_b)
 {
@@ -353,7 +388,7 @@ bool ranges_partially_overlap(const void* a, const void* b, size_t bytes_a, size
 scan_status_t plain_scan(bool excl, scan_op_t op, scan_dtype_t dt, const void* in, void* out, size_t n,
                          void* stream)
 {
-    if ((unsigned)op > SCAN_OP_AFFINE || (unsigned)dt > SCAN_U32X2) return SCAN_ERR_UNSUPPORTED;
+    if ((unsigned)op > SCAN_OP_MAT2 || (unsigned)dt > SCAN_U32X4) return SCAN_ERR_UNSUPPORTED;
     const Runner r = excl ? plain_runner<true>(op, dt) : plain_runner<false>(op, dt);
     if (!r) return SCAN_ERR_UNSUPPORTED;
     if (n == 0) return SCAN_OK;

@@ -30,6 +30,13 @@ namespace dwpt {
 struct Affine {
     uint32_t a, b;
 };
+struct MaxCount {
+    int32_t m;   // the largest value so far
+    uint32_t c;  // the summed counts of the elements that carry it
+};
+struct Mat2 {
+    uint32_t a, b, c, d;  // [[a, b], [c, d]], row-major
+};
 
 // ---------------------------------------------------------------- helpers
 template <typename V>
@@ -146,6 +153,32 @@ struct OpAffine : SameCarry<Affine, OpAffine> {
     __device__ __forceinline__ static Affine combine(Affine e, Affine l)
     {
         return {l.a * e.a, l.a * e.b + l.b};
+    }
+};
+
+// ---------------------------------------------------------------- (max, count)
+// The "(maximum, number of occurrences)" composite operator [L7 concept 1,
+// operator generalisation]: keep the larger value; on a tie add the counts
+// (mod 2^32).  Identity (INT32_MIN, 0).
+struct OpMaxCount : SameCarry<MaxCount, OpMaxCount> {
+    __device__ __forceinline__ static MaxCount identity() { return {INT32_MIN, 0u}; }
+    __device__ __forceinline__ static MaxCount combine(MaxCount e, MaxCount l)
+    {
+        if (l.m > e.m) return l;
+        if (l.m == e.m) return {e.m, e.c + l.c};
+        return e;
+    }
+};
+
+// ---------------------------------------------------------------- 2x2 matrices
+// Matrix multiplication [L7 concept 1] over uint32 (mod 2^32), the later
+// factor on the left: X_e (+) X_l = X_l * X_e, as for the affine maps, which
+// are the matrices [[a, b], [0, 1]].  Identity: the identity matrix.
+struct OpMat2 : SameCarry<Mat2, OpMat2> {
+    __device__ __forceinline__ static Mat2 identity() { return {1u, 0u, 0u, 1u}; }
+    __device__ __forceinline__ static Mat2 combine(Mat2 e, Mat2 l)
+    {
+        return {l.a * e.a + l.b * e.c, l.a * e.b + l.b * e.d, l.c * e.a + l.d * e.c, l.c * e.b + l.d * e.d};
     }
 };
 

@@ -16,8 +16,8 @@
  *     Calls only enqueue work: they return before the GPU has finished, and
  *     results (and device-side errors, see scan_get_device_error) are visible
  *     after the stream is synchronised.
- *   - n is an element count (pairs for the affine dtype).  n == 0 returns
- *     SCAN_OK and launches nothing.
+ *   - n is an element count (pairs for the U32X2 and I32_U32 dtypes,
+ *     matrices for U32X4).  n == 0 returns SCAN_OK and launches nothing.
  *   - Pointers must be aligned to the element size; 16-byte alignment selects
  *     the vector path, anything else a slower scalar path with the same
  *     results.  `out` may equal `in` (in-place); partial overlap is rejected.
@@ -35,7 +35,8 @@
  *
  * Valid combinations:
  *   scan_inclusive / scan_exclusive: ADD, MAX, MIN with I32, U32, F32;
- *                                    AFFINE with U32X2.
+ *                                    AFFINE with U32X2; MAX_COUNT with
+ *                                    I32_U32; MAT2 with U32X4.
  *   segmented_scan:                  ADD, MAX, MIN with I32, U32, F32.
  *   compact:                         I32, U32, F32.
  * Integer ADD wraps modulo 2^32.  F32 ADD results may differ from an exact
@@ -66,14 +67,18 @@ typedef enum {
     SCAN_OP_ADD = 0,
     SCAN_OP_MAX = 1,
     SCAN_OP_MIN = 2,
-    SCAN_OP_AFFINE = 3 /* x -> a*x + b maps composed, later map applied after */
+    SCAN_OP_AFFINE = 3,    /* x -> a*x + b maps composed, later map applied after */
+    SCAN_OP_MAX_COUNT = 4, /* (maximum, number of occurrences) composite */
+    SCAN_OP_MAT2 = 5       /* 2x2 matrix product, later factor on the left */
 } scan_op_t;
 
 typedef enum {
     SCAN_I32 = 0,
     SCAN_U32 = 1,
     SCAN_F32 = 2,
-    SCAN_U32X2 = 3 /* (a, b) pairs of uint32, 8 bytes per element */
+    SCAN_U32X2 = 3,   /* (a, b) pairs of uint32, 8 bytes per element */
+    SCAN_I32_U32 = 4, /* (int32 value, uint32 count) pairs, 8 bytes per element */
+    SCAN_U32X4 = 5    /* 2x2 uint32 matrices [[a, b], [c, d]] stored a, b, c, d: 16 bytes */
 } scan_dtype_t;
 
 /*
@@ -85,6 +90,11 @@ typedef enum {
  * (a2,b2) o (a1,b1) = (a2*a1, a2*b1 + b2) mod 2^32, i.e. its b component is
  * the recurrence y_i = a_i*y_{i-1} + b_i with y_{-1} = 0 [L7 concept 1,
  * recurrences as scans].
+ * MAX_COUNT and MAT2 are the composite and matrix operators [L7 concept 1,
+ * operator generalisation]: (v1,c1) (+) (v2,c2) keeps the larger value and,
+ * on a tie, adds the counts (mod 2^32) -- fed (x_i, 1) it gives the maximum
+ * so far and how often it occurred; MAT2 multiplies 2x2 matrices mod 2^32
+ * with the later factor on the left (affine maps are [[a, b], [0, 1]]).
  */
 scan_status_t scan_inclusive(scan_op_t op, scan_dtype_t dtype, const void* in, void* out,
                              size_t n, void* stream);
@@ -93,7 +103,7 @@ scan_status_t scan_inclusive(scan_op_t op, scan_dtype_t dtype, const void* in, v
  * Exclusive scan: out[0] = identity, out[i] = in[0] (+) ... (+) in[i-1].
  * [L7 concept 1; PMPP9 §9.1 (identity table); YLY §2.2]  Identities: ADD 0,
  * MAX the type's lowest value (-inf for F32), MIN its highest (+inf),
- * AFFINE (1, 0).
+ * AFFINE (1, 0), MAX_COUNT (INT32_MIN, 0), MAT2 the identity matrix.
  */
 scan_status_t scan_exclusive(scan_op_t op, scan_dtype_t dtype, const void* in, void* out,
                              size_t n, void* stream);

@@ -162,3 +162,26 @@ def float32_sym(seed: int, n: int) -> np.ndarray:
     """float32 uniform in [-1, 1) on the 2^-23 grid."""
     return _map_chunks(seed, n, 0, np.float32,
                        lambda u: ((u >> np.uint64(40)).astype(np.float64) * 2.0**-23 - 1.0).astype(np.float32))
+
+
+def maxcount_pairs(seed: int, n: int, span: int = 1000, unit_counts: bool = True) -> np.ndarray:
+    """(n, 2) int32 pairs (value, count): values uniform in [-span, span] (so
+    that the running maximum ties often), counts 1, or with unit_counts False
+    uniform uint32 (stored as int32 bits)."""
+    s = _stream_seed(seed, 0)
+    out = np.empty((n, 2), np.int32)
+
+    def work(c0, c1):
+        u = _draws_span(s, c0, c1 - c0)
+        out[c0:c1, 0] = ((u >> np.uint64(32)) % np.uint64(2 * span + 1)).astype(np.int64) - span
+        if unit_counts:
+            out[c0:c1, 1] = 1
+        else:
+            out[c0:c1, 1] = (u & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.int32)
+    _parallel(n, work)
+    return out
+
+
+def mat2_elems(seed: int, n: int) -> np.ndarray:
+    """(n, 4) uint32: 2x2 matrices [[a, b], [c, d]] stored (a, b, c, d), entries uniform."""
+    return uint32_full(seed, 4 * n).reshape(n, 4)

@@ -67,6 +67,21 @@ def test_argument_checks_before_any_launch():
     assert L.scan_inclusive(9, I32, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
     assert L.segmented_scan(AFF, PAIR, 1024, 4096, 2048, 10, 0, None) == binding.SCAN_ERR_UNSUPPORTED
     assert L.compact(PAIR, 1024, 2048, 4096, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    MC, MAT2, MCPAIR, MAT = 4, 5, 4, 5
+    assert L.scan_inclusive(MC, I32, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(MC, PAIR, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(MAT2, PAIR, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_exclusive(ADD, MAT, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(MAX, MCPAIR, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(6, MAT, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(MAT2, 6, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.segmented_scan(MC, MCPAIR, 1024, 4096, 2048, 10, 0, None) == binding.SCAN_ERR_UNSUPPORTED
+    # a 2x2 matrix is one 16-byte vector: 16-byte alignment; a pair needs 8
+    assert L.scan_inclusive(MAT2, MAT, 1032, 8192, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.scan_inclusive(MAT2, MAT, 1024, 8200, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.scan_inclusive(MC, MCPAIR, 1028, 8192, 10, None) == binding.SCAN_ERR_INVALID
+    # in-place is allowed, partial overlap is not (n matrices of 16 bytes)
+    assert L.scan_inclusive(MAT2, MAT, 1024, 1024 + 16 * 5, 10, None) == binding.SCAN_ERR_INVALID
     # invalid pointers, alignment and overlap
     assert L.scan_inclusive(ADD, I32, None, 2048, 10, None) == binding.SCAN_ERR_INVALID
     assert L.scan_inclusive(ADD, I32, 1025, 4096, 10, None) == binding.SCAN_ERR_INVALID

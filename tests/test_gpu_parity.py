@@ -132,6 +132,54 @@ def test_affine_parity(exclusive, odd):
                          "affine excl=%s odd=%s n=%d path=%s" % (exclusive, odd, n, path))
 
 
+# ---------------------------------------------------------------- composite and matrix operators
+TILE_MC = 15 * 64 * 6   # (value, count) pairs per tile
+TILE_M2 = 15 * 64 * 2   # 2x2 matrices per tile
+PAIR_SIZES = [1, 2, 63, 64, 65, 1000, 4097, TILE_M2 - 1, TILE_M2, TILE_M2 + 1, TILE_MC - 1, TILE_MC,
+              TILE_MC + 1, 3 * TILE_MC + 17, 65537, 250001]
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+@pytest.mark.parametrize("counts", ["unit", "wrap"])
+def test_maxcount_parity(exclusive, counts):
+    fn = dw.scan_exclusive if exclusive else dw.scan_inclusive
+    for k, n in enumerate(PAIR_SIZES):
+        # values in [-20, 20]: the running maximum ties often
+        vc = si.maxcount_pairs(600 + k, n, span=20, unit_counts=(counts == "unit"))
+        ref = oracle.scan_maxcount(vc, exclusive=exclusive)
+        for path in paths_for(n):
+            with Path(path):
+                y = from_dev(fn(to_dev(vc), "maxcount"))
+            assert_equal(y, ref, "maxcount excl=%s counts=%s n=%d path=%s" % (exclusive, counts, n, path))
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_mat2_parity(exclusive):
+    fn = dw.scan_exclusive if exclusive else dw.scan_inclusive
+    for k, n in enumerate(PAIR_SIZES):
+        x = si.mat2_elems(700 + k, n)
+        ref = oracle.scan_mat2(x, exclusive=exclusive)
+        for path in paths_for(n):
+            with Path(path):
+                y = from_dev(fn(to_dev(x), "mat2"))
+            assert_equal(y, ref, "mat2 excl=%s n=%d path=%s" % (exclusive, n, path))
+
+
+def test_mat2_special_cases():
+    n = 7 * TILE_M2 + 5
+    # powers of [[1, 1], [1, 0]] (Fibonacci numbers mod 2^32)
+    x = np.tile(np.array([1, 1, 1, 0], np.uint32), (n, 1))
+    for path in ("multi", "fallback", "rts"):
+        with Path(path):
+            assert_equal(from_dev(dw.scan_inclusive(to_dev(x), "mat2")), oracle.scan_mat2(x), "fib " + path)
+    # affine maps as [[a, b], [0, 1]]: the matrix scan's first row is the affine scan
+    ab = si.affine_pairs(95, n)
+    m = np.zeros((n, 4), np.uint32)
+    m[:, 0], m[:, 1], m[:, 3] = ab[:, 0], ab[:, 1], 1
+    y = from_dev(dw.scan_inclusive(to_dev(m), "mat2"))
+    assert_equal(np.ascontiguousarray(y[:, :2]), from_dev(dw.scan_inclusive(to_dev(ab), "affine")), "mat2 vs affine")
+
+
 # ---------------------------------------------------------------- segmented scans
 HEAD_MIXES = {
     "mean1000": lambda s, n: si.segment_heads(s, n, 1000.0),
