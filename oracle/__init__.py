@@ -64,6 +64,7 @@ def _load():
         "oracle_scan_affine": [I, P, P, L],
         "oracle_scan_maxcount": [I, P, P, L],
         "oracle_scan_mat2": [I, P, P, L],
+        "oracle_csr_offsets": [P, L, ctypes.c_uint32, P],
         "oracle_segscan_i32": [I, I, P, P, P, L],
         "oracle_segscan_u32": [I, I, P, P, P, L],
         "oracle_segscan_f32_add": [I, P, P, P, P, L],
@@ -172,6 +173,16 @@ def scan_mat2(x: np.ndarray, exclusive: bool = False) -> np.ndarray:
     y = np.empty((n, 4), np.uint32)
     lib.oracle_scan_mat2(1 if exclusive else 0, _ptr(x), _ptr(y), n)
     return y
+
+
+def csr_offsets(rows: np.ndarray, n_rows: int) -> np.ndarray:
+    """CSR row pointers (n_rows + 1 uint32) of COO row indices: row_ptr[r] is
+    the number of entries with row index < r; indices >= n_rows are ignored."""
+    lib = _load()
+    rows = _contig(rows, np.uint32)
+    row_ptr = np.empty(n_rows + 1, np.uint32)
+    lib.oracle_csr_offsets(_ptr(rows), rows.shape[0], n_rows, _ptr(row_ptr))
+    return row_ptr
 
 
 def segmented_scan(op: str, x: np.ndarray, heads: np.ndarray, exclusive: bool = False):

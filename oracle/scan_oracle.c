@@ -14,6 +14,7 @@
  *   [YLY]   "CUDA编程并行前缀和扫描详解" (tutorial, m.youleyou.com)
  *   [PMPP9] "第9章并行模式：前缀和 - Scan算法 (Parallel Patterns: Prefix Sum -
  *           Scan Algorithms)" (PMPP chapter 9 notes, bittern.cn)
+ *   [ECE408] "UIUC ECE 408 应用并行编程" (course index, runguoli.com)
  *
  * Definitions followed:
  *   inclusive  y[i] = x[0] (+) ... (+) x[i]
@@ -38,6 +39,7 @@
  *   of occurrences)" operator]: (v1,c1) (+) (v2,c2) keeps the larger value
  *   and adds the counts on a tie, empty fold (INT32_MIN, 0); 2x2 matrices
  *   multiply with the later factor on the left, empty product the identity.
+ *   CSR row offsets are the exclusive scan of the per-row entry counts.
  */
 #include <math.h>
 #include <stdint.h>
@@ -238,6 +240,27 @@ void oracle_scan_mat2(int exclusive, const uint32_t *x, uint32_t *y, int64_t n)
             y[4 * i + 2] = P[2];
             y[4 * i + 3] = P[3];
         }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* CSR row offsets from COO row indices: building the CSR sparse format */
+/* is among the uses of a prefix sum that [YLY] lists in its            */
+/* introduction, and [ECE408] (L09) gives the layout, rowPtr[N+1].      */
+/* Count the entries of every row, then row_ptr = exclusive scan of the */
+/* counts, n_rows + 1 values; row_ptr[n_rows] = the entries counted.    */
+/* Entries whose row index is n_rows or more are not counted.            */
+/* ------------------------------------------------------------------ */
+void oracle_csr_offsets(const uint32_t *rows, int64_t nnz, uint32_t n_rows, uint32_t *row_ptr)
+{
+    for (uint32_t r = 0; r <= n_rows; ++r) row_ptr[r] = 0u;
+    for (int64_t i = 0; i < nnz; ++i)
+        if (rows[i] < n_rows) row_ptr[rows[i]] += 1u;
+    uint32_t acc = 0u;
+    for (uint32_t r = 0; r <= n_rows; ++r) {
+        uint32_t c = row_ptr[r];
+        row_ptr[r] = acc;
+        acc += c;
     }
 }
 

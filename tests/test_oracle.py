@@ -464,3 +464,35 @@ def test_mat2_determinant_is_multiplicative():
     for i in range(n):
         acc = acc * det(x[i]) % M
         assert det(y[i]) == acc, i
+
+
+# ---------------------------------------------------------------- CSR row offsets
+# Building the CSR format is among the uses of a prefix sum listed in the
+# introduction of "CUDA编程并行前缀和扫描详解"; its row pointer array has
+# N + 1 entries ("UIUC ECE 408 应用并行编程", L09).
+
+def test_csr_offsets_bruteforce():
+    rng = np.random.default_rng(13)
+    for n_rows, nnz in ((1, 0), (1, 5), (7, 30), (50, 200), (300, 40)):
+        rows = rng.integers(0, n_rows + 3, nnz).astype(np.uint32)  # some out of range
+        rp = oracle.csr_offsets(rows, n_rows)
+        assert rp.shape == (n_rows + 1,)
+        for r in range(n_rows + 1):
+            assert int(rp[r]) == sum(1 for v in rows if int(v) < r), (n_rows, r)
+
+
+def test_csr_offsets_closed_forms():
+    # k entries in every row: row_ptr[r] = k * r
+    n_rows, k = 1000, 7
+    rows = np.repeat(np.arange(n_rows, dtype=np.uint32), k)
+    np.testing.assert_array_equal(oracle.csr_offsets(rows, n_rows), k * np.arange(n_rows + 1))
+    # sorted rows (with empty rows): row_ptr[r] is the first index whose row is >= r
+    rows = np.sort(si.uint32_full(15, 20000) % 3000).astype(np.uint32)
+    rp = oracle.csr_offsets(rows, 3000)
+    np.testing.assert_array_equal(rp, np.searchsorted(rows, np.arange(3001), side="left"))
+    # unsorted: the same offsets as the sorted indices
+    perm = si.uint32_full(16, rows.size) .argsort(kind="stable")
+    np.testing.assert_array_equal(oracle.csr_offsets(rows[perm], 3000), rp)
+    # indices past the last row are not counted
+    assert int(oracle.csr_offsets(np.array([0, 5, 9, 2], np.uint32), 5)[-1]) == 2
+    np.testing.assert_array_equal(oracle.csr_offsets(np.zeros(0, np.uint32), 4), np.zeros(5, np.uint32))
