@@ -404,6 +404,14 @@ def suite(dw, torch, si, out_path, steps):
     ym = torch.empty_like(m)
     rec("2x2 uint32 matrix product inclusive 2^25 matrices", 1 << 25, 32, lambda: dw.scan_inclusive(m, "mat2", out=ym))
     del m, ym
+    # CSR row offsets of 2^27 sorted COO row indices over 2^23 rows (16 per row on
+    # average); per entry: the index read once, and 4 / 16 bytes of row_ptr written
+    nnz, n_rows = 1 << 27, 1 << 23
+    rows = torch.from_numpy(np.sort(si.uint32_full(10, nnz) % n_rows).astype(np.uint32)).cuda()
+    rp = torch.empty(n_rows + 1, dtype=torch.uint32, device="cuda")
+    rec("CSR row offsets, 2^27 sorted COO entries over 2^23 rows", nnz, 4 + 4 * (n_rows + 1) / nnz,
+        lambda: dw.csr_row_offsets(rows, n_rows, out=rp))
+    del rows, rp
     for k in range(5, 16):
         n = 4 ** k
         xm = torch.from_numpy(si.int32_full(6, n)).cuda()

@@ -22,7 +22,7 @@ _DTYPES = {torch.int32: SCAN_I32, torch.uint32: SCAN_U32, torch.float32: SCAN_F3
 
 EXPORTS = ("scan_inclusive", "scan_exclusive", "segmented_scan", "compact", "scan_status_string",
            "scan_get_device_error", "scan_release_workspace", "scan_set_small_n_max",
-           "scan_set_spin_limit", "scan_set_multi_tile_mode", "scan_copy_probe")
+           "scan_set_spin_limit", "scan_set_multi_tile_mode", "scan_copy_probe", "csr_row_offsets")
 
 _lib = None
 
@@ -54,6 +54,7 @@ def lib() -> ctypes.CDLL:
         "scan_set_spin_limit": ([U], U),
         "scan_set_multi_tile_mode": ([I], I),
         "scan_copy_probe": ([P, P, S, P], I),
+        "csr_row_offsets": ([P, S, U, P, P], I),
     }
     for name, (argtypes, restype) in sig.items():
         fn = getattr(L, name)
@@ -141,6 +142,24 @@ def segmented_scan(x: torch.Tensor, heads: torch.Tensor, op: str = "add", exclus
     out = _prep(x, out)
     _check(lib().segmented_scan(OPS[op], dt, x.data_ptr(), heads.data_ptr(), out.data_ptr(), x.shape[0],
                                 1 if exclusive else 0, _stream(stream)), "segmented_scan")
+    return out
+
+
+def csr_row_offsets(rows: torch.Tensor, n_rows: int, out: torch.Tensor | None = None, stream=None):
+    """CSR row pointers of COO row indices: out[r] = #entries with row < r, r = 0 .. n_rows
+    (n_rows + 1 values; indices >= n_rows are not counted).  rows: 1-D int32/uint32 device tensor."""
+    if rows.dtype not in (torch.int32, torch.uint32) or rows.dim() != 1:
+        raise TypeError("rows must be a 1-D int32/uint32 tensor")
+    if not rows.is_cuda or not rows.is_contiguous():
+        raise ValueError("rows must be a contiguous device tensor")
+    if not 0 <= n_rows < 2**32 - 1:
+        raise ValueError("n_rows out of range")
+    if out is None:
+        out = torch.empty(n_rows + 1, dtype=torch.uint32, device=rows.device)
+    elif out.shape != (n_rows + 1,) or out.dtype not in (torch.int32, torch.uint32) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (n_rows + 1,) int32/uint32 tensor")
+    _check(lib().csr_row_offsets(rows.data_ptr(), rows.shape[0], n_rows, out.data_ptr(), _stream(stream)),
+           "csr_row_offsets")
     return out
 
 

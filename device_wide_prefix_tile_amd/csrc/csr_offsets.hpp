@@ -1,0 +1,61 @@
+// CSR row offsets from COO row indices: row_ptr[r] = number of entries with
+// row index < r, for r = 0 .. n_rows.  Building the CSR sparse format is one
+// of the uses of a prefix sum listed in the introduction of
+// "CUDA编程并行前缀和扫描详解"; the row pointer array has N + 1 entries
+// ("UIUC ECE 408 应用并行编程", L09).  Two steps: count the entries of every
+// row into row_ptr (csr_count_kernel, after row_ptr is zeroed), then an
+// exclusive add scan of the n_rows + 1 counts in place (the library's scan).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wave_ops.hpp"
+
+namespace dwpt {
+
+constexpr int kCsrBlock = 256;
+constexpr int kCsrSteps = 16;  // 64-entry windows per wavefront and chunk
+
+__global__ __launch_bounds__(kCsrBlock) void zero_u32_kernel(uint32_t* p, uint64_t n)
+{
+    for (uint64_t i = blockIdx.x * (uint64_t)kCsrBlock + threadIdx.x; i < n; i += (uint64_t)gridDim.x * kCsrBlock)
+        p[i] = 0u;
+}
+
+// Every wavefront takes chunks of kCsrSteps windows of 64 consecutive
+// entries, one entry per lane (coalesced 4-byte loads, all issued before any
+// is used).  In a window, a lane whose row differs from its left neighbour's
+// starts a run; the ballot of run starts gives each run's length, and the
+// lane that starts it adds the whole run with one atomic.  Sorted input thus
+// costs about one atomic per row and window, unsorted input one per entry at
+// worst; both count exactly.  Rows >= n_rows are skipped.
+__global__ __launch_bounds__(kCsrBlock) void csr_count_kernel(const uint32_t* __restrict__ rows, uint64_t nnz,
+                                                              uint32_t n_rows, uint32_t* counts)
+{
+    const int lane = lane_id();
+    const uint64_t wave = (blockIdx.x * (uint64_t)kCsrBlock + threadIdx.x) >> 6;
+    const uint64_t waves = (gridDim.x * (uint64_t)kCsrBlock) >> 6;
+    constexpr uint64_t kChunk = 64 * kCsrSteps;
+    for (uint64_t base = wave * kChunk; base < nnz; base += waves * kChunk) {
+        uint32_t r[kCsrSteps];
+#pragma unroll
+        for (int s = 0; s < kCsrSteps; ++s) {
+            const uint64_t i = base + (uint64_t)s * 64 + lane;
+            r[s] = i < nnz ? rows[i] : 0xFFFFFFFFu;  // past the end: never a valid row
+        }
+#pragma unroll
+        for (int s = 0; s < kCsrSteps; ++s) {
+            const uint32_t prev = wave_shift_up(r[s], ~r[s]);  // lane 0: a value unequal to its own
+            const bool start = r[s] != prev;
+            const uint64_t starts = wave_ballot(start);
+            // the next run start above this lane, or the end of the window
+            const uint64_t above = lane == 63 ? 0ull : starts & (~0ull << (lane + 1));
+            const uint32_t len = (uint32_t)((above ? __builtin_ctzll(above) : 64) - lane);
+            if (start && r[s] < n_rows)
+                __hip_atomic_fetch_add(&counts[r[s]], len, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+}  // namespace dwpt

@@ -1,7 +1,7 @@
 // scan_api.hip -- C ABI of libdwpt_scan.so: argument checks, the
 // (op, dtype, variant) dispatch table, workspace management and launches.
-// The kernels are in tile_scan.hpp and reduce_then_scan.hpp; the ABI is
-// documented in dwpt_scan.h.
+// The kernels are in tile_scan.hpp, reduce_then_scan.hpp and
+// csr_offsets.hpp; the ABI is documented in dwpt_scan.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -11,6 +11,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "csr_offsets.hpp"
 #include "dwpt_scan.h"
 #include "reduce_then_scan.hpp"
 #include "tile_scan.hpp"
@@ -441,6 +442,37 @@ scan_status_t segmented_scan(scan_op_t op, scan_dtype_t dtype, const void* in, c
             return SCAN_ERR_INVALID;
         const Call c{in, out, head_flags, nullptr, n, static_cast<hipStream_t>(stream)};
         return r(c, is_aligned(in, 16) && is_aligned(out, 16) && is_aligned(head_flags, 4));
+    } catch (const std::bad_alloc&) {
+        return SCAN_ERR_NOMEM;
+    }
+}
+
+scan_status_t csr_row_offsets(const uint32_t* row_idx, size_t nnz, uint32_t n_rows, uint32_t* row_ptr,
+                              void* stream)
+{
+    try {
+        const size_t np = (size_t)n_rows + 1;
+        if (!row_ptr || !is_aligned(row_ptr, 4)) return SCAN_ERR_INVALID;
+        if (nnz > 0 && (!row_idx || !is_aligned(row_idx, 4))) return SCAN_ERR_INVALID;
+        if (nnz >= ((size_t)1 << 32)) return SCAN_ERR_INVALID;  // offsets are uint32
+        if (nnz > 0) {
+            const uintptr_t a = (uintptr_t)row_idx, b = (uintptr_t)row_ptr;
+            if (a < b + np * 4 && b < a + nnz * 4) return SCAN_ERR_INVALID;  // any overlap
+        }
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        // counts of every row into row_ptr[0 .. n_rows), row_ptr[n_rows] = 0
+        const unsigned zgrid = (unsigned)std::min<size_t>((np + kCsrBlock - 1) / kCsrBlock, 4096);
+        hipLaunchKernelGGL(zero_u32_kernel, dim3(zgrid), dim3(kCsrBlock), 0, s, row_ptr, (uint64_t)np);
+        if (nnz > 0) {
+            const size_t chunks = (nnz + 64 * kCsrSteps - 1) / (64 * kCsrSteps);  // one per wavefront
+            const unsigned grid = (unsigned)std::min<size_t>((chunks + kCsrBlock / 64 - 1) / (kCsrBlock / 64), 4096);
+            hipLaunchKernelGGL(csr_count_kernel, dim3(grid), dim3(kCsrBlock), 0, s, row_idx, (uint64_t)nnz, n_rows,
+                               row_ptr);
+        }
+        if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+        // row_ptr = exclusive scan of the counts, in place
+        const Call c{row_ptr, row_ptr, nullptr, nullptr, np, s};
+        return run_scan<OpAdd<uint32_t>, true>(c, is_aligned(row_ptr, 16));
     } catch (const std::bad_alloc&) {
         return SCAN_ERR_NOMEM;
     }

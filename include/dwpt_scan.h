@@ -131,6 +131,22 @@ scan_status_t segmented_scan(scan_op_t op, scan_dtype_t dtype, const void* in,
 scan_status_t compact(scan_dtype_t dtype, const void* in, void* out, uint32_t* d_count, size_t n,
                       void* stream);
 
+/*
+ * CSR row offsets from COO row indices: row_ptr[r] = the number of entries
+ * i with row_idx[i] < r, for r = 0 .. n_rows (n_rows + 1 values, so
+ * row_ptr[n_rows] is the number of entries counted).  Entries whose row
+ * index is n_rows or more are not counted.  The counts of every row go to
+ * row_ptr, and an exclusive add scan of them in place gives the offsets:
+ * building the CSR format is among the uses of a prefix sum that [YLY]
+ * lists in its introduction, and the row pointer array has N + 1 entries
+ * ("UIUC ECE 408 应用并行编程", L09).  row_idx (nnz uint32, any order) and
+ * row_ptr (n_rows + 1 uint32, caller-owned) are device arrays aligned to 4
+ * bytes that must not overlap; nnz < 2^32.  Sorted indices cost about one
+ * atomic add per row, unsorted ones up to one per entry.
+ */
+scan_status_t csr_row_offsets(const uint32_t* row_idx, size_t nnz, uint32_t n_rows, uint32_t* row_ptr,
+                              void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* scan_status_string(scan_status_t s);
 

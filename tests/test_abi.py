@@ -92,6 +92,15 @@ def test_argument_checks_before_any_launch():
     assert L.compact(F32, 1024, 8192, None, 10, None) == binding.SCAN_ERR_INVALID
     assert L.compact(F32, 1024, 8192, 1 << 20, 1 << 32, None) == binding.SCAN_ERR_INVALID
     assert L.scan_copy_probe(1024, 2048, 10, None) == binding.SCAN_ERR_INVALID
+    # CSR row offsets: row_ptr required and aligned, indices required when nnz > 0,
+    # no overlap at all, nnz below 2^32
+    assert L.csr_row_offsets(1024, 10, 5, None, None) == binding.SCAN_ERR_INVALID
+    assert L.csr_row_offsets(1024, 10, 5, 8194, None) == binding.SCAN_ERR_INVALID
+    assert L.csr_row_offsets(None, 10, 5, 8192, None) == binding.SCAN_ERR_INVALID
+    assert L.csr_row_offsets(1026, 10, 5, 8192, None) == binding.SCAN_ERR_INVALID
+    assert L.csr_row_offsets(1024, 10, 5, 1024, None) == binding.SCAN_ERR_INVALID
+    assert L.csr_row_offsets(1024, 10, 5, 1024 + 36, None) == binding.SCAN_ERR_INVALID
+    assert L.csr_row_offsets(1024, 1 << 32, 5, 1 << 40, None) == binding.SCAN_ERR_INVALID
 
 
 def test_tuning_knobs_round_trip():
