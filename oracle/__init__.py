@@ -65,6 +65,7 @@ def _load():
         "oracle_scan_maxcount": [I, P, P, L],
         "oracle_scan_mat2": [I, P, P, L],
         "oracle_csr_offsets": [P, L, ctypes.c_uint32, P],
+        "oracle_radix_split": [P, P, L, ctypes.c_uint32, P, P],
         "oracle_segscan_i32": [I, I, P, P, P, L],
         "oracle_segscan_u32": [I, I, P, P, P, L],
         "oracle_segscan_f32_add": [I, P, P, P, P, L],
@@ -183,6 +184,22 @@ def csr_offsets(rows: np.ndarray, n_rows: int) -> np.ndarray:
     row_ptr = np.empty(n_rows + 1, np.uint32)
     lib.oracle_csr_offsets(_ptr(rows), rows.shape[0], n_rows, _ptr(row_ptr))
     return row_ptr
+
+
+def radix_split(keys: np.ndarray, shift: int, vals: np.ndarray | None = None):
+    """One stable radix-sort pass by the digit (key >> shift) & 255: returns
+    (keys_out, vals_out or None)."""
+    lib = _load()
+    keys = _contig(keys, np.uint32)
+    n = keys.shape[0]
+    ko = np.empty(n, np.uint32)
+    if vals is None:
+        lib.oracle_radix_split(_ptr(keys), None, n, shift, _ptr(ko), None)
+        return ko, None
+    vals = _contig(vals, np.uint32)
+    vo = np.empty(n, np.uint32)
+    lib.oracle_radix_split(_ptr(keys), _ptr(vals), n, shift, _ptr(ko), _ptr(vo))
+    return ko, vo
 
 
 def segmented_scan(op: str, x: np.ndarray, heads: np.ndarray, exclusive: bool = False):

@@ -40,6 +40,9 @@
  *   and adds the counts on a tie, empty fold (INT32_MIN, 0); 2x2 matrices
  *   multiply with the later factor on the left, empty product the identity.
  *   CSR row offsets are the exclusive scan of the per-row entry counts.
+ *   A radix-sort pass places every key by an exclusive scan of the digit
+ *   counts [L7 concept 2, radix sort; PMPP9 §9.6 radix sort], keeping the
+ *   input order within a digit; 32-bit keys take four 8-bit passes.
  */
 #include <math.h>
 #include <stdint.h>
@@ -261,6 +264,34 @@ void oracle_csr_offsets(const uint32_t *rows, int64_t nnz, uint32_t n_rows, uint
         uint32_t c = row_ptr[r];
         row_ptr[r] = acc;
         acc += c;
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* One pass of a radix sort: a stable split of uint32 keys (and their    */
+/* values, if any) by the 8-bit digit (key >> shift) & 255.  Radix sort */
+/* splits by digit and places every element with a scan of the digit    */
+/* histogram [L7 concept 2; PMPP9 §9.6]; 32-bit keys take four passes.  */
+/* Written out: count every digit, exclusive scan of the 256 counts,     */
+/* then each element in input order to the next free place of its digit.*/
+/* ------------------------------------------------------------------ */
+void oracle_radix_split(const uint32_t *keys, const uint32_t *vals, int64_t n, uint32_t shift,
+                        uint32_t *keys_out, uint32_t *vals_out)
+{
+    int64_t start[256];
+    int64_t count[256];
+    for (int d = 0; d < 256; ++d) count[d] = 0;
+    for (int64_t i = 0; i < n; ++i) count[(keys[i] >> shift) & 255u] += 1;
+    int64_t acc = 0;
+    for (int d = 0; d < 256; ++d) {
+        start[d] = acc;
+        acc += count[d];
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        const uint32_t d = (keys[i] >> shift) & 255u;
+        const int64_t at = start[d]++;
+        keys_out[at] = keys[i];
+        if (vals) vals_out[at] = vals[i];
     }
 }
 

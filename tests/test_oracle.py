@@ -496,3 +496,47 @@ def test_csr_offsets_closed_forms():
     # indices past the last row are not counted
     assert int(oracle.csr_offsets(np.array([0, 5, 9, 2], np.uint32), 5)[-1]) == 2
     np.testing.assert_array_equal(oracle.csr_offsets(np.zeros(0, np.uint32), 4), np.zeros(5, np.uint32))
+
+
+# ---------------------------------------------------------------- radix-sort split pass
+# "Lecture 7: 并行模式五 —— 前缀和 / 扫描", concept 2: radix sort splits by digit
+# and places every element with a scan; a 32-bit key takes four 8-bit passes.
+
+def test_radix_split_bruteforce():
+    rng = np.random.default_rng(17)
+    for n in (0, 1, 2, 9, 300):
+        keys = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)
+        vals = np.arange(n, dtype=np.uint32)
+        for shift in (0, 8, 20, 24):
+            ko, vo = oracle.radix_split(keys, shift, vals)
+            digit = lambda k: (int(k) >> shift) & 255
+            want = sorted(range(n), key=lambda i: (digit(keys[i]), i))  # stable by construction
+            assert [int(v) for v in vo] == want
+            assert [int(k) for k in ko] == [int(keys[i]) for i in want]
+
+
+def test_radix_split_matches_stable_argsort():
+    n = 100000
+    keys = si.uint32_full(18, n) % np.uint32(5000)  # many equal keys and digits
+    vals = si.uint32_full(19, n)
+    for shift in (0, 4, 8):
+        d = (keys >> np.uint32(shift)) & np.uint32(255)
+        perm = np.argsort(d, kind="stable")
+        ko, vo = oracle.radix_split(keys, shift, vals)
+        np.testing.assert_array_equal(ko, keys[perm])
+        np.testing.assert_array_equal(vo, vals[perm])
+        ko2, none = oracle.radix_split(keys, shift)
+        assert none is None
+        np.testing.assert_array_equal(ko2, ko)
+
+
+def test_radix_four_passes_sort():
+    n = 50000
+    keys = si.uint32_full(20, n)
+    keys[::7] = keys[3]  # duplicates
+    vals = np.arange(n, dtype=np.uint32)
+    k, v = keys, vals
+    for shift in (0, 8, 16, 24):
+        k, v = oracle.radix_split(k, shift, v)
+    np.testing.assert_array_equal(k, np.sort(keys))
+    np.testing.assert_array_equal(v, np.argsort(keys, kind="stable"))
