@@ -81,6 +81,12 @@ WORKLOADS = [
      lambda n, kept: 16 * n),
     ("2x2 matrix product inclusive 2^25 matrices", "tile_scan_persistent<dwpt::OpMat2, false", 1 << 25,
      lambda n, kept: 32 * n),
+    ("CSR row counts, 2^27 sorted COO row indices (indices read once)", "csr_count_kernel", 1 << 27,
+     lambda n, kept: 4 * n),
+    ("radix split histogram pass, 2^28 uint32 keys (keys read once)", "radix_hist_kernel", 1 << 28,
+     lambda n, kept: 4 * n),
+    ("radix split scatter pass, 2^28 uint32 keys (keys read + written)", "radix_scatter_kernel<false>", 1 << 28,
+     lambda n, kept: 8 * n),
 ]
 
 
@@ -244,6 +250,7 @@ def summarize_workload_traffic(fetch_dir, write_dir):
 
 def workloads_once(dw, torch, si, steps):
     """Each full-size workload `steps` times, one input resident at a time (for counter runs)."""
+    import numpy as np
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1.0)
@@ -288,6 +295,18 @@ def workloads_once(dw, torch, si, steps):
     ym = torch.empty_like(m)
     for _ in range(steps):
         dw.scan_inclusive(m, "mat2", out=ym)
+    del m, ym
+    nnz, n_rows = 1 << 27, 1 << 23
+    rows = torch.from_numpy(np.sort(si.uint32_full(10, nnz) % n_rows).astype(np.uint32)).cuda()
+    rp = torch.empty(n_rows + 1, dtype=torch.uint32, device="cuda")
+    for _ in range(steps):
+        dw.csr_row_offsets(rows, n_rows, out=rp)
+    del rows, rp
+    k = torch.from_numpy(si.uint32_full(11, 1 << 28)).cuda()
+    ko = torch.empty_like(k)
+    for _ in range(steps):
+        dw.radix_split(k, 8, keys_out=ko)
+    del k, ko
     torch.cuda.synchronize()
     err = dw.scan_get_device_error()
     print(json.dumps({"workloads_once": steps, "device_error": err}), flush=True)
@@ -412,6 +431,26 @@ def suite(dw, torch, si, out_path, steps):
     rec("CSR row offsets, 2^27 sorted COO entries over 2^23 rows", nnz, 4 + 4 * (n_rows + 1) / nnz,
         lambda: dw.csr_row_offsets(rows, n_rows, out=rp))
     del rows, rp
+    # one radix-sort pass (stable split by the digit (key >> 8) & 255): algorithmic bytes are
+    # one read and one write of every key (and value); the three launches move 12 B per key
+    # plus the scan of 256 counts per 8192-key tile
+    keys = torch.from_numpy(si.uint32_full(11, 1 << 28)).cuda()
+    k1, k2 = torch.empty_like(keys), torch.empty_like(keys)
+    rec("radix split pass, 2^28 uint32 keys", 1 << 28, 8, lambda: dw.radix_split(keys, 8, keys_out=k1))
+
+    def four_passes():
+        dw.radix_split(keys, 0, keys_out=k1)
+        dw.radix_split(k1, 8, keys_out=k2)
+        dw.radix_split(k2, 16, keys_out=k1)
+        dw.radix_split(k1, 24, keys_out=k2)
+    rec("radix sort (four 8-bit passes), 2^28 uint32 keys", 1 << 28, 32, four_passes)
+    del keys, k1, k2
+    keys = torch.from_numpy(si.uint32_full(12, 1 << 27)).cuda()
+    vals = torch.from_numpy(si.uint32_full(13, 1 << 27)).cuda()
+    ko, vo = torch.empty_like(keys), torch.empty_like(vals)
+    rec("radix split pass, 2^27 uint32 key-value pairs", 1 << 27, 16,
+        lambda: dw.radix_split(keys, 8, vals, keys_out=ko, vals_out=vo))
+    del keys, vals, ko, vo
     for k in range(5, 16):
         n = 4 ** k
         xm = torch.from_numpy(si.int32_full(6, n)).cuda()

@@ -22,7 +22,8 @@ _DTYPES = {torch.int32: SCAN_I32, torch.uint32: SCAN_U32, torch.float32: SCAN_F3
 
 EXPORTS = ("scan_inclusive", "scan_exclusive", "segmented_scan", "compact", "scan_status_string",
            "scan_get_device_error", "scan_release_workspace", "scan_set_small_n_max",
-           "scan_set_spin_limit", "scan_set_multi_tile_mode", "scan_copy_probe", "csr_row_offsets")
+           "scan_set_spin_limit", "scan_set_multi_tile_mode", "scan_copy_probe", "csr_row_offsets",
+           "radix_split")
 
 _lib = None
 
@@ -55,6 +56,7 @@ def lib() -> ctypes.CDLL:
         "scan_set_multi_tile_mode": ([I], I),
         "scan_copy_probe": ([P, P, S, P], I),
         "csr_row_offsets": ([P, S, U, P, P], I),
+        "radix_split": ([P, P, S, U, P, P, P], I),
     }
     for name, (argtypes, restype) in sig.items():
         fn = getattr(L, name)
@@ -161,6 +163,46 @@ def csr_row_offsets(rows: torch.Tensor, n_rows: int, out: torch.Tensor | None = 
     _check(lib().csr_row_offsets(rows.data_ptr(), rows.shape[0], n_rows, out.data_ptr(), _stream(stream)),
            "csr_row_offsets")
     return out
+
+
+def _u32_vector(x: torch.Tensor, name: str):
+    if x.dtype not in (torch.int32, torch.uint32) or x.dim() != 1:
+        raise TypeError("%s must be a 1-D int32/uint32 tensor" % name)
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("%s must be a contiguous device tensor" % name)
+
+
+def radix_split(keys: torch.Tensor, shift: int, vals: torch.Tensor | None = None,
+                keys_out: torch.Tensor | None = None, vals_out: torch.Tensor | None = None, stream=None):
+    """One stable radix-sort pass by the digit (key >> shift) & 255 of uint32 keys.
+
+    Returns (keys_out, vals_out); vals_out is None when vals is None.  Outputs are
+    allocated when not given and must not overlap the inputs."""
+    _u32_vector(keys, "keys")
+    n = keys.shape[0]
+    if not 0 <= shift <= 31:
+        raise ValueError("shift must be in 0 .. 31")
+    if keys_out is None:
+        keys_out = torch.empty_like(keys)
+    _u32_vector(keys_out, "keys_out")
+    if keys_out.shape[0] != n:
+        raise ValueError("keys_out must hold n keys")
+    vp = vop = None
+    if vals is not None:
+        _u32_vector(vals, "vals")
+        if vals.shape[0] != n:
+            raise ValueError("vals must hold n values")
+        if vals_out is None:
+            vals_out = torch.empty_like(vals)
+        _u32_vector(vals_out, "vals_out")
+        if vals_out.shape[0] != n:
+            raise ValueError("vals_out must hold n values")
+        vp, vop = vals.data_ptr(), vals_out.data_ptr()
+    elif vals_out is not None:
+        raise ValueError("vals_out given without vals")
+    _check(lib().radix_split(keys.data_ptr(), vp, n, shift, keys_out.data_ptr(), vop, _stream(stream)),
+           "radix_split")
+    return keys_out, vals_out
 
 
 def compact(x: torch.Tensor, out: torch.Tensor | None = None, count: torch.Tensor | None = None,

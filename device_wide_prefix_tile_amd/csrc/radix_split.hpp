@@ -1,0 +1,286 @@
+// One pass of a least-significant-digit radix sort: a stable split of uint32
+// keys (and, if given, their uint32 values) by the 8-bit digit
+// (key >> shift) & 255.  Radix sort is a split by digit followed by a scan
+// that gives every element its place; 32-bit keys take four such passes
+// ("Lecture 7: 并行模式五 —— 前缀和 / 扫描", concept 2; PMPP chapter 9 notes,
+// §9.6: the scan of the digit histogram gives each bucket's start).
+//
+// Three launches on the caller's stream:
+//   1. radix_hist_kernel: tile t's count of every digit d, stored digit-major
+//      at hist[d * T + t] (T tiles);
+//   2. the library's exclusive add scan of hist, in place: hist[d * T + t]
+//      becomes the output position of tile t's first key of digit d (all
+//      smaller digits come first, then the same digit in earlier tiles);
+//   3. radix_scatter_kernel: every key's rank among the keys of its digit in
+//      its tile, the tile reordered by digit in LDS, and each digit's run
+//      written to its position.
+//
+// Ranking inside a wavefront, one round of 64 keys at a time: every lane
+// sets its bit in an LDS word kept for its digit and reads the word back,
+// which gives the mask of lanes holding the same digit (a round whose keys
+// all share one digit skips this).  A key's rank is the number of those
+// lanes below it plus the wavefront's count of the digit so far, which the
+// lowest lane of the group advances by the group's size with one LDS add.
+//
+// Measured on MI355X with 2^28 keys: eight ballots of the digit bits find
+// the same masks with about 40 more vector instructions per round, which
+// made the pass 6% slower; LDS adds from many lanes to one word are slow
+// (all 64 on one word: five times the time of the loads), hence the counter
+// copies of the histogram pass.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "wave_ops.hpp"
+
+namespace dwpt {
+
+constexpr int kRsBlock = 512;                  // 8 wavefronts
+constexpr int kRsItems = 16;                   // keys per lane
+constexpr int kRsWaves = kRsBlock / 64;
+constexpr int kRsWaveKeys = 64 * kRsItems;     // wavefront w owns keys [w * kRsWaveKeys, ...) of the tile
+constexpr int kRsTile = kRsBlock * kRsItems;   // 8192 keys
+constexpr int kRsDigits = 256;
+static_assert(kRsBlock >= kRsDigits, "one thread per digit");
+
+// Number of lanes of mask m below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Tile of workgroup b of T (one tile per workgroup).  Workgroups are dealt
+// to the chip's 8 XCDs in turn (workgroup b to XCD b % 8), and each XCD has
+// its own L2: XCD x takes the x-th eighth of the tiles, in order.
+// Neighbouring tiles then run on one XCD at about the same time, so the
+// partial cache lines that they write side by side (a digit's run of one
+// tile ends where the next tile's begins) are merged in that XCD's L2
+// before they go to memory.
+__device__ __forceinline__ uint32_t rs_tile(uint32_t b, uint32_t T)
+{
+    constexpr uint32_t kXcds = 8;
+    const uint32_t x = b % kXcds, i = b / kXcds, q = T / kXcds, r = T % kXcds;
+    return x * q + (x < r ? x : r) + i;
+}
+
+// Keys of this lane: round v holds key tile_base + w * kRsWaveKeys + v * 64 + lane,
+// so the order of (wavefront, round, lane) is the input order.  FULL: the
+// whole tile lies below n.
+template <bool FULL>
+__device__ __forceinline__ void load_keys(const uint32_t* __restrict__ src, uint64_t base, uint64_t n, int lane,
+                                          uint32_t (&k)[kRsItems])
+{
+#pragma unroll
+    for (int v = 0; v < kRsItems; ++v) {
+        const uint64_t i = base + (uint64_t)v * 64 + lane;
+        k[v] = FULL || i < n ? src[i] : 0u;
+    }
+}
+
+// This lane's keys of tile t.
+__device__ __forceinline__ void load_tile(const uint32_t* __restrict__ src, uint32_t t, uint64_t n, int w, int lane,
+                                          uint32_t (&k)[kRsItems])
+{
+    const uint64_t base = (uint64_t)t * kRsTile + (uint64_t)w * kRsWaveKeys;
+    if ((uint64_t)(t + 1) * kRsTile <= n)
+        load_keys<true>(src, base, n, lane, k);
+    else
+        load_keys<false>(src, base, n, lane, k);
+}
+
+// Histogram counters: one set per workgroup with kRsCopies copies of each
+// digit's counter side by side; lane l adds to copy l % kRsCopies.  LDS adds
+// to one word from many lanes of an instruction are slow (measured: 64 lanes
+// on one word cost about five times the loads; up to four per word cost
+// nothing visible), and with 16 copies at most 4 lanes ever share a word.
+constexpr int kRsCopies = 16;
+
+template <bool FULL>
+__device__ __forceinline__ void hist_count(uint32_t* cnt, const uint32_t (&k)[kRsItems], uint64_t base, uint64_t n,
+                                           uint32_t shift, int lane)
+{
+    uint32_t* my = cnt + (lane % kRsCopies);
+#pragma unroll
+    for (int v = 0; v < kRsItems; ++v)
+        if (FULL || base + (uint64_t)v * 64 + lane < n) atomicAdd(my + ((k[v] >> shift) & 255u) * kRsCopies, 1u);
+}
+
+// Pass 1: hist[d * T + t] = number of keys of digit d in tile t.
+__global__ __launch_bounds__(kRsBlock) void radix_hist_kernel(const uint32_t* __restrict__ keys, uint64_t n,
+                                                              uint32_t shift, uint32_t T, uint32_t* __restrict__ hist)
+{
+    __shared__ uint32_t s_cnt[kRsDigits * kRsCopies];
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    const uint32_t t = rs_tile(blockIdx.x, T);
+    uint32_t k[kRsItems];
+    load_tile(keys, t, n, w, lane, k);
+    for (int i = threadIdx.x; i < kRsDigits * kRsCopies; i += kRsBlock) s_cnt[i] = 0u;
+    __syncthreads();
+    const uint64_t base = (uint64_t)t * kRsTile + (uint64_t)w * kRsWaveKeys;
+    if ((uint64_t)(t + 1) * kRsTile <= n)
+        hist_count<true>(s_cnt, k, base, n, shift, lane);
+    else
+        hist_count<false>(s_cnt, k, base, n, shift, lane);
+    __syncthreads();
+    if (threadIdx.x < kRsDigits) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < kRsCopies; ++i) c += s_cnt[threadIdx.x * kRsCopies + i];
+        hist[(uint64_t)threadIdx.x * T + t] = c;
+    }
+}
+
+struct RsShared {
+    uint32_t cnt[kRsWaves][kRsDigits];  // per wavefront: running count, then the wavefront's first slot of the digit
+    uint32_t start[kRsDigits];          // digit's first slot in the reordered tile
+    uint32_t base[kRsDigits];           // output position of the tile's first key of the digit, minus start
+    uint32_t part[kRsDigits / 64];
+    union {
+        uint32_t buf[kRsTile];            // the tile reordered by digit: keys, then values
+        uint64_t grp[kRsWaves][kRsDigits];  // while ranking: per wavefront, the lanes holding each digit
+    };
+    uint8_t dig[kRsTile];               // digit of every slot (for the values)
+};
+
+// One tile: keys k (values x) of this lane, counters and digit groups clear.
+template <bool VALS, bool FULL>
+__device__ __forceinline__ void scatter_tile(RsShared& sh, const uint32_t (&k)[kRsItems], const uint32_t (&x)[kRsItems],
+                                             uint64_t n, uint32_t shift, uint32_t g, uint64_t tile_base,
+                                             uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out)
+{
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    const uint64_t base = tile_base + (uint64_t)w * kRsWaveKeys;
+    const uint32_t cnt = FULL ? (uint32_t)kRsTile : (uint32_t)(n - tile_base);
+
+    // rank of every key among the earlier keys of its digit in this
+    // wavefront: the lowest lane of each group of equal digits adds the
+    // group's size to the digit's counter and receives the count before it,
+    // which the other lanes of the group fetch from it.  The adds of
+    // successive rounds need not wait for each other.
+    uint32_t rank[kRsItems];
+    const uint64_t my_bit = 1ull << lane;
+#pragma unroll
+    for (int v = 0; v < kRsItems; ++v) {
+        const bool valid = FULL || base + (uint64_t)v * 64 + lane < n;
+        const uint32_t d = (k[v] >> shift) & 255u;
+        // the lanes holding digit d: every lane sets its bit in the digit's
+        // word, reads the word back, and the lowest of them clears it again
+        // (a wavefront's LDS operations take effect in order).  A round whose
+        // keys share one digit skips this.
+        const uint64_t vm = wave_ballot(valid);
+        const uint32_t d0 = __builtin_amdgcn_readfirstlane(d);
+        uint64_t m = vm;
+        if (wave_ballot(valid && d == d0) != vm) {
+            uint64_t* slot = &sh.grp[w][d];
+            if (valid) atomicOr(slot, my_bit);
+            m = valid ? *slot : 0ull;
+            if (valid && lanes_below(m) == 0) *slot = 0ull;
+        }
+        const uint32_t below = lanes_below(m);
+        uint32_t before = 0;
+        if (valid && below == 0) before = atomicAdd(&sh.cnt[w][d], (uint32_t)__builtin_popcountll(m));
+        const int first = (int)__builtin_ctzll(m | (1ull << 63));  // lowest lane of the group
+        rank[v] = (uint32_t)__builtin_amdgcn_ds_bpermute(first << 2, (int)before) + below;
+    }
+    __syncthreads();
+
+    // per digit: exclusive prefix over the wavefronts, the tile's count, and
+    // the exclusive scan of the counts over the digits
+    if (threadIdx.x < kRsDigits) {
+        const int d = threadIdx.x;
+        uint32_t run = 0;
+#pragma unroll
+        for (int j = 0; j < kRsWaves; ++j) {
+            const uint32_t c = sh.cnt[j][d];
+            sh.cnt[j][d] = run;
+            run += c;
+        }
+        const auto add = [](uint32_t a, uint32_t b) { return a + b; };
+        const uint32_t incl = wave_inclusive_scan(run, 0u, add);
+        if (lane == 63) sh.part[w] = incl;
+        sh.start[d] = incl - run;  // within this wavefront's 64 digits, completed below
+    }
+    __syncthreads();
+    if (threadIdx.x < kRsDigits) {
+        const int d = threadIdx.x;
+        uint32_t before = 0;
+#pragma unroll
+        for (int j = 0; j < kRsDigits / 64; ++j)
+            if (j < w) before += sh.part[j];
+        const uint32_t start = sh.start[d] + before;
+        sh.base[d] = g - start;
+#pragma unroll
+        for (int j = 0; j < kRsWaves; ++j) sh.cnt[j][d] += start;
+    }
+    __syncthreads();
+
+    // reorder the tile by digit (stable) in LDS; rank[] becomes the slot
+#pragma unroll
+    for (int v = 0; v < kRsItems; ++v) {
+        const bool valid = FULL || base + (uint64_t)v * 64 + lane < n;
+        const uint32_t d = (k[v] >> shift) & 255u;
+        rank[v] += sh.cnt[w][d];
+        if (valid) {
+            sh.buf[rank[v]] = k[v];
+            if (VALS) sh.dig[rank[v]] = (uint8_t)d;
+        }
+    }
+    __syncthreads();
+
+    // consecutive slots of a digit go to consecutive output positions
+#pragma unroll
+    for (int v = 0; v < kRsItems; ++v) {
+        const uint32_t j = (uint32_t)v * kRsBlock + threadIdx.x;
+        if (FULL || j < cnt) {
+            const uint32_t key = sh.buf[j];
+            keys_out[sh.base[(key >> shift) & 255u] + j] = key;
+        }
+    }
+    if (VALS) {
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < kRsItems; ++v)
+            if (FULL || base + (uint64_t)v * 64 + lane < n) sh.buf[rank[v]] = x[v];
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < kRsItems; ++v) {
+            const uint32_t j = (uint32_t)v * kRsBlock + threadIdx.x;
+            if (FULL || j < cnt) vals_out[sh.base[sh.dig[j]] + j] = sh.buf[j];
+        }
+    }
+}
+
+// Pass 3: `offs` is the exclusive scan of pass 1's hist.  Writes the tile's
+// keys (and values) to their places in keys_out (vals_out).
+template <bool VALS>
+__global__ __launch_bounds__(kRsBlock) void radix_scatter_kernel(const uint32_t* __restrict__ keys,
+                                                                 const uint32_t* __restrict__ vals, uint64_t n,
+                                                                 uint32_t shift, uint32_t T,
+                                                                 const uint32_t* __restrict__ offs,
+                                                                 uint32_t* __restrict__ keys_out,
+                                                                 uint32_t* __restrict__ vals_out)
+{
+    __shared__ RsShared sh;
+    const int lane = lane_id();
+    const int w = threadIdx.x >> 6;
+    const uint32_t t = rs_tile(blockIdx.x, T);
+    uint32_t k[kRsItems], x[kRsItems];
+    load_tile(keys, t, n, w, lane, k);
+    if (VALS) load_tile(vals, t, n, w, lane, x);
+    const uint32_t g = threadIdx.x < kRsDigits ? offs[(uint64_t)threadIdx.x * T + t] : 0u;
+    for (int i = threadIdx.x; i < kRsWaves * kRsDigits; i += kRsBlock) {
+        (&sh.cnt[0][0])[i] = 0u;
+        (&sh.grp[0][0])[i] = 0ull;
+    }
+    __syncthreads();  // counters and groups cleared
+    const uint64_t tile_base = (uint64_t)t * kRsTile;
+    if (tile_base + kRsTile <= n)
+        scatter_tile<VALS, true>(sh, k, x, n, shift, g, tile_base, keys_out, vals_out);
+    else
+        scatter_tile<VALS, false>(sh, k, x, n, shift, g, tile_base, keys_out, vals_out);
+}
+
+}  // namespace dwpt

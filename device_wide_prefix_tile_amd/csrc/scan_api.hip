@@ -13,6 +13,7 @@
 
 #include "csr_offsets.hpp"
 #include "dwpt_scan.h"
+#include "radix_split.hpp"
 #include "reduce_then_scan.hpp"
 #include "tile_scan.hpp"
 
@@ -113,6 +114,10 @@ struct Workspace {
     // current one
     void* rts = nullptr;
     size_t rts_bytes = 0;
+    // radix passes' digit histograms: scanned in place by the library's own
+    // scan, so kept apart from both buffers above
+    void* hist = nullptr;
+    size_t hist_bytes = 0;
 };
 std::map<std::pair<int, void*>, Workspace> g_ws;
 constexpr size_t kHeaderBytes = 512;  // line 0: err word, tile counter; lines 1-3: persistent-kernel counters
@@ -179,26 +184,45 @@ scan_status_t acquire_workspace(hipStream_t s, size_t words, Workspace** out)
     return SCAN_OK;
 }
 
+// Grows the plain device buffer *p (capacity *have bytes) to at least
+// `bytes`, after the stream has finished with the old one.
+scan_status_t grow_buffer(hipStream_t s, void** p, size_t* have, size_t bytes)
+{
+    if (*have >= bytes) return SCAN_OK;
+    size_t cap = *have ? *have * 2 : (size_t)1 << 16;
+    while (cap < bytes) cap *= 2;
+    if (*p) {
+        if (hipStreamSynchronize(s) != hipSuccess) return SCAN_ERR_HIP;
+        (void)hipFree(*p);
+        *p = nullptr;
+        *have = 0;
+    }
+    if (hipMalloc(p, cap) != hipSuccess) {
+        (void)hipGetLastError();
+        *p = nullptr;
+        return SCAN_ERR_NOMEM;
+    }
+    *have = cap;
+    return SCAN_OK;
+}
+
 // Called with g_mu held, after acquire_workspace: at least `bytes` of
 // reduce-then-scan memory in the workspace.
 scan_status_t acquire_rts(hipStream_t s, Workspace& ws, size_t bytes)
 {
-    if (ws.rts_bytes >= bytes) return SCAN_OK;
-    size_t cap = ws.rts_bytes ? ws.rts_bytes * 2 : (size_t)1 << 16;
-    while (cap < bytes) cap *= 2;
-    if (ws.rts) {
-        if (hipStreamSynchronize(s) != hipSuccess) return SCAN_ERR_HIP;
-        (void)hipFree(ws.rts);
-        ws.rts = nullptr;
-        ws.rts_bytes = 0;
-    }
-    if (hipMalloc(&ws.rts, cap) != hipSuccess) {
-        (void)hipGetLastError();
-        ws.rts = nullptr;
-        return SCAN_ERR_NOMEM;
-    }
-    ws.rts_bytes = cap;
-    return SCAN_OK;
+    return grow_buffer(s, &ws.rts, &ws.rts_bytes, bytes);
+}
+
+// Called with g_mu held: at least `bytes` of histogram memory in the
+// (device, stream) workspace.
+scan_status_t acquire_hist(hipStream_t s, size_t bytes, void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SCAN_ERR_HIP;
+    Workspace& ws = g_ws[std::make_pair(dev, (void*)s)];
+    const scan_status_t st = grow_buffer(s, &ws.hist, &ws.hist_bytes, bytes);
+    *out = ws.hist;
+    return st;
 }
 
 // ------------------------------------------------------------ launches
@@ -478,6 +502,55 @@ scan_status_t csr_row_offsets(const uint32_t* row_idx, size_t nnz, uint32_t n_ro
     }
 }
 
+scan_status_t radix_split(const uint32_t* keys, const uint32_t* vals, size_t n, uint32_t shift,
+                          uint32_t* keys_out, uint32_t* vals_out, void* stream)
+{
+    try {
+        if (shift > 31) return SCAN_ERR_INVALID;
+        if (n == 0) return SCAN_OK;
+        if ((vals == nullptr) != (vals_out == nullptr)) return SCAN_ERR_INVALID;
+        if (n >= ((size_t)1 << 32)) return SCAN_ERR_INVALID;  // positions are uint32
+        if (!keys || !keys_out || !is_aligned(keys, 4) || !is_aligned(keys_out, 4)) return SCAN_ERR_INVALID;
+        if (vals && (!is_aligned(vals, 4) || !is_aligned(vals_out, 4))) return SCAN_ERR_INVALID;
+        const size_t b = n * 4;
+        const auto overlap = [b](const void* x, const void* y) {
+            return x && y && (uintptr_t)x < (uintptr_t)y + b && (uintptr_t)y < (uintptr_t)x + b;
+        };
+        // outputs are written while other tiles still read the inputs
+        if (overlap(keys_out, keys) || overlap(keys_out, vals) || overlap(keys_out, vals_out) ||
+            overlap(vals_out, keys) || overlap(vals_out, vals))
+            return SCAN_ERR_INVALID;
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        const uint32_t T = (uint32_t)((n + kRsTile - 1) / kRsTile);
+        const size_t nh = (size_t)kRsDigits * T;
+        void* hist = nullptr;
+        {
+            std::lock_guard<std::mutex> lock(g_mu);
+            const scan_status_t st = acquire_hist(s, nh * 4, &hist);
+            if (st != SCAN_OK) return st;
+        }
+        uint32_t* h = static_cast<uint32_t*>(hist);
+        hipLaunchKernelGGL(radix_hist_kernel, dim3(T), dim3(kRsBlock), 0,
+                           s, keys, (uint64_t)n, shift, T, h);
+        if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
+        // each (digit, tile) count -> the output position of its first key
+        const Call c{h, h, nullptr, nullptr, nh, s};
+        const scan_status_t st = run_scan<OpAdd<uint32_t>, true>(c, true);
+        if (st != SCAN_OK) return st;
+        if (vals)
+            hipLaunchKernelGGL(radix_scatter_kernel<true>,
+                               dim3(T), dim3(kRsBlock), 0, s,
+                               keys, vals, (uint64_t)n, shift, T, (const uint32_t*)h, keys_out, vals_out);
+        else
+            hipLaunchKernelGGL(radix_scatter_kernel<false>,
+                               dim3(T), dim3(kRsBlock), 0, s,
+                               keys, vals, (uint64_t)n, shift, T, (const uint32_t*)h, keys_out, vals_out);
+        return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
+    } catch (const std::bad_alloc&) {
+        return SCAN_ERR_NOMEM;
+    }
+}
+
 scan_status_t compact(scan_dtype_t dtype, const void* in, void* out, uint32_t* d_count, size_t n, void* stream)
 {
     try {
@@ -545,11 +618,12 @@ scan_status_t scan_release_workspace(void)
     (void)hipGetDevice(&cur);
     scan_status_t st = SCAN_OK;
     for (auto& kv : g_ws) {
-        if (!kv.second.mem && !kv.second.rts) continue;
+        if (!kv.second.mem && !kv.second.rts && !kv.second.hist) continue;
         if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
             st = SCAN_ERR_HIP;
         if (kv.second.mem && hipFree(kv.second.mem) != hipSuccess) st = SCAN_ERR_HIP;
         if (kv.second.rts && hipFree(kv.second.rts) != hipSuccess) st = SCAN_ERR_HIP;
+        if (kv.second.hist && hipFree(kv.second.hist) != hipSuccess) st = SCAN_ERR_HIP;
     }
     g_ws.clear();
     (void)hipSetDevice(cur);

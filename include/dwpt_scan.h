@@ -147,6 +147,25 @@ scan_status_t compact(scan_dtype_t dtype, const void* in, void* out, uint32_t* d
 scan_status_t csr_row_offsets(const uint32_t* row_idx, size_t nnz, uint32_t n_rows, uint32_t* row_ptr,
                               void* stream);
 
+/*
+ * One pass of a least-significant-digit radix sort: a stable split of the
+ * uint32 keys by the 8-bit digit (key >> shift) & 255.  keys_out receives
+ * the keys ordered by digit, keys of one digit in their input order; if
+ * vals is given, vals_out receives each key's value at the key's new place.
+ * Four passes with shift = 0, 8, 16, 24 sort 32-bit keys.  Radix sort is a
+ * split by digit plus a scan that places every element [L7 concept 2,
+ * radix sort]; the scan of the digit histogram gives each bucket's first
+ * position [PMPP9 §9.6 radix sort].
+ *
+ * keys, keys_out (and vals, vals_out) are device arrays of n uint32 aligned
+ * to 4 bytes; vals and vals_out are both NULL or both non-NULL.  No output
+ * may overlap an input or the other output (the split is out of place).
+ * shift <= 31; n < 2^32.  n == 0 does nothing.  The digit histogram (256
+ * uint32 per 8192 keys) lives in the library's per-stream workspace.
+ */
+scan_status_t radix_split(const uint32_t* keys, const uint32_t* vals, size_t n, uint32_t shift,
+                          uint32_t* keys_out, uint32_t* vals_out, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* scan_status_string(scan_status_t s);
 

@@ -103,6 +103,27 @@ def test_argument_checks_before_any_launch():
     assert L.csr_row_offsets(1024, 1 << 32, 5, 1 << 40, None) == binding.SCAN_ERR_INVALID
 
 
+def test_radix_split_argument_checks():
+    """Rejected on the host, before any device work (fake addresses are never touched)."""
+    L = binding.lib()
+    ok, bad = binding.SCAN_OK, binding.SCAN_ERR_INVALID
+    assert L.radix_split(None, None, 0, 0, None, None, None) == ok  # nothing to do
+    assert L.radix_split(1024, None, 10, 32, 1 << 20, None, None) == bad  # shift > 31
+    assert L.radix_split(1024, 4096, 10, 0, 1 << 20, None, None) == bad  # vals without vals_out
+    assert L.radix_split(1024, 4096, 0, 0, 1 << 20, None, None) == ok  # n == 0: nothing is read
+    assert L.radix_split(1024, None, 10, 0, 1 << 20, 4096, None) == bad  # vals_out without vals
+    assert L.radix_split(None, None, 10, 0, 1 << 20, None, None) == bad
+    assert L.radix_split(1024, None, 10, 0, None, None, None) == bad
+    assert L.radix_split(1026, None, 10, 0, 1 << 20, None, None) == bad  # misaligned
+    assert L.radix_split(1024, 1 << 16, 10, 0, 1 << 20, (1 << 24) + 2, None) == bad
+    assert L.radix_split(1024, None, 1 << 32, 0, 1 << 40, None, None) == bad  # n >= 2^32
+    assert L.radix_split(1024, None, 10, 0, 1024, None, None) == bad  # in place
+    assert L.radix_split(1024, None, 10, 0, 1024 + 36, None, None) == bad  # partial overlap
+    assert L.radix_split(1024, 1 << 16, 10, 0, 1 << 20, 1 << 16, None) == bad  # vals_out is vals
+    assert L.radix_split(1024, 1 << 16, 10, 0, 1 << 20, 1024 + 8, None) == bad  # vals_out over keys
+    assert L.radix_split(1024, 1 << 16, 10, 0, 1 << 20, (1 << 20) + 4, None) == bad  # outputs overlap
+
+
 def test_tuning_knobs_round_trip():
     old = binding.scan_set_small_n_max(12345)
     assert binding.scan_set_small_n_max(old) == 12345
