@@ -62,7 +62,10 @@ PROFILE_CMDS = {
                 "python3 bench.py --workloads-once 3",
     "wl_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/prof_wl_write -o wl -- "
                 "python3 bench.py --workloads-once 3",
+    "wl_trace": "rocprofv3 --kernel-trace -f csv -d $OUT/prof_wl_trace -o wl -- "
+                "python3 bench.py --workloads-once 40",
 }
+WL_TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_times_all_workloads.txt")
 
 # Full-size workloads for per-kernel counter runs: (label, kernel-name fragment,
 # n, algorithmic bytes per launch as a function of n and the kept count).
@@ -246,6 +249,39 @@ def summarize_workload_traffic(fetch_dir, write_dir):
     with open(TRAFFIC_ALL_FILE, "w") as f:
         f.write("\n".join(out) + "\n")
     print(open(TRAFFIC_ALL_FILE).read())
+
+
+def summarize_workload_trace(trace_dir):
+    """Kernel durations of every full-size workload's dominant kernel (kernel trace of
+    --workloads-once K: the median over the last half of each kernel's K dispatches, after
+    the clocks have settled) against its algorithmic bytes."""
+    import numpy as np
+    import seeded_inputs as si
+    durs = {w[1]: [] for w in WORKLOADS}
+    rows = sorted(_csv_rows(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
+        for frag in durs:
+            if frag in r.get("Kernel_Name", ""):
+                durs[frag].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    kept = int(np.count_nonzero(si.float32_normal(3, 1 << 28) > 0))
+    out = ["# Kernel duration per launch of each full-size workload's main kernel (rocprofv3 kernel trace)",
+           "# command: " + PROFILE_CMDS["wl_trace"],
+           "# median over the last half of the kernel's dispatches; GB/s = algorithmic bytes / duration",
+           "source_hash: " + kernel_source_hash(),
+           "# workload | kernel | dispatches | median us | algorithmic MB | GB/s | % of 8 TB/s"]
+    for label, frag, n, alg in WORKLOADS:
+        d = durs[frag]
+        if not d:
+            out.append("%s | %s | 0 | missing" % (label, frag))
+            continue
+        med = statistics.median(d[len(d) // 2:])
+        a = alg(n, kept)
+        out.append("%s | %s | %d | %.2f | %.1f | %.1f | %.1f" % (label, frag, len(d), med, a / 1e6,
+                                                                a / (med * 1e-6) / 1e9,
+                                                                100 * a / (med * 1e-6) / 1e9 / PEAK_GBPS))
+    with open(WL_TRACE_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(open(WL_TRACE_FILE).read())
 
 
 def workloads_once(dw, torch, si, steps):
@@ -488,11 +524,16 @@ def main():
                     help="write profiles/ summaries from rocprofv3 CSV output and exit")
     ap.add_argument("--workloads-once", type=int, metavar="K",
                     help="run every full-size workload K times (for counter runs) and exit")
+    ap.add_argument("--summarize-wl-trace", metavar="TRACE_DIR",
+                    help="write the per-workload kernel time summary from a --workloads-once trace")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the per-workload traffic summary under profiles/ and exit")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(*args.summarize_rocprof)
+        return
+    if args.summarize_wl_trace:
+        summarize_workload_trace(args.summarize_wl_trace)
         return
     if args.summarize_traffic:
         summarize_workload_traffic(*args.summarize_traffic)
