@@ -73,8 +73,15 @@ def status_string(status: int) -> str:
 scan_status_string = status_string
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream) -> int:
+    """Handle of `stream` (a torch stream or a raw handle); None: the current device's current
+    stream, read without building a torch Stream object (which costs more than a launch)."""
     if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(torch.cuda.current_device())
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
