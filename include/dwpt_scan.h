@@ -27,11 +27,18 @@
  *     the table below gives SCAN_ERR_UNSUPPORTED; a failed HIP call gives
  *     SCAN_ERR_HIP (hipGetLastError has the HIP code); failure to get
  *     workspace memory gives SCAN_ERR_NOMEM.
- *   - Workspace: the multi-tile path keeps a small status array (8 or 16 bytes
- *     per tile of 2-4 K elements) and a tile counter per (device, stream),
- *     allocated on first use, grown when needed and reused across calls
- *     without clearing.  Calls on one stream are serialised by the stream;
- *     calls on different streams use different workspaces.
+ *   - Workspace: the multi-tile path keeps a status array (17 eight-byte
+ *     words per tile of 1920-15360 elements for each 4 bytes of carry) and
+ *     three counters per (device, stream); reduce-then-scan and the radix
+ *     pass add a plain buffer each (the tile carries; 256 uint32 counts per
+ *     8192-key tile).  Each is allocated on first use, grown when needed
+ *     (after the stream has drained) and reused across calls without
+ *     clearing.  Calls on one stream are serialised by the stream; calls on
+ *     different streams use different workspaces.
+ *   - Host threads: entry points may be called from several threads, but
+ *     calls on one stream must come from one thread at a time (a call may
+ *     grow that stream's workspace while the previous call's kernels are
+ *     still queued on it, which is safe only in stream order).
  *
  * Valid combinations:
  *   scan_inclusive / scan_exclusive: ADD, MAX, MIN with I32, U32, F32;
