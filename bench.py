@@ -64,7 +64,14 @@ PROFILE_CMDS = {
                 "python3 bench.py --workloads-once 3",
     "wl_trace": "rocprofv3 --kernel-trace -f csv -d $OUT/prof_wl_trace -o wl -- "
                 "python3 bench.py --workloads-once 40",
+    "wl_insts": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD "
+                "SQ_INSTS_VMEM_WR SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE -f csv -d $OUT/prof_wl_insts -o wl -- "
+                "python3 bench.py --workloads-once 3",
 }
+WL_INSTS_FILE = os.path.join(ROOT, "profiles", "instructions_all_workloads.txt")
+# one wave64 VALU instruction keeps a 16-lane SIMD busy for at least 4 cycles;
+# MI355X: 256 CUs x 4 SIMDs at 2.4 GHz
+VALU_ISSUE_PER_S = 256 * 4 * 2.4e9 / 4
 WL_TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_times_all_workloads.txt")
 
 # Full-size workloads for per-kernel counter runs: (label, kernel-name fragment,
@@ -282,6 +289,51 @@ def summarize_workload_trace(trace_dir):
     with open(WL_TRACE_FILE, "w") as f:
         f.write("\n".join(out) + "\n")
     print(open(WL_TRACE_FILE).read())
+
+
+def summarize_workload_insts(insts_dir, trace_summary=WL_TRACE_FILE):
+    """Instruction counts per launch of every full-size workload's main kernel (SQ counters,
+    summed over the chip), and the time the VALU instructions alone need at full issue rate,
+    against the kernel's measured duration."""
+    names = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD",
+             "SQ_INSTS_VMEM_WR", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE")
+    per = {}
+    for name in names:
+        per[name] = _counter_means(insts_dir, name, [w[1] for w in WORKLOADS])
+    dur = {}
+    if os.path.exists(trace_summary):
+        for line in open(trace_summary):
+            parts = [x.strip() for x in line.split("|")]
+            if len(parts) >= 4 and not line.startswith("#"):
+                try:
+                    dur[parts[1]] = float(parts[3])
+                except ValueError:
+                    pass
+    out = ["# Instructions per launch of each full-size workload's main kernel (rocprofv3 SQ counters)",
+           "# command: " + PROFILE_CMDS["wl_insts"],
+           "# mean over the kernel's dispatches; counters summed over the chip.  valu_us = VALU",
+           "# instructions x 4 cycles / (1024 SIMDs x 2.4 GHz): the least time they need; kernel_us from",
+           "# " + os.path.basename(trace_summary) + "; lds_conflict_share = LDS bank-conflict cycles / (256 CUs x",
+           "# GRBM_GUI_ACTIVE / 8 XCDs), the share of each CU's time spent in bank conflicts.",
+           "source_hash: " + kernel_source_hash(),
+           "# workload | waves | VALU | SALU | LDS | VMEM rd | VMEM wr | valu_us | kernel_us | valu/kernel | "
+           "lds_conflict_share"]
+    for label, frag, n, alg in WORKLOADS:
+        v = {k: per[k][frag] for k in names}
+        if v["SQ_INSTS_VALU"] is None:
+            out.append("%s | counters missing" % label)
+            continue
+        valu_us = v["SQ_INSTS_VALU"] / VALU_ISSUE_PER_S * 1e6
+        k_us = dur.get(frag)
+        gui = v["GRBM_GUI_ACTIVE"] / 8 if v["GRBM_GUI_ACTIVE"] else None
+        conf = v["SQ_LDS_BANK_CONFLICT"] / (256 * gui) if gui and v["SQ_LDS_BANK_CONFLICT"] is not None else None
+        out.append("%s | %.0f | %.4g | %.4g | %.4g | %.4g | %.4g | %.1f | %s | %s | %s" % (
+            label, v["SQ_WAVES"], v["SQ_INSTS_VALU"], v["SQ_INSTS_SALU"], v["SQ_INSTS_LDS"], v["SQ_INSTS_VMEM_RD"],
+            v["SQ_INSTS_VMEM_WR"], valu_us, "%.1f" % k_us if k_us else "-",
+            "%.2f" % (valu_us / k_us) if k_us else "-", "%.2f" % conf if conf is not None else "-"))
+    with open(WL_INSTS_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(open(WL_INSTS_FILE).read())
 
 
 def workloads_once(dw, torch, si, steps):
@@ -524,6 +576,8 @@ def main():
                     help="write profiles/ summaries from rocprofv3 CSV output and exit")
     ap.add_argument("--workloads-once", type=int, metavar="K",
                     help="run every full-size workload K times (for counter runs) and exit")
+    ap.add_argument("--summarize-wl-insts", metavar="PMC_DIR",
+                    help="write the per-workload instruction summary from a --workloads-once SQ counter run")
     ap.add_argument("--summarize-wl-trace", metavar="TRACE_DIR",
                     help="write the per-workload kernel time summary from a --workloads-once trace")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -531,6 +585,9 @@ def main():
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(*args.summarize_rocprof)
+        return
+    if args.summarize_wl_insts:
+        summarize_workload_insts(args.summarize_wl_insts)
         return
     if args.summarize_wl_trace:
         summarize_workload_trace(args.summarize_wl_trace)
