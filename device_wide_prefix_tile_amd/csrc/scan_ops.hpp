@@ -170,6 +170,23 @@ struct OpMaxCount : SameCarry<MaxCount, OpMaxCount> {
     }
 };
 
+// ---------------------------------------------------------------- commutativity
+// Operators whose result does not depend on the order of the operands, bit
+// for bit: integer add/max/min, float add (exact per operation; only the
+// rounding of a longer sum depends on its association, which the float
+// tolerance already allows) and (maximum, count).  Not float max/min (the
+// earlier of +0 and -0 wins), affine maps, matrices or segmented pairs.  A
+// tile's total may then be folded lane by lane over all its rounds first.
+template <class Op> struct IsCommutative { static constexpr bool value = false; };
+template <> struct IsCommutative<OpAdd<int32_t>> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpAdd<uint32_t>> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpAdd<float>> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpMax<int32_t>> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpMax<uint32_t>> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpMin<int32_t>> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpMin<uint32_t>> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpMaxCount> { static constexpr bool value = true; };
+
 // ---------------------------------------------------------------- 2x2 matrices
 // Matrix multiplication [L7 concept 1] over uint32 (mod 2^32), the later
 // factor on the left: X_e (+) X_l = X_l * X_e, as for the affine maps, which

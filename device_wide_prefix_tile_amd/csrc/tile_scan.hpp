@@ -641,6 +641,18 @@ __device__ __forceinline__ typename Op::value_t reduce_wave(uint64_t wave_base, 
     V x[R][VEC];
     uint32_t raw_head[R];
     to_values<Op, R, VEC>(wave_base, lane, e, h4, x, raw_head);
+#ifndef DWPT_COMMUTATIVE_REDUCE
+#define DWPT_COMMUTATIVE_REDUCE 1
+#endif
+    if constexpr (DWPT_COMMUTATIVE_REDUCE && IsCommutative<Op>::value) {
+        // order-free: each lane folds all its elements, then one wavefront pass
+        V t = x[0][0];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = (r == 0 ? 1 : 0); j < VEC; ++j) t = Op::combine(t, x[r][j]);
+        return read_lane(wave_inclusive_scan(t, ident, comb), 63);
+    }
     V total = ident;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
