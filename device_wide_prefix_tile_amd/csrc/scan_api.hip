@@ -51,10 +51,10 @@ namespace {
 #define DWPT_WAIT_MC 3
 #endif
 #ifndef DWPT_ITEMS16           // 16-byte values (2x2 matrices)
-#define DWPT_ITEMS16 2
+#define DWPT_ITEMS16 4
 #endif
 #ifndef DWPT_WAIT16
-#define DWPT_WAIT16 4
+#define DWPT_WAIT16 3
 #endif
 #ifndef DWPT_ITEMS_SEG         // segmented scans (value + head flag)
 #define DWPT_ITEMS_SEG 12

@@ -838,6 +838,146 @@ struct WaveTile {
     }
 };
 
+// ------------------------------------------------------------ blocked layout
+// Operators with expensive combines (32-bit multiplies, compare-and-select
+// pairs) are scanned in a blocked layout: each lane holds R consecutive
+// 16-byte chunks of the wavefront's share instead of one chunk per round, so
+// a tile takes one wavefront scan for its total and one for the exclusive
+// lane prefixes instead of R each, and the serial in-lane scan covers all
+// ITEMS elements.  Loads and stores stay one chunk per lane and round (lanes
+// reading R consecutive chunks each were measured at 0.7-3.9 TB/s against
+// 6.1-6.5 for this order); the chunks change places through LDS, within the
+// wavefront (its LDS operations take effect in order, so no barrier).
+#ifndef DWPT_BLOCKED
+#define DWPT_BLOCKED 1
+#endif
+template <class Op> struct UseBlocked { static constexpr bool value = false; };
+#if DWPT_BLOCKED
+template <> struct UseBlocked<OpAffine> { static constexpr bool value = true; };
+template <> struct UseBlocked<OpMaxCount> { static constexpr bool value = true; };
+template <> struct UseBlocked<OpMat2> { static constexpr bool value = true; };
+#endif
+
+// LDS chunk slot of chunk c: one chunk of padding after every R, which keeps
+// both orders of access free of bank conflicts.
+template <int R>
+__device__ __forceinline__ int tr_slot(int c)
+{
+    return c + c / R;
+}
+template <int R>
+constexpr int tr_slots()
+{
+    return 64 * R + 64;
+}
+
+// In place: round-ordered chunks (chunk r of this lane is chunk r * 64 + lane
+// of the wavefront) to lane-ordered ones (chunk r is lane * R + r), or back.
+template <int R, int VEC, typename E>
+__device__ __forceinline__ void transpose_chunks(u32x4* tr, int lane, E (&e)[R][VEC], bool to_blocked)
+{
+    static_assert(sizeof(E) * VEC == 16, "16-byte chunks");
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        u32x4 v;
+        __builtin_memcpy(&v, e[r], 16);
+        tr[tr_slot<R>(to_blocked ? r * 64 + lane : lane * R + r)] = v;
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const u32x4 v = tr[tr_slot<R>(to_blocked ? lane * R + r : r * 64 + lane)];
+        __builtin_memcpy(e[r], &v, 16);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Wavefront total of a tile held in blocked order (lane-major: the lane's
+// elements are consecutive).
+template <class Op, int R, int VEC>
+__device__ __forceinline__ typename Op::value_t reduce_blocked(const typename Op::elem_t (&e)[R][VEC])
+{
+    using V = typename Op::value_t;
+    const V ident = Op::identity();
+    const auto comb = [](V a, V b) { return Op::combine(a, b); };
+    V t = make_value<Op>(e[0][0], 0u);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = (r == 0 ? 1 : 0); j < VEC; ++j) t = Op::combine(t, make_value<Op>(e[r][j], 0u));
+    return read_lane(wave_inclusive_scan(t, ident, comb), 63);
+}
+
+// Scan of a tile held in blocked order, prefix applied, back to round order
+// through LDS, stored like apply_store.
+template <class Op, bool EXCL, int R, int VEC>
+__device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
+                                                   u32x4* tr, typename Op::carry_t P,
+                                                   typename Op::value_t wave_prefix,
+                                                   const typename Op::elem_t (&e)[R][VEC])
+{
+    using E = typename Op::elem_t;
+    using V = typename Op::value_t;
+    const V ident = Op::identity();
+    const auto comb = [](V a, V b) { return Op::combine(a, b); };
+    V x[R][VEC];
+    V run = make_value<Op>(e[0][0], 0u);
+    x[0][0] = run;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = (r == 0 ? 1 : 0); j < VEC; ++j) {
+            run = Op::combine(run, make_value<Op>(e[r][j], 0u));
+            x[r][j] = run;
+        }
+    const V lane_excl = wave_shift_up(wave_inclusive_scan(run, ident, comb), ident);
+    const typename Op::prep_t pc =
+        Op::prepare(Op::combine_carry(P, Op::to_carry(Op::combine(wave_prefix, lane_excl))));
+    E y[R][VEC];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            if constexpr (EXCL) {
+                const V before = (r == 0 && j == 0) ? ident : (j == 0 ? x[r - 1][VEC - 1] : x[r][j - 1]);
+                y[r][j] = elem_of<Op>(Op::apply(pc, before));
+            } else {
+                y[r][j] = elem_of<Op>(Op::apply(pc, x[r][j]));
+            }
+        }
+    transpose_chunks<R, VEC, E>(tr, lane, y, false);
+    E* __restrict__ out = static_cast<E*>(p.out);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
+        if (vec) {
+            store_vec<E, VEC>(out + i0, y[r]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                if (i0 + j < p.n) out[i0 + j] = y[r][j];
+        }
+    }
+}
+
+// A wavefront's total of the tile in e; in the blocked layout, e is first
+// rearranged into it (in place) for the scan that follows later.
+template <class Op, int R, int VEC, bool BLK>
+__device__ __forceinline__ typename Op::value_t tile_wave_total(uint64_t wave_base, int lane, u32x4* tr,
+                                                                typename Op::elem_t (&e)[R][VEC],
+                                                                const uint32_t (&h4)[R])
+{
+    if constexpr (BLK) {
+        transpose_chunks<R, VEC, typename Op::elem_t>(tr, lane, e, true);
+        return reduce_blocked<Op, R, VEC>(e);
+    } else {
+        (void)tr;
+        return reduce_wave<Op, R, VEC>(wave_base, lane, e, h4);
+    }
+}
+
 template <class Op, bool EXCL, int BLOCK, int ITEMS, int WAIT>
 __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
 {
@@ -850,12 +990,16 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     using Slot = PipeSlot<V, C, G::ND>;
     constexpr int R = G::R, VEC = G::VEC, ND = G::ND;
     static_assert(!IsSeg<Op>::value || VEC == 4, "segmented scans use 4-byte elements");
+    constexpr bool BLK = UseBlocked<Op>::value;
+    static_assert(!BLK || !IsSeg<Op>::value, "segmented scans keep the round order");
 
     __shared__ Slot s_slot[kPipeSlots];
     __shared__ TileIdRing s_ids;
     __shared__ uint32_t s_role;
+    __shared__ u32x4 s_tr[BLK ? ND : 1][BLK ? tr_slots<R>() : 1];
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
+    u32x4* tr = BLK ? s_tr[w < ND ? w : 0] : nullptr;
     if (start_workgroup(p, s_slot, &s_ids, &s_role) == 0) {
         if (w == 0) {
             (void)resolve_stream<Op, DWPT_RESOLVE_SPAN>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
@@ -884,7 +1028,8 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
 #pragma unroll
     for (int q = 0; q < kPipeTiles; ++q)
         if (t[q].tile < p.num_tiles)
-            hand_over_slot<Op, Slot, ND>(p, t[q].tile, q, w, lane, reduce_wave<Op, R, VEC>(t[q].base, lane, e[q], h[q]),
+            hand_over_slot<Op, Slot, ND>(p, t[q].tile, q, w, lane,
+                                         tile_wave_total<Op, R, VEC, BLK>(t[q].base, lane, tr, e[q], h[q]),
                                          &s_slot[q % kPipeSlots]);
     for (uint32_t k = 0; t[0].tile < p.num_tiles; ++k) {
         constexpr int NEW = kPipeTiles - 1, PUB = kPipeWait - 1;
@@ -896,12 +1041,18 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
         if (k >= 1 && t[NEW].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], h[NEW]);
         if (k >= 2 && t[PUB].tile < p.num_tiles)
             hand_over_slot<Op, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane,
-                                         reduce_wave<Op, R, VEC>(t[PUB].base, lane, e[PUB], h[PUB]),
+                                         tile_wave_total<Op, R, VEC, BLK>(t[PUB].base, lane, tr, e[PUB], h[PUB]),
                                          &s_slot[(k + PUB) % kPipeSlots]);
 
         Slot* slot = &s_slot[k % kPipeSlots];
         wait_seq(&slot->prefix_seq, k + 1);
-        {
+        if constexpr (BLK) {
+            V wave_prefix = Op::identity();
+#pragma unroll
+            for (int q = 0; q < ND; ++q)
+                if (q < w) wave_prefix = Op::combine(wave_prefix, slot->wave_total[q]);
+            scan_store_blocked<Op, EXCL, R, VEC>(p, t[0].base, t[0].vec, lane, tr, slot->prefix, wave_prefix, e[0]);
+        } else {
             V x[R][VEC], lane_excl[R], round_carry[R + 1];
             uint32_t raw_head[R];
             to_values<Op, R, VEC>(t[0].base, lane, e[0], h[0], x, raw_head);
