@@ -57,10 +57,10 @@ namespace {
 #define DWPT_WAIT16 3
 #endif
 #ifndef DWPT_ITEMS_SEG         // segmented scans (value + head flag)
-#define DWPT_ITEMS_SEG 12
+#define DWPT_ITEMS_SEG 16
 #endif
 #ifndef DWPT_WAIT_SEG
-#define DWPT_WAIT_SEG 3
+#define DWPT_WAIT_SEG 2
 #endif
 #ifndef DWPT_ITEMS_COMPACT     // stream compaction
 #define DWPT_ITEMS_COMPACT 12

@@ -856,6 +856,12 @@ template <class Op> struct UseBlocked { static constexpr bool value = false; };
 template <> struct UseBlocked<OpAffine> { static constexpr bool value = true; };
 template <> struct UseBlocked<OpMaxCount> { static constexpr bool value = true; };
 template <> struct UseBlocked<OpMat2> { static constexpr bool value = true; };
+#ifndef DWPT_BLOCKED_SEG
+#define DWPT_BLOCKED_SEG 1
+#endif
+#if DWPT_BLOCKED_SEG
+template <class B> struct UseBlocked<OpSeg<B>> { static constexpr bool value = true; };
+#endif
 #endif
 
 // LDS chunk slot of chunk c: one chunk of padding after every R, which keeps
@@ -894,19 +900,56 @@ __device__ __forceinline__ void transpose_chunks(u32x4* tr, int lane, E (&e)[R][
     __builtin_amdgcn_wave_barrier();
 }
 
+// The same for the head-flag bytes of segmented scans (one 32-bit word per
+// chunk), in place.
+template <int R>
+__device__ __forceinline__ void transpose_words(uint32_t* trh, int lane, uint32_t (&h)[R], bool to_blocked)
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r) trh[tr_slot<R>(to_blocked ? r * 64 + lane : lane * R + r)] = h[r];
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int r = 0; r < R; ++r) h[r] = trh[tr_slot<R>(to_blocked ? lane * R + r : r * 64 + lane)];
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Head bits of the lane's chunks in blocked order (bit j of hb[r]: element j
+// of chunk lane * R + r starts a segment; element 0 of the input always does).
+template <class Op, int R, int VEC>
+__device__ __forceinline__ void heads_blocked(uint64_t wave_base, int lane, const uint32_t (&h4)[R],
+                                              uint32_t (&hb)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        uint32_t b = 0;
+        if constexpr (IsSeg<Op>::value) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) b |= ((h4[r] >> (8 * j)) & 0xFFu) ? (1u << j) : 0u;
+            if (wave_base + (uint64_t)(lane * R + r) * VEC == 0) b |= 1u;
+        }
+        hb[r] = b;
+    }
+}
+
 // Wavefront total of a tile held in blocked order (lane-major: the lane's
 // elements are consecutive).
 template <class Op, int R, int VEC>
-__device__ __forceinline__ typename Op::value_t reduce_blocked(const typename Op::elem_t (&e)[R][VEC])
+__device__ __forceinline__ typename Op::value_t reduce_blocked(uint64_t wave_base, int lane,
+                                                               const typename Op::elem_t (&e)[R][VEC],
+                                                               const uint32_t (&h4)[R])
 {
     using V = typename Op::value_t;
     const V ident = Op::identity();
     const auto comb = [](V a, V b) { return Op::combine(a, b); };
-    V t = make_value<Op>(e[0][0], 0u);
+    uint32_t hb[R];
+    heads_blocked<Op, R, VEC>(wave_base, lane, h4, hb);
+    V t = make_value<Op>(e[0][0], hb[0] & 1u);
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int j = (r == 0 ? 1 : 0); j < VEC; ++j) t = Op::combine(t, make_value<Op>(e[r][j], 0u));
+        for (int j = (r == 0 ? 1 : 0); j < VEC; ++j) t = Op::combine(t, make_value<Op>(e[r][j], (hb[r] >> j) & 1u));
     return read_lane(wave_inclusive_scan(t, ident, comb), 63);
 }
 
@@ -916,20 +959,22 @@ template <class Op, bool EXCL, int R, int VEC>
 __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
                                                    u32x4* tr, typename Op::carry_t P,
                                                    typename Op::value_t wave_prefix,
-                                                   const typename Op::elem_t (&e)[R][VEC])
+                                                   const typename Op::elem_t (&e)[R][VEC], const uint32_t (&h4)[R])
 {
     using E = typename Op::elem_t;
     using V = typename Op::value_t;
     const V ident = Op::identity();
     const auto comb = [](V a, V b) { return Op::combine(a, b); };
+    uint32_t hb[R];
+    heads_blocked<Op, R, VEC>(wave_base, lane, h4, hb);
     V x[R][VEC];
-    V run = make_value<Op>(e[0][0], 0u);
+    V run = make_value<Op>(e[0][0], hb[0] & 1u);
     x[0][0] = run;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int j = (r == 0 ? 1 : 0); j < VEC; ++j) {
-            run = Op::combine(run, make_value<Op>(e[r][j], 0u));
+            run = Op::combine(run, make_value<Op>(e[r][j], (hb[r] >> j) & 1u));
             x[r][j] = run;
         }
     const V lane_excl = wave_shift_up(wave_inclusive_scan(run, ident, comb), ident);
@@ -942,7 +987,10 @@ __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t
         for (int j = 0; j < VEC; ++j) {
             if constexpr (EXCL) {
                 const V before = (r == 0 && j == 0) ? ident : (j == 0 ? x[r - 1][VEC - 1] : x[r][j - 1]);
-                y[r][j] = elem_of<Op>(Op::apply(pc, before));
+                V v = Op::apply(pc, before);
+                if constexpr (IsSeg<Op>::value)
+                    if ((hb[r] >> j) & 1u) v = ident;
+                y[r][j] = elem_of<Op>(v);
             } else {
                 y[r][j] = elem_of<Op>(Op::apply(pc, x[r][j]));
             }
@@ -966,14 +1014,16 @@ __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t
 // rearranged into it (in place) for the scan that follows later.
 template <class Op, int R, int VEC, bool BLK>
 __device__ __forceinline__ typename Op::value_t tile_wave_total(uint64_t wave_base, int lane, u32x4* tr,
-                                                                typename Op::elem_t (&e)[R][VEC],
-                                                                const uint32_t (&h4)[R])
+                                                                uint32_t* trh, typename Op::elem_t (&e)[R][VEC],
+                                                                uint32_t (&h4)[R])
 {
     if constexpr (BLK) {
         transpose_chunks<R, VEC, typename Op::elem_t>(tr, lane, e, true);
-        return reduce_blocked<Op, R, VEC>(e);
+        if constexpr (IsSeg<Op>::value) transpose_words<R>(trh, lane, h4, true);
+        return reduce_blocked<Op, R, VEC>(wave_base, lane, e, h4);
     } else {
         (void)tr;
+        (void)trh;
         return reduce_wave<Op, R, VEC>(wave_base, lane, e, h4);
     }
 }
@@ -991,15 +1041,17 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     constexpr int R = G::R, VEC = G::VEC, ND = G::ND;
     static_assert(!IsSeg<Op>::value || VEC == 4, "segmented scans use 4-byte elements");
     constexpr bool BLK = UseBlocked<Op>::value;
-    static_assert(!BLK || !IsSeg<Op>::value, "segmented scans keep the round order");
+    constexpr bool BLKH = BLK && IsSeg<Op>::value;
 
     __shared__ Slot s_slot[kPipeSlots];
     __shared__ TileIdRing s_ids;
     __shared__ uint32_t s_role;
     __shared__ u32x4 s_tr[BLK ? ND : 1][BLK ? tr_slots<R>() : 1];
+    __shared__ uint32_t s_trh[BLKH ? ND : 1][BLKH ? tr_slots<R>() : 1];
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
     u32x4* tr = BLK ? s_tr[w < ND ? w : 0] : nullptr;
+    uint32_t* trh = BLKH ? s_trh[w < ND ? w : 0] : nullptr;
     if (start_workgroup(p, s_slot, &s_ids, &s_role) == 0) {
         if (w == 0) {
             (void)resolve_stream<Op, DWPT_RESOLVE_SPAN>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
@@ -1029,7 +1081,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     for (int q = 0; q < kPipeTiles; ++q)
         if (t[q].tile < p.num_tiles)
             hand_over_slot<Op, Slot, ND>(p, t[q].tile, q, w, lane,
-                                         tile_wave_total<Op, R, VEC, BLK>(t[q].base, lane, tr, e[q], h[q]),
+                                         tile_wave_total<Op, R, VEC, BLK>(t[q].base, lane, tr, trh, e[q], h[q]),
                                          &s_slot[q % kPipeSlots]);
     for (uint32_t k = 0; t[0].tile < p.num_tiles; ++k) {
         constexpr int NEW = kPipeTiles - 1, PUB = kPipeWait - 1;
@@ -1041,7 +1093,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
         if (k >= 1 && t[NEW].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], h[NEW]);
         if (k >= 2 && t[PUB].tile < p.num_tiles)
             hand_over_slot<Op, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane,
-                                         tile_wave_total<Op, R, VEC, BLK>(t[PUB].base, lane, tr, e[PUB], h[PUB]),
+                                         tile_wave_total<Op, R, VEC, BLK>(t[PUB].base, lane, tr, trh, e[PUB], h[PUB]),
                                          &s_slot[(k + PUB) % kPipeSlots]);
 
         Slot* slot = &s_slot[k % kPipeSlots];
@@ -1051,7 +1103,8 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
 #pragma unroll
             for (int q = 0; q < ND; ++q)
                 if (q < w) wave_prefix = Op::combine(wave_prefix, slot->wave_total[q]);
-            scan_store_blocked<Op, EXCL, R, VEC>(p, t[0].base, t[0].vec, lane, tr, slot->prefix, wave_prefix, e[0]);
+            scan_store_blocked<Op, EXCL, R, VEC>(p, t[0].base, t[0].vec, lane, tr, slot->prefix, wave_prefix, e[0],
+                                                 h[0]);
         } else {
             V x[R][VEC], lane_excl[R], round_carry[R + 1];
             uint32_t raw_head[R];

@@ -21,7 +21,9 @@ from parity_helpers import assert_equal, assert_f32_close, from_dev, to_dev
 pytestmark = pytest.mark.gpu
 
 TILE = 15 * 64 * 16   # elements per tile of plain 4-byte scans (15 data wavefronts x 64 lanes x 16)
-TILE12 = 15 * 64 * 12  # elements per tile of segmented scans and compaction
+TILE12 = 15 * 64 * 12  # elements per tile of compaction
+TILE_SEG = 15 * 64 * 16  # elements per tile of segmented scans (16 consecutive elements per lane in the
+                         # persistent kernel, 1024 per wavefront)
 TILE8 = 15 * 64 * 8   # pairs per tile of the 8-byte affine type
 SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1000, 4097, TILE8 - 1, TILE8, TILE8 + 1, TILE12 - 1, TILE12,
          TILE12 + 1, TILE - 1, TILE, TILE + 1, 3 * TILE + 17, 65536 + 1, 250001, 1000003]
@@ -187,8 +189,10 @@ HEAD_MIXES = {
     "mean5000": lambda s, n: si.segment_heads(s, n, 5000.0),
     "all": lambda s, n: np.ones(n, np.uint8),
     "first_only": lambda s, n: np.zeros(n, np.uint8),
-    "tile_starts": lambda s, n: (np.arange(n) % TILE12 == 0).astype(np.uint8) * 7,
-    "tile_ends": lambda s, n: (np.arange(n) % TILE12 == TILE12 - 1).astype(np.uint8),
+    "tile_starts": lambda s, n: (np.arange(n) % TILE_SEG == 0).astype(np.uint8) * 7,
+    "tile_ends": lambda s, n: (np.arange(n) % TILE_SEG == TILE_SEG - 1).astype(np.uint8),
+    "lane_starts": lambda s, n: (np.arange(n) % 16 == 0).astype(np.uint8),
+    "wave_ends": lambda s, n: (np.arange(n) % 1024 == 1023).astype(np.uint8),
 }
 
 
@@ -196,7 +200,8 @@ HEAD_MIXES = {
 @pytest.mark.parametrize("op", ["add", "max", "min"])
 @pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
 def test_segmented_parity(op, dt, exclusive):
-    for k, n in enumerate([1, 2, 65, TILE12 - 1, TILE12 + 1, TILE + 1, 3 * TILE12 + 17, 250001, 1000003]):
+    for k, n in enumerate([1, 2, 65, TILE12 - 1, TILE12 + 1, TILE_SEG - 1, TILE_SEG + 1, 3 * TILE_SEG + 17, 250001,
+                           1000003]):
         x = values(dt, n, 300 + k) if dt != "i32" else si.int32_pm100(300 + k, n)
         for mix, gen in HEAD_MIXES.items():
             h = gen(400 + k, n)
