@@ -1170,13 +1170,13 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
         return;
     }
 
-    const auto kept_bits = [&](const T (&e)[R][VEC], uint64_t base, uint32_t (&kept)[R]) {
+    // elements past n were loaded as the lowest value of T, which is never kept
+    const auto kept_bits = [&](const T (&e)[R][VEC], uint64_t, uint32_t (&kept)[R]) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const uint64_t i0 = base + (uint64_t)(r * 64 + lane) * VEC;
             uint32_t b = 0;
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) b |= (keep(e[r][j]) && i0 + j < p.n) ? (1u << j) : 0u;
+            for (int j = 0; j < VEC; ++j) b |= keep(e[r][j]) ? (1u << j) : 0u;
             kept[r] = b;
         }
     };
