@@ -22,13 +22,16 @@ Also reported:
   copy_probe    a plain 16-byte copy of 1 GiB with streaming hints, for the
                 achievable bandwidth of a one-read-one-write kernel.
 
---suite FILE additionally times every scan workload (int32 exclusive add at
-2^20 and 2^28, compaction, affine, segmented add, the max-scan size sweep)
-and writes one JSON line per workload to FILE.
+--suite FILE additionally times every workload (int32 exclusive add at 2^20
+and 2^28, int32 max, compaction, affine, segmented add, (maximum, count),
+2x2 matrices, CSR row offsets, radix split passes and a four-pass sort, the
+max-scan size sweep with reduce-then-scan beside it) and writes one JSON line
+per workload to FILE.
 
 --workloads-once K runs each full-size workload K times (for rocprofv3
-counter passes); --summarize-traffic and --summarize-rocprof turn rocprofv3
-CSV output into the summaries under profiles/.
+passes); --summarize-rocprof, --summarize-traffic, --summarize-wl-trace and
+--summarize-wl-insts turn rocprofv3 CSV output into the summaries under
+profiles/.
 """
 import argparse
 import hashlib
@@ -596,8 +599,8 @@ def main():
         summarize_workload_traffic(*args.summarize_traffic)
         return
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only (--gpus %d requested); "
-              "the scan is not sharded across GPUs" % args.gpus, file=sys.stderr)
+        print("bench.py: the scan runs on one GPU; --gpus %d is not supported "
+              "(the library does not shard a scan across GPUs)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
