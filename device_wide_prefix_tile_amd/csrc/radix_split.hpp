@@ -36,13 +36,20 @@
 
 namespace dwpt {
 
-constexpr int kRsBlock = 512;                  // 8 wavefronts
-constexpr int kRsItems = 16;                   // keys per lane
+#ifndef DWPT_RS_BLOCK
+#define DWPT_RS_BLOCK 512
+#endif
+#ifndef DWPT_RS_ITEMS
+#define DWPT_RS_ITEMS 16
+#endif
+constexpr int kRsBlock = DWPT_RS_BLOCK;        // threads per workgroup
+constexpr int kRsItems = DWPT_RS_ITEMS;        // keys per lane
 constexpr int kRsWaves = kRsBlock / 64;
 constexpr int kRsWaveKeys = 64 * kRsItems;     // wavefront w owns keys [w * kRsWaveKeys, ...) of the tile
 constexpr int kRsTile = kRsBlock * kRsItems;   // 8192 keys
 constexpr int kRsDigits = 256;
 static_assert(kRsBlock >= kRsDigits, "one thread per digit");
+static_assert(kRsTile == 8192, "8192-key tiles");
 
 // Number of lanes of mask m below this lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m)

@@ -30,6 +30,14 @@
 // walks all tiles in order and carries the prefix in registers instead of
 // using the status array (the small-n path: no workspace, no atomics).
 //
+// Large inputs run the persistent kernel (tile_scan_persistent): as many
+// workgroups as fit stay resident and pipeline several tiles each, a
+// resolver workgroup turns the published tile totals into prefixes in tile
+// order, and the same steps 2-7 run per tile.  There, operators with
+// expensive combines keep each lane's elements in element order ("blocked
+// lane layout", exchanged through LDS after the loads and before the
+// stores), so that a tile needs one wavefront scan instead of R.
+//
 // Compaction [L7 concept 2 "扫描的典型应用"; PMPP9 §9.6]: the predicate
 // x > 0 is evaluated in registers, the 0/1 flags are scanned the same way
 // (uint32 count), each wavefront packs its kept elements in LDS in order and
