@@ -408,3 +408,29 @@ def test_bounded_waits_report_timeout_and_recover():
         dw.scan_set_multi_tile_mode(old_mode)
         assert_f32_close(y, ref, s, "after timeout mode=%d" % mode)
         assert dw.scan_get_device_error() == 0
+
+
+@pytest.mark.parametrize("path", ["multi", "auto"])
+def test_blocked_layout_unaligned_and_in_place(path):
+    """The persistent kernel's blocked lane layout (affine, (maximum, count), 2x2 matrices,
+    segmented scans) on the element-wise path (views one element off 16-byte alignment), in
+    place, and over ragged tails."""
+    n = 3 * TILE_SEG + 4321
+    with Path(path):
+        ab = si.affine_pairs(81, n + 1)
+        y = from_dev(dw.scan_inclusive(to_dev(ab)[1:], "affine"))
+        assert_equal(y, oracle.scan_affine(ab[1:]), "unaligned affine")
+        vc = si.maxcount_pairs(82, n + 1)
+        y = from_dev(dw.scan_exclusive(to_dev(vc)[1:], "maxcount"))
+        assert_equal(y, oracle.scan_maxcount(vc[1:], exclusive=True), "unaligned maxcount")
+        x = si.int32_pm100(83, n + 1)
+        h = si.segment_heads(84, n + 1, 37.0)
+        y = from_dev(dw.segmented_scan(to_dev(x)[1:], to_dev(h)[1:], "add", exclusive=True))
+        assert_equal(y, oracle.segmented_scan("add", x[1:], h[1:], exclusive=True), "unaligned segmented")
+        m = si.mat2_elems(85, n)
+        t = to_dev(m)
+        dw.scan_inclusive(t, "mat2", out=t)
+        assert_equal(from_dev(t), oracle.scan_mat2(m), "in-place mat2")
+        t = to_dev(ab)
+        dw.scan_exclusive(t, "affine", out=t)
+        assert_equal(from_dev(t), oracle.scan_affine(ab, exclusive=True), "in-place affine")
