@@ -946,7 +946,8 @@ __device__ __forceinline__ void heads_blocked(uint64_t wave_base, int lane, cons
 template <class Op, int R, int VEC>
 __device__ __forceinline__ typename Op::value_t reduce_blocked(uint64_t wave_base, int lane,
                                                                const typename Op::elem_t (&e)[R][VEC],
-                                                               const uint32_t (&h4)[R])
+                                                               const uint32_t (&h4)[R],
+                                                               typename Op::value_t& lane_excl)
 {
     using V = typename Op::value_t;
     const V ident = Op::identity();
@@ -958,7 +959,9 @@ __device__ __forceinline__ typename Op::value_t reduce_blocked(uint64_t wave_bas
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int j = (r == 0 ? 1 : 0); j < VEC; ++j) t = Op::combine(t, make_value<Op>(e[r][j], (hb[r] >> j) & 1u));
-    return read_lane(wave_inclusive_scan(t, ident, comb), 63);
+    const V incl = wave_inclusive_scan(t, ident, comb);
+    lane_excl = wave_shift_up(incl, ident);
+    return read_lane(incl, 63);
 }
 
 // Scan of a tile held in blocked order, prefix applied, back to round order
@@ -967,7 +970,8 @@ template <class Op, bool EXCL, int R, int VEC>
 __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
                                                    u32x4* tr, typename Op::carry_t P,
                                                    typename Op::value_t wave_prefix,
-                                                   const typename Op::elem_t (&e)[R][VEC], const uint32_t (&h4)[R])
+                                                   const typename Op::elem_t (&e)[R][VEC], const uint32_t (&h4)[R],
+                                                   typename Op::value_t lane_excl, bool have_lane_excl)
 {
     using E = typename Op::elem_t;
     using V = typename Op::value_t;
@@ -985,7 +989,7 @@ __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t
             run = Op::combine(run, make_value<Op>(e[r][j], (hb[r] >> j) & 1u));
             x[r][j] = run;
         }
-    const V lane_excl = wave_shift_up(wave_inclusive_scan(run, ident, comb), ident);
+    if (!have_lane_excl) lane_excl = wave_shift_up(wave_inclusive_scan(run, ident, comb), ident);
     const typename Op::prep_t pc =
         Op::prepare(Op::combine_carry(P, Op::to_carry(Op::combine(wave_prefix, lane_excl))));
     E y[R][VEC];
@@ -1020,18 +1024,21 @@ __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t
 
 // A wavefront's total of the tile in e; in the blocked layout, e is first
 // rearranged into it (in place) for the scan that follows later.
+// (lane_excl: in the blocked layout, the fold of the lower lanes' elements,
+// kept for the scan of the tile.)
 template <class Op, int R, int VEC, bool BLK>
 __device__ __forceinline__ typename Op::value_t tile_wave_total(uint64_t wave_base, int lane, u32x4* tr,
                                                                 uint32_t* trh, typename Op::elem_t (&e)[R][VEC],
-                                                                uint32_t (&h4)[R])
+                                                                uint32_t (&h4)[R], typename Op::value_t& lane_excl)
 {
     if constexpr (BLK) {
         transpose_chunks<R, VEC, typename Op::elem_t>(tr, lane, e, true);
         if constexpr (IsSeg<Op>::value) transpose_words<R>(trh, lane, h4, true);
-        return reduce_blocked<Op, R, VEC>(wave_base, lane, e, h4);
+        return reduce_blocked<Op, R, VEC>(wave_base, lane, e, h4, lane_excl);
     } else {
         (void)tr;
         (void)trh;
+        (void)lane_excl;
         return reduce_wave<Op, R, VEC>(wave_base, lane, e, h4);
     }
 }
@@ -1078,6 +1085,11 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     // prefix, stages 1 .. WAIT-1 have their totals out, the newest loads.
     E e[kPipeTiles][R][VEC];
     uint32_t h[kPipeTiles][R];
+    // segmented scans in the blocked layout keep each stage's lane prefix from
+    // the wavefront scan of its total (for the other blocked operators the
+    // extra registers cost more than the second wavefront scan: measured)
+    constexpr bool KEEP = BLK && IsSeg<Op>::value;
+    V lx[kPipeTiles];
     WaveTile<G> t[kPipeTiles];
 #pragma unroll
     for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id(&s_ids, q), w);
@@ -1089,7 +1101,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     for (int q = 0; q < kPipeTiles; ++q)
         if (t[q].tile < p.num_tiles)
             hand_over_slot<Op, Slot, ND>(p, t[q].tile, q, w, lane,
-                                         tile_wave_total<Op, R, VEC, BLK>(t[q].base, lane, tr, trh, e[q], h[q]),
+                                         tile_wave_total<Op, R, VEC, BLK>(t[q].base, lane, tr, trh, e[q], h[q], lx[q]),
                                          &s_slot[q % kPipeSlots]);
     for (uint32_t k = 0; t[0].tile < p.num_tiles; ++k) {
         constexpr int NEW = kPipeTiles - 1, PUB = kPipeWait - 1;
@@ -1101,7 +1113,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
         if (k >= 1 && t[NEW].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], h[NEW]);
         if (k >= 2 && t[PUB].tile < p.num_tiles)
             hand_over_slot<Op, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane,
-                                         tile_wave_total<Op, R, VEC, BLK>(t[PUB].base, lane, tr, trh, e[PUB], h[PUB]),
+                                         tile_wave_total<Op, R, VEC, BLK>(t[PUB].base, lane, tr, trh, e[PUB], h[PUB], lx[PUB]),
                                          &s_slot[(k + PUB) % kPipeSlots]);
 
         Slot* slot = &s_slot[k % kPipeSlots];
@@ -1112,7 +1124,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
             for (int q = 0; q < ND; ++q)
                 if (q < w) wave_prefix = Op::combine(wave_prefix, slot->wave_total[q]);
             scan_store_blocked<Op, EXCL, R, VEC>(p, t[0].base, t[0].vec, lane, tr, slot->prefix, wave_prefix, e[0],
-                                                 h[0]);
+                                                 h[0], lx[0], KEEP);
         } else {
             V x[R][VEC], lane_excl[R], round_carry[R + 1];
             uint32_t raw_head[R];
@@ -1129,6 +1141,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
 #pragma unroll
         for (int q = 0; q + 1 < kPipeTiles; ++q) {
             t[q] = t[q + 1];
+            if constexpr (KEEP) lx[q] = lx[q + 1];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 h[q][r] = h[q + 1][r];
