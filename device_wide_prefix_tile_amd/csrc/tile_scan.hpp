@@ -569,9 +569,14 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //    waits for totals; a total is published before its workgroup waits for
 //    any later prefix; every wait is bounded by the spin limit.
 constexpr int kPipeSlots = 16;  // >= 2 * WAIT (see the ring note above)
-#ifndef DWPT_RESOLVE_SPAN
-#define DWPT_RESOLVE_SPAN 4  // tiles per lane of the resolver's window
-#endif
+// Tiles per lane of the resolver's window (64 * span tiles per poll round).
+// Measured at full size: a window of 128 tiles beat 256 for the float32 add
+// (354.5 -> 351.5 us), affine (197 -> 190) and segmented scans (227 -> 225)
+// and was even for the integer scans and compaction; the (maximum, count)
+// and matrix scans were slower with it (421 -> 460 and 252 -> 254 us).
+template <class Op> struct ResolveSpan { static constexpr int value = 2; };
+template <> struct ResolveSpan<OpMaxCount> { static constexpr int value = 4; };
+template <> struct ResolveSpan<OpMat2> { static constexpr int value = 4; };
 
 template <class V, class C, int ND>
 struct PipeSlot {
@@ -1069,7 +1074,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     uint32_t* trh = BLKH ? s_trh[w < ND ? w : 0] : nullptr;
     if (start_workgroup(p, s_slot, &s_ids, &s_role) == 0) {
         if (w == 0) {
-            (void)resolve_stream<Op, DWPT_RESOLVE_SPAN>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
+            (void)resolve_stream<Op, ResolveSpan<Op>::value>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
             if (lane == 0) retire_workgroup(p);
         }
         return;
@@ -1175,7 +1180,7 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
     const int w = threadIdx.x >> 6;
     if (start_workgroup(p, s_slot, &s_ids, &s_role) == 0) {
         if (w == 0) {
-            const uint32_t total = resolve_stream<Cnt, DWPT_RESOLVE_SPAN>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
+            const uint32_t total = resolve_stream<Cnt, ResolveSpan<Cnt>::value>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
             if (lane == 0) {
                 *p.count = total;
                 retire_workgroup(p);
