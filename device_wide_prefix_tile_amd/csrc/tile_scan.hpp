@@ -569,12 +569,14 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //    waits for totals; a total is published before its workgroup waits for
 //    any later prefix; every wait is bounded by the spin limit.
 constexpr int kPipeSlots = 16;  // >= 2 * WAIT (see the ring note above)
-// Tiles per lane of the resolver's window (64 * span tiles per poll round).
-// Measured at full size: a window of 128 tiles beat 256 for the float32 add
-// (354.5 -> 351.5 us), affine (197 -> 190) and segmented scans (227 -> 225)
-// and was even for the integer scans and compaction; the (maximum, count)
-// and matrix scans were slower with it (421 -> 460 and 252 -> 254 us).
-template <class Op> struct ResolveSpan { static constexpr int value = 2; };
+// Tiles per lane of the resolver's window (64 * span tiles per poll round),
+// as measured at full size: windows of 64 tiles against 128 and 256 —
+// float32 add 349.5 / 352 / 354.5 us, int32 exclusive add 346.8 / 349.5 /
+// 349, affine 190.2 / 191.6 / 197, compaction 332.5 / 334 / 334; segmented
+// scans 246.7 / 227.3 / 227; (maximum, count) 423 (64 and 128) / 421 (256)
+// and 2x2 matrices 254 (128) / 252 (256).
+template <class Op> struct ResolveSpan { static constexpr int value = 1; };
+template <class B> struct ResolveSpan<OpSeg<B>> { static constexpr int value = 2; };
 template <> struct ResolveSpan<OpMaxCount> { static constexpr int value = 4; };
 template <> struct ResolveSpan<OpMat2> { static constexpr int value = 4; };
 
