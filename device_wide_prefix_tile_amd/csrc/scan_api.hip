@@ -36,7 +36,7 @@ namespace {
 #define DWPT_ITEMS4 16
 #endif
 #ifndef DWPT_WAIT4
-#define DWPT_WAIT4 4
+#define DWPT_WAIT4 3
 #endif
 #ifndef DWPT_ITEMS8            // 8-byte values (affine pairs)
 #define DWPT_ITEMS8 8
