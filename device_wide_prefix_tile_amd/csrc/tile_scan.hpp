@@ -1162,6 +1162,15 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     if (w == 0 && lane == 0) retire_workgroup(p);
 }
 
+// Writes a wavefront's cnt packed elements from LDS to out[dst ...), with
+// the streaming hint (measured: 333 -> 329 us for the float32 compaction at
+// 2^28; 16-byte stores after an element-wise head gave 330).
+template <typename T>
+__device__ __forceinline__ void write_packed(T* __restrict__ out, uint64_t dst, const T* region, uint32_t cnt, int lane)
+{
+    for (uint32_t i = lane; i < cnt; i += 64) __builtin_nontemporal_store(region[i], out + dst + i);
+}
+
 template <typename T, int BLOCK, int ITEMS, int WAIT>
 __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
 {
@@ -1249,7 +1258,7 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
         for (int q = 0; q < ND; ++q)
             if (q < w) wave_prefix += slot->wave_total[q];
         const uint64_t dst = (uint64_t)slot->prefix + wave_prefix;
-        for (uint32_t i = lane; i < cnt; i += 64) out[dst + i] = region[i];
+        write_packed<T>(out, dst, region, cnt, lane);
 #pragma unroll
         for (int q = 0; q + 1 < kPipeTiles; ++q) {
             t[q] = t[q + 1];
