@@ -36,3 +36,36 @@ def test_distributions():
     assert 900 < mean_len < 1100
     ab = si.affine_pairs(4, 1000, odd_a=True)
     assert np.all(ab[:, 0] & 1)
+
+
+def test_full_range_generators():
+    n = 1 << 20
+    u = si.uint32_full(9, n)
+    assert u.dtype == np.uint32
+    assert u.min() < (1 << 20) and u.max() > 0xFFFFFFFF - (1 << 20)
+    assert abs(u.astype(np.float64).mean() / 2.0**32 - 0.5) < 0.01
+    # each of the four bytes is uniform over 0..255 (radix digits)
+    for shift in (0, 8, 16, 24):
+        counts = np.bincount((u >> np.uint32(shift)) & np.uint32(255), minlength=256)
+        assert counts.min() > 0.9 * n / 256 and counts.max() < 1.1 * n / 256
+    i = si.int32_full(9, n)
+    assert np.array_equal(i.view(np.uint32), u)  # same draws, reinterpreted
+    s = si.float32_sym(10, n)
+    assert s.min() >= -1.0 and s.max() < 1.0 and abs(s.mean()) < 0.01
+    assert np.all(s * np.float32(2.0**23) == np.round(s * np.float32(2.0**23)))  # on the 2^-23 grid
+
+
+def test_pair_and_matrix_generators():
+    n = 1 << 18
+    mc = si.maxcount_pairs(11, n, span=50)
+    assert mc.shape == (n, 2) and mc.dtype == np.int32
+    assert mc[:, 0].min() == -50 and mc[:, 0].max() == 50 and np.all(mc[:, 1] == 1)
+    mw = si.maxcount_pairs(11, n, span=50, unit_counts=False)
+    assert np.array_equal(mw[:, 0], mc[:, 0])  # the values do not depend on the count mode
+    assert len(np.unique(mw[:, 1])) > n // 2
+    m = si.mat2_elems(12, n)
+    assert m.shape == (n, 4) and m.dtype == np.uint32
+    assert np.array_equal(m.reshape(-1), si.uint32_full(12, 4 * n))
+    for seed in (11, 12):  # reproducible call to call
+        assert np.array_equal(si.maxcount_pairs(seed, 1000), si.maxcount_pairs(seed, 1000))
+    assert np.array_equal(si.mat2_elems(12, 1000), si.mat2_elems(12, 1000))
