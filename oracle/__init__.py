@@ -64,6 +64,7 @@ def _load():
         "oracle_scan_affine": [I, P, P, L],
         "oracle_scan_maxcount": [I, P, P, L],
         "oracle_scan_mat2": [I, P, P, L],
+        "oracle_scan_mat3": [I, P, P, L],
         "oracle_csr_offsets": [P, L, ctypes.c_uint32, P],
         "oracle_radix_split": [P, P, L, ctypes.c_uint32, P, P],
         "oracle_segscan_i32": [I, I, P, P, P, L],
@@ -174,6 +175,24 @@ def scan_mat2(x: np.ndarray, exclusive: bool = False) -> np.ndarray:
     y = np.empty((n, 4), np.uint32)
     lib.oracle_scan_mat2(1 if exclusive else 0, _ptr(x), _ptr(y), n)
     return y
+
+
+def scan_mat3(x: np.ndarray, exclusive: bool = False) -> np.ndarray:
+    """Scan of 3x3 uint32 matrices, shape (n, 9) (row-major) or (n, 3, 3).
+
+    Element i of an inclusive result is X_i X_{i-1} ... X_0 mod 2^32, the
+    later factor on the left; the empty product is the identity.  Returns
+    the shape it was given.
+    """
+    lib = _load()
+    x = _contig(x, np.uint32)
+    shape = x.shape
+    if not ((x.ndim == 2 and x.shape[1] == 9) or (x.ndim == 3 and x.shape[1:] == (3, 3))):
+        raise ValueError("x must have shape (n, 9) or (n, 3, 3)")
+    n = x.shape[0]
+    y = np.empty((n, 9), np.uint32)
+    lib.oracle_scan_mat3(1 if exclusive else 0, _ptr(x), _ptr(y), n)
+    return y.reshape(shape)
 
 
 def csr_offsets(rows: np.ndarray, n_rows: int) -> np.ndarray:

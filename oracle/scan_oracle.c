@@ -37,8 +37,9 @@
  *   Composite and matrix operators [L7 concept 1, operator generalisation,
  *   which names matrix multiplication and a user-defined "(maximum, number
  *   of occurrences)" operator]: (v1,c1) (+) (v2,c2) keeps the larger value
- *   and adds the counts on a tie, empty fold (INT32_MIN, 0); 2x2 matrices
- *   multiply with the later factor on the left, empty product the identity.
+ *   and adds the counts on a tie, empty fold (INT32_MIN, 0); 2x2 and 3x3
+ *   matrices multiply with the later factor on the left, empty product the
+ *   identity.
  *   CSR row offsets are the exclusive scan of the per-row entry counts.
  *   A radix-sort pass places every key by an exclusive scan of the digit
  *   counts [L7 concept 2, radix sort; PMPP9 §9.6 radix sort], keeping the
@@ -243,6 +244,33 @@ void oracle_scan_mat2(int exclusive, const uint32_t *x, uint32_t *y, int64_t n)
             y[4 * i + 2] = P[2];
             y[4 * i + 3] = P[3];
         }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Products of 3x3 uint32 matrices (row-major, 9 words per element),    */
+/* the same operator one size up: element i of an inclusive result is  */
+/* X_i * X_{i-1} * ... * X_0 mod 2^32, the later factor on the left;    */
+/* the empty product is the identity matrix.                            */
+/* ------------------------------------------------------------------ */
+void oracle_scan_mat3(int exclusive, const uint32_t *x, uint32_t *y, int64_t n)
+{
+    uint32_t P[9] = {1u, 0u, 0u, 0u, 1u, 0u, 0u, 0u, 1u};
+    for (int64_t i = 0; i < n; ++i) {
+        const uint32_t *X = x + 9 * i;
+        uint32_t Q[9];
+        if (exclusive)
+            for (int k = 0; k < 9; ++k) y[9 * i + k] = P[k];
+        /* Q = X * P: row r of X times column c of P */
+        for (int r = 0; r < 3; ++r)
+            for (int c = 0; c < 3; ++c) {
+                uint32_t acc = 0u;
+                for (int k = 0; k < 3; ++k) acc += X[3 * r + k] * P[3 * k + c];
+                Q[3 * r + c] = acc;
+            }
+        for (int k = 0; k < 9; ++k) P[k] = Q[k];
+        if (!exclusive)
+            for (int k = 0; k < 9; ++k) y[9 * i + k] = P[k];
     }
 }
 

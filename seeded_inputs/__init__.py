@@ -185,3 +185,8 @@ def maxcount_pairs(seed: int, n: int, span: int = 1000, unit_counts: bool = True
 def mat2_elems(seed: int, n: int) -> np.ndarray:
     """(n, 4) uint32: 2x2 matrices [[a, b], [c, d]] stored (a, b, c, d), entries uniform."""
     return uint32_full(seed, 4 * n).reshape(n, 4)
+
+
+def mat3_elems(seed: int, n: int) -> np.ndarray:
+    """(n, 9) uint32: 3x3 matrices stored row-major, entries uniform."""
+    return uint32_full(seed, 9 * n).reshape(n, 9)

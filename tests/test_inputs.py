@@ -69,3 +69,6 @@ def test_pair_and_matrix_generators():
     for seed in (11, 12):  # reproducible call to call
         assert np.array_equal(si.maxcount_pairs(seed, 1000), si.maxcount_pairs(seed, 1000))
     assert np.array_equal(si.mat2_elems(12, 1000), si.mat2_elems(12, 1000))
+    m3 = si.mat3_elems(19, 1000)
+    assert m3.shape == (1000, 9) and m3.dtype == np.uint32
+    assert np.array_equal(m3.reshape(-1), si.uint32_full(19, 9000))

@@ -466,6 +466,104 @@ def test_mat2_determinant_is_multiplicative():
         assert det(y[i]) == acc, i
 
 
+def _mat3_mul(x, y):
+    """3x3 product x * y mod 2^32 of two row-major 9-tuples, in Python ints."""
+    M = 2**32
+    return tuple(sum(int(x[3 * r + k]) * int(y[3 * k + c]) for k in range(3)) % M
+                 for r in range(3) for c in range(3))
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_bruteforce_mat3(exclusive):
+    rng = np.random.default_rng(15)
+    for n in (1, 2, 3, 5, 17):
+        x = rng.integers(0, 2**32, (n, 9), dtype=np.uint64).astype(np.uint32)
+        y = oracle.scan_mat3(x, exclusive=exclusive)
+        for i in range(n):
+            P = (1, 0, 0, 0, 1, 0, 0, 0, 1)
+            for k in range(i if exclusive else i + 1):
+                P = _mat3_mul(x[k], P)  # the later factor on the left
+            assert tuple(int(t) for t in y[i]) == P, i
+    assert oracle.scan_mat3(x.reshape(-1, 3, 3), exclusive=exclusive).shape == (17, 3, 3)
+
+
+def test_mat3_tribonacci_powers():
+    # every element the companion matrix T = [[1, 1, 1], [1, 0, 0], [0, 1, 0]]
+    # of s(k+3) = s(k+2) + s(k+1) + s(k): T maps (s(k+2), s(k+1), s(k)) to
+    # (s(k+3), s(k+2), s(k+1)), so column j of T^m is (s_j(m+2), s_j(m+1),
+    # s_j(m)) for the sequence s_j started from the j-th unit vector
+    # (s_j(2), s_j(1), s_j(0)) = e_j -- sequences from the recurrence alone
+    n = 400
+    x = np.tile(np.array([1, 1, 1, 1, 0, 0, 0, 1, 0], np.uint32), (n, 1))
+    y = oracle.scan_mat3(x)
+    cols = []
+    for j in range(3):
+        e = [0, 0, 0]
+        e[j] = 1
+        s = [e[2], e[1], e[0]]
+        while len(s) < n + 4:
+            s.append(s[-1] + s[-2] + s[-3])
+        cols.append(s)
+    for i in range(n):
+        m = i + 1  # inclusive element i is T^(i+1)
+        want = [cols[c][m + 2 - r] % 2**32 for r in range(3) for c in range(3)]
+        assert [int(t) for t in y[i]] == want, i
+
+
+def test_mat3_embeds_mat2():
+    # [[A, 0], [0, 1]] multiplies like A: the upper-left block of the 3x3
+    # scan must be the 2x2 scan (pinned above) and the rest stay [0, 0, 1]
+    n = 2000
+    a = si.mat2_elems(16, n)
+    x = np.zeros((n, 9), np.uint32)
+    x[:, 0], x[:, 1], x[:, 3], x[:, 4], x[:, 8] = a[:, 0], a[:, 1], a[:, 2], a[:, 3], 1
+    for exclusive in (False, True):
+        y = oracle.scan_mat3(x, exclusive=exclusive)
+        np.testing.assert_array_equal(y[:, [0, 1, 3, 4]], oracle.scan_mat2(a, exclusive=exclusive))
+        np.testing.assert_array_equal(y[:, [2, 5, 6, 7]], 0)
+        np.testing.assert_array_equal(y[:, 8], 1)
+
+
+def test_mat3_permutations_compose():
+    # permutation matrices (column j has its 1 in row p[j]) multiply like the
+    # permutations compose: X_i ... X_0 is the matrix of p_i o ... o p_0,
+    # computed here by following indices, without any matrix product
+    rng = np.random.default_rng(17)
+    n = 500
+    perms = [tuple(rng.permutation(3)) for _ in range(n)]
+    x = np.zeros((n, 9), np.uint32)
+    for i, p in enumerate(perms):
+        for j in range(3):
+            x[i, 3 * p[j] + j] = 1
+    for exclusive in (False, True):
+        y = oracle.scan_mat3(x, exclusive=exclusive)
+        comp = (0, 1, 2)
+        for i, p in enumerate(perms):
+            if not exclusive:
+                comp = tuple(p[comp[j]] for j in range(3))
+            want = np.zeros(9, np.uint32)
+            for j in range(3):
+                want[3 * comp[j] + j] = 1
+            assert np.array_equal(y[i], want), (exclusive, i)
+            if exclusive:
+                comp = tuple(p[comp[j]] for j in range(3))
+
+
+def test_mat3_determinant_is_multiplicative():
+    n = 1000
+    x = si.uint32_full(18, 9 * n).reshape(n, 9)
+    y = oracle.scan_mat3(x)
+    M = 2**32
+
+    def det(t):  # cofactor expansion along the first row
+        a, b, c, d, e, f, g, h, k = (int(v) for v in t)
+        return (a * (e * k - f * h) - b * (d * k - f * g) + c * (d * h - e * g)) % M
+    acc = 1
+    for i in range(n):
+        acc = acc * det(x[i]) % M
+        assert det(y[i]) == acc, i
+
+
 # ---------------------------------------------------------------- CSR row offsets
 # Building the CSR format is among the uses of a prefix sum listed in the
 # introduction of "CUDA编程并行前缀和扫描详解"; its row pointer array has
