@@ -24,7 +24,7 @@ Also reported:
 
 --suite FILE additionally times every workload (int32 exclusive add at 2^20
 and 2^28, int32 max, compaction, affine, segmented add, (maximum, count),
-2x2 matrices, CSR row offsets, radix split passes and a four-pass sort, the
+2x2 and 3x3 matrices, CSR row offsets, radix split passes and a four-pass sort, the
 max-scan size sweep with reduce-then-scan beside it) and writes one JSON line
 per workload to FILE.
 
@@ -94,6 +94,8 @@ WORKLOADS = [
      lambda n, kept: 16 * n),
     ("2x2 matrix product inclusive 2^25 matrices", "tile_scan_persistent<dwpt::OpMat2, false", 1 << 25,
      lambda n, kept: 32 * n),
+    ("3x3 matrix product inclusive 2^24 matrices", "tile_scan_persistent<dwpt::OpMat3, false", 1 << 24,
+     lambda n, kept: 72 * n),
     ("CSR row counts, 2^27 sorted COO row indices (indices read once)", "csr_count_kernel", 1 << 27,
      lambda n, kept: 4 * n),
     ("radix split histogram pass, 2^28 uint32 keys (keys read once)", "radix_hist_kernel", 1 << 28,
@@ -387,6 +389,11 @@ def workloads_once(dw, torch, si, steps):
     for _ in range(steps):
         dw.scan_inclusive(m, "mat2", out=ym)
     del m, ym
+    m3 = torch.from_numpy(si.mat3_elems(10, 1 << 24)).cuda()
+    ym3 = torch.empty_like(m3)
+    for _ in range(steps):
+        dw.scan_inclusive(m3, "mat3", out=ym3)
+    del m3, ym3
     nnz, n_rows = 1 << 27, 1 << 23
     rows = torch.from_numpy(np.sort(si.uint32_full(10, nnz) % n_rows).astype(np.uint32)).cuda()
     rp = torch.empty(n_rows + 1, dtype=torch.uint32, device="cuda")
@@ -514,6 +521,11 @@ def suite(dw, torch, si, out_path, steps):
     ym = torch.empty_like(m)
     rec("2x2 uint32 matrix product inclusive 2^25 matrices", 1 << 25, 32, lambda: dw.scan_inclusive(m, "mat2", out=ym))
     del m, ym
+    m3 = torch.from_numpy(si.mat3_elems(10, 1 << 24)).cuda()
+    ym3 = torch.empty_like(m3)
+    rec("3x3 uint32 matrix product inclusive 2^24 matrices", 1 << 24, 72,
+        lambda: dw.scan_inclusive(m3, "mat3", out=ym3))
+    del m3, ym3
     # CSR row offsets of 2^27 sorted COO row indices over 2^23 rows (16 per row on
     # average); per entry: the index read once, and 4 / 16 bytes of row_ptr written
     nnz, n_rows = 1 << 27, 1 << 23

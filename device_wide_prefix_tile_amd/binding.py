@@ -16,8 +16,8 @@ import torch
 from . import build as _build
 
 SCAN_OK, SCAN_ERR_INVALID, SCAN_ERR_UNSUPPORTED, SCAN_ERR_NOMEM, SCAN_ERR_HIP, SCAN_ERR_TIMEOUT = range(6)
-OPS = {"add": 0, "max": 1, "min": 2, "affine": 3, "maxcount": 4, "mat2": 5}
-SCAN_I32, SCAN_U32, SCAN_F32, SCAN_U32X2, SCAN_I32_U32, SCAN_U32X4 = range(6)
+OPS = {"add": 0, "max": 1, "min": 2, "affine": 3, "maxcount": 4, "mat2": 5, "mat3": 6}
+SCAN_I32, SCAN_U32, SCAN_F32, SCAN_U32X2, SCAN_I32_U32, SCAN_U32X4, SCAN_U32X9 = range(7)
 _DTYPES = {torch.int32: SCAN_I32, torch.uint32: SCAN_U32, torch.float32: SCAN_F32}
 
 EXPORTS = ("scan_inclusive", "scan_exclusive", "segmented_scan", "compact", "scan_status_string",
@@ -104,6 +104,11 @@ def _dtype_code(x: torch.Tensor, op: str) -> int:
         if x.dtype not in (torch.int32, torch.uint32) or x.dim() != 2 or x.shape[1] != 4:
             raise TypeError("mat2 scans take an (n, 4) uint32 tensor of [[a, b], [c, d]] as (a, b, c, d)")
         return SCAN_U32X4
+    if op == "mat3":
+        if x.dtype not in (torch.int32, torch.uint32) or not (
+                (x.dim() == 2 and x.shape[1] == 9) or (x.dim() == 3 and tuple(x.shape[1:]) == (3, 3))):
+            raise TypeError("mat3 scans take an (n, 9) or (n, 3, 3) uint32 tensor of row-major 3x3 matrices")
+        return SCAN_U32X9
     if x.dtype not in _DTYPES:
         raise TypeError("unsupported dtype %s" % x.dtype)
     return _DTYPES[x.dtype]
@@ -123,7 +128,7 @@ def _prep(x: torch.Tensor, out):
 
 def scan_inclusive(x: torch.Tensor, op: str = "add", out: torch.Tensor | None = None, stream=None):
     """out[i] = x[0] (+) ... (+) x[i]; op in add/max/min (1-D), affine or maxcount ((n, 2)
-    pairs), mat2 ((n, 4) matrices)."""
+    pairs), mat2 ((n, 4) matrices), mat3 ((n, 9) or (n, 3, 3) matrices)."""
     dt = _dtype_code(x, op)
     out = _prep(x, out)
     _check(lib().scan_inclusive(OPS[op], dt, x.data_ptr(), out.data_ptr(), x.shape[0], _stream(stream)),

@@ -56,6 +56,18 @@ namespace {
 #ifndef DWPT_WAIT16
 #define DWPT_WAIT16 3
 #endif
+#ifndef DWPT_BLOCK16
+#define DWPT_BLOCK16 DWPT_BLOCK
+#endif
+#ifndef DWPT_BLOCK36           // 36-byte values (3x3 matrices): 512 threads, so 256 registers per lane
+#define DWPT_BLOCK36 512
+#endif
+#ifndef DWPT_ITEMS36
+#define DWPT_ITEMS36 8
+#endif
+#ifndef DWPT_WAIT36
+#define DWPT_WAIT36 1
+#endif
 #ifndef DWPT_ITEMS_SEG         // segmented scans (value + head flag)
 #define DWPT_ITEMS_SEG 16
 #endif
@@ -71,17 +83,19 @@ namespace {
 template <class Op>
 struct Shape {
     static constexpr bool SEG = IsSeg<Op>::value, WIDE = sizeof(typename Op::elem_t) == 8,
-                          WIDE16 = sizeof(typename Op::elem_t) == 16;
-    static constexpr int BLOCK = DWPT_BLOCK;
+                          WIDE16 = sizeof(typename Op::elem_t) == 16, WIDE36 = sizeof(typename Op::elem_t) == 36;
+    static constexpr int BLOCK = WIDE36 ? DWPT_BLOCK36 : WIDE16 ? DWPT_BLOCK16 : DWPT_BLOCK;
     static constexpr bool MC = std::is_same<Op, OpMaxCount>::value;
     static constexpr int ITEMS = SEG      ? DWPT_ITEMS_SEG
                                  : MC     ? DWPT_ITEMS_MC
+                                 : WIDE36 ? DWPT_ITEMS36
                                  : WIDE16 ? DWPT_ITEMS16
                                  : WIDE   ? DWPT_ITEMS8
                                           : DWPT_ITEMS4;
     static constexpr int TILE = Geometry<Op, BLOCK, ITEMS>::TILE;
     static constexpr int WAIT = SEG      ? DWPT_WAIT_SEG
                                 : MC     ? DWPT_WAIT_MC
+                                : WIDE36 ? DWPT_WAIT36
                                 : WIDE16 ? DWPT_WAIT16
                                 : WIDE   ? DWPT_WAIT8
                                          : DWPT_WAIT4;
@@ -375,6 +389,7 @@ Runner plain_runner(int op, int dt)
     if (op == SCAN_OP_AFFINE && dt == SCAN_U32X2) return run_scan<OpAffine, EXCL>;
     if (op == SCAN_OP_MAX_COUNT && dt == SCAN_I32_U32) return run_scan<OpMaxCount, EXCL>;
     if (op == SCAN_OP_MAT2 && dt == SCAN_U32X4) return run_scan<OpMat2, EXCL>;
+    if (op == SCAN_OP_MAT3 && dt == SCAN_U32X9) return run_scan<OpMat3, EXCL>;
     return nullptr;
 }
 
@@ -392,16 +407,21 @@ Runner seg_runner(int op, int dt)
     return table[op][dt];
 }
 
-// Element size, which is also the alignment an array of the type needs.
+// Element size in bytes.
 size_t elem_size(int dt)
 {
     switch (dt) {
         case SCAN_U32X2:
         case SCAN_I32_U32: return 8;
         case SCAN_U32X4: return 16;
+        case SCAN_U32X9: return 36;
         default: return 4;
     }
 }
+
+// Alignment an array of the type needs: its size, except 4 bytes for the
+// 36-byte matrices (arrays of uint32).
+size_t elem_align(int dt) { return dt == SCAN_U32X9 ? 4 : elem_size(dt); }
 
 bool ranges_partially_overlap(const void* a, const void* b, size_t bytes_a, size_t bytes_b)
 {
@@ -413,13 +433,13 @@ bool ranges_partially_overlap(const void* a, const void* b, size_t bytes_a, size
 scan_status_t plain_scan(bool excl, scan_op_t op, scan_dtype_t dt, const void* in, void* out, size_t n,
                          void* stream)
 {
-    if ((unsigned)op > SCAN_OP_MAT2 || (unsigned)dt > SCAN_U32X4) return SCAN_ERR_UNSUPPORTED;
+    if ((unsigned)op > SCAN_OP_MAT3 || (unsigned)dt > SCAN_U32X9) return SCAN_ERR_UNSUPPORTED;
     const Runner r = excl ? plain_runner<true>(op, dt) : plain_runner<false>(op, dt);
     if (!r) return SCAN_ERR_UNSUPPORTED;
     if (n == 0) return SCAN_OK;
     const size_t es = elem_size(dt);
     if (!in || !out) return SCAN_ERR_INVALID;
-    if (!is_aligned(in, es) || !is_aligned(out, es)) return SCAN_ERR_INVALID;
+    if (!is_aligned(in, elem_align(dt)) || !is_aligned(out, elem_align(dt))) return SCAN_ERR_INVALID;
     if (n > ((size_t)1 << 40)) return SCAN_ERR_INVALID;
     if (ranges_partially_overlap(in, out, n * es, n * es)) return SCAN_ERR_INVALID;
     const Call c{in, out, nullptr, nullptr, n, static_cast<hipStream_t>(stream)};

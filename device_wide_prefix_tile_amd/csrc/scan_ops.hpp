@@ -37,6 +37,9 @@ struct MaxCount {
 struct Mat2 {
     uint32_t a, b, c, d;  // [[a, b], [c, d]], row-major
 };
+struct Mat3 {
+    uint32_t m[9];  // row-major: m[3 * r + c] is row r, column c
+};
 
 // ---------------------------------------------------------------- helpers
 template <typename V>
@@ -196,6 +199,23 @@ struct OpMat2 : SameCarry<Mat2, OpMat2> {
     __device__ __forceinline__ static Mat2 combine(Mat2 e, Mat2 l)
     {
         return {l.a * e.a + l.b * e.c, l.a * e.b + l.b * e.d, l.c * e.a + l.d * e.c, l.c * e.b + l.d * e.d};
+    }
+};
+
+// ---------------------------------------------------------------- 3x3 matrices
+// The same product one size up: X_e (+) X_l = X_l * X_e mod 2^32, 27
+// multiplies per combine.  Identity: the identity matrix.
+struct OpMat3 : SameCarry<Mat3, OpMat3> {
+    __device__ __forceinline__ static Mat3 identity() { return {{1u, 0u, 0u, 0u, 1u, 0u, 0u, 0u, 1u}}; }
+    __device__ __forceinline__ static Mat3 combine(Mat3 e, Mat3 l)
+    {
+        Mat3 r;
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                r.m[3 * i + j] = l.m[3 * i] * e.m[j] + l.m[3 * i + 1] * e.m[3 + j] + l.m[3 * i + 2] * e.m[6 + j];
+        return r;
     }
 };
 

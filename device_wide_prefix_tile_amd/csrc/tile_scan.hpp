@@ -103,27 +103,39 @@ __device__ __forceinline__ bool resets(typename Op::value_t v)
 #define DWPT_STATIC_TILES 0  // 1: tile number = workgroup index instead of a counter
 #endif
 
+// One lane's VEC consecutive elements: one 16-byte access, or K of them for
+// elements that do not divide 16 bytes (3x3 matrices: 4 x 36 bytes = K = 9).
 template <typename E, int VEC>
 __device__ __forceinline__ void load_vec(const E* p, E (&e)[VEC])
 {
-    static_assert(sizeof(E) * VEC == 16, "16-byte vector");
+    constexpr int K = (int)sizeof(E) * VEC / 16;
+    static_assert(sizeof(E) * VEC % 16 == 0, "whole 16-byte chunks");
+    u32x4 v[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
 #if DWPT_NT_LOADS
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        v[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + k);
 #else
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        v[k] = reinterpret_cast<const u32x4*>(p)[k];
 #endif
-    __builtin_memcpy(e, &v, 16);
+    }
+    __builtin_memcpy(e, v, 16 * K);
 }
 template <typename E, int VEC>
 __device__ __forceinline__ void store_vec(E* p, const E (&e)[VEC])
 {
-    u32x4 v;
-    __builtin_memcpy(&v, e, 16);
+    constexpr int K = (int)sizeof(E) * VEC / 16;
+    static_assert(sizeof(E) * VEC % 16 == 0, "whole 16-byte chunks");
+    u32x4 v[K];
+    __builtin_memcpy(v, e, 16 * K);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
 #if DWPT_NT_STORES
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+        __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4*>(p) + k);
 #else
-    *reinterpret_cast<u32x4*>(p) = v;
+        reinterpret_cast<u32x4*>(p)[k] = v[k];
 #endif
+    }
 }
 
 // Tile number of this workgroup: taken from a counter in the order
@@ -150,10 +162,22 @@ __device__ __forceinline__ uint32_t take_tile(const ScanParams& p, uint32_t* s_t
 // Tile geometry: ND data wavefronts of 64 lanes, each lane holding R rounds
 // of VEC consecutive elements (ITEMS = R * VEC per lane); the last wavefront
 // of the workgroup does the look-back.
+// Elements per lane and round: one 16-byte chunk's worth, or for elements
+// larger than 16 bytes the fewest that fill whole chunks (K of them).
+template <typename E>
+struct VecShape {
+    static constexpr int VEC = sizeof(E) <= 16 ? 16 / (int)sizeof(E) : sizeof(E) % 16 == 0 ? 1
+                               : sizeof(E) % 8 == 0                  ? 2
+                                                                     : 4;
+    static constexpr int K = (int)sizeof(E) * VEC / 16;
+    static_assert(sizeof(E) % 4 == 0 && sizeof(E) * VEC % 16 == 0, "whole 16-byte chunks");
+};
+
 template <class Op, int BLOCK, int ITEMS>
 struct Geometry {
     using E = typename Op::elem_t;
-    static constexpr int VEC = 16 / (int)sizeof(E);
+    static constexpr int VEC = VecShape<E>::VEC;
+    static constexpr int K = VecShape<E>::K;  // 16-byte chunks per round and lane
     static constexpr int R = ITEMS / VEC;
     static constexpr int NW = BLOCK / 64;
     static constexpr int ND = NW - 1;
@@ -579,6 +603,10 @@ template <class Op> struct ResolveSpan { static constexpr int value = 1; };
 template <class B> struct ResolveSpan<OpSeg<B>> { static constexpr int value = 2; };
 template <> struct ResolveSpan<OpMaxCount> { static constexpr int value = 4; };
 template <> struct ResolveSpan<OpMat2> { static constexpr int value = 4; };
+#ifndef DWPT_RESOLVE_SPAN36
+#define DWPT_RESOLVE_SPAN36 2
+#endif
+template <> struct ResolveSpan<OpMat3> { static constexpr int value = DWPT_RESOLVE_SPAN36; };
 
 template <class V, class C, int ND>
 struct PipeSlot {
@@ -598,6 +626,11 @@ __device__ __forceinline__ typename Op::elem_t elem_identity()
 // Issues one wavefront's loads of a tile into raw registers (the data is not
 // used here, so nothing waits for it).  Out-of-range elements read as the
 // identity; h4[r] holds the head-flag bytes of round r.
+// Elements wider than 16 bytes (K > 1 chunks per round) are only scanned in
+// the blocked layout, and load their chunks round by round instead: chunk c
+// of the lane is chunk c * 64 + lane of the wavefront's share (one 16-byte
+// access per lane and round, like every other type), and the share's tail
+// past n reads as identity words.
 template <class Op, int R, int VEC>
 __device__ __forceinline__ void issue_loads(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
                                             typename Op::elem_t (&e)[R][VEC], uint32_t (&h4)[R])
@@ -605,6 +638,42 @@ __device__ __forceinline__ void issue_loads(const ScanParams& p, uint64_t wave_b
     using E = typename Op::elem_t;
     constexpr bool SEG = IsSeg<Op>::value;
     const E* __restrict__ in = static_cast<const E*>(p.in);
+    constexpr int K = VecShape<E>::K;
+    if constexpr (K > 1) {
+        static_assert(!SEG, "wide elements are not segmented");
+        constexpr int C = R * K, W = (int)sizeof(E) / 4;
+        u32x4 v[C];
+        const uint32_t* __restrict__ src = static_cast<const uint32_t*>(p.in) + wave_base * W;
+        if (vec) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+#if DWPT_NT_LOADS
+                v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + c * 64 + lane);
+#else
+                v[c] = reinterpret_cast<const u32x4*>(src)[c * 64 + lane];
+#endif
+            }
+        } else {
+            uint32_t id[W];
+            to_words(elem_identity<Op>(), id);
+            const uint64_t words_in = wave_base < p.n ? (p.n - wave_base) * W : 0;  // words of the share below n
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t wq = (uint32_t)((c * 64 + lane) * 4 + q);
+                    uint32_t x = id[0];
+#pragma unroll
+                    for (int t = 1; t < W; ++t)
+                        if (wq % W == (uint32_t)t) x = id[t];
+                    v[c][q] = wq < words_in ? src[wq] : x;
+                }
+        }
+        __builtin_memcpy(e, v, 16 * C);
+#pragma unroll
+        for (int r = 0; r < R; ++r) h4[r] = 0;
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
@@ -878,6 +947,7 @@ template <> struct UseBlocked<OpMat2> { static constexpr bool value = true; };
 template <class B> struct UseBlocked<OpSeg<B>> { static constexpr bool value = true; };
 #endif
 #endif
+template <> struct UseBlocked<OpMat3> { static constexpr bool value = true; };  // always (wide elements)
 
 // LDS chunk slot of chunk c: one chunk of padding after every R, which keeps
 // both orders of access free of bank conflicts.
@@ -892,25 +962,23 @@ constexpr int tr_slots()
     return 64 * R + 64;
 }
 
-// In place: round-ordered chunks (chunk r of this lane is chunk r * 64 + lane
-// of the wavefront) to lane-ordered ones (chunk r is lane * R + r), or back.
+// In place: round-ordered chunks (chunk c of this lane is chunk c * 64 + lane
+// of the wavefront) to lane-ordered ones (chunk c is lane * C + c), or back;
+// C = R chunks, or R * K for elements wider than 16 bytes.
 template <int R, int VEC, typename E>
 __device__ __forceinline__ void transpose_chunks(u32x4* tr, int lane, E (&e)[R][VEC], bool to_blocked)
 {
-    static_assert(sizeof(E) * VEC == 16, "16-byte chunks");
+    static_assert(sizeof(E) * VEC % 16 == 0, "16-byte chunks");
+    constexpr int C = R * (int)(sizeof(E) * VEC / 16);
+    u32x4 v[C];
+    __builtin_memcpy(v, e, 16 * C);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        u32x4 v;
-        __builtin_memcpy(&v, e[r], 16);
-        tr[tr_slot<R>(to_blocked ? r * 64 + lane : lane * R + r)] = v;
-    }
+    for (int c = 0; c < C; ++c) tr[tr_slot<C>(to_blocked ? c * 64 + lane : lane * C + c)] = v[c];
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const u32x4 v = tr[tr_slot<R>(to_blocked ? lane * R + r : r * 64 + lane)];
-        __builtin_memcpy(e[r], &v, 16);
-    }
+    for (int c = 0; c < C; ++c) v[c] = tr[tr_slot<C>(to_blocked ? lane * C + c : c * 64 + lane)];
+    __builtin_memcpy(e, v, 16 * C);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_wave_barrier();
 }
@@ -1015,6 +1083,33 @@ __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t
             }
         }
     transpose_chunks<R, VEC, E>(tr, lane, y, false);
+    constexpr int K = VecShape<E>::K;
+    if constexpr (K > 1) {  // chunk c goes to chunk c * 64 + lane of the share (see issue_loads)
+        constexpr int C = R * K, W = (int)sizeof(E) / 4;
+        u32x4 v[C];
+        __builtin_memcpy(v, y, 16 * C);
+        uint32_t* __restrict__ dst = static_cast<uint32_t*>(p.out) + wave_base * W;
+        if (vec) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+#if DWPT_NT_STORES
+                __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4*>(dst) + c * 64 + lane);
+#else
+                reinterpret_cast<u32x4*>(dst)[c * 64 + lane] = v[c];
+#endif
+            }
+        } else {
+            const uint64_t words_in = wave_base < p.n ? (p.n - wave_base) * W : 0;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t wq = (uint32_t)((c * 64 + lane) * 4 + q);
+                    if (wq < words_in) dst[wq] = v[c][q];
+                }
+        }
+        return;
+    }
     E* __restrict__ out = static_cast<E*>(p.out);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -1064,11 +1159,12 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     static_assert(!IsSeg<Op>::value || VEC == 4, "segmented scans use 4-byte elements");
     constexpr bool BLK = UseBlocked<Op>::value;
     constexpr bool BLKH = BLK && IsSeg<Op>::value;
+    static_assert(G::K == 1 || BLK, "elements wider than 16 bytes use the blocked layout");
 
     __shared__ Slot s_slot[kPipeSlots];
     __shared__ TileIdRing s_ids;
     __shared__ uint32_t s_role;
-    __shared__ u32x4 s_tr[BLK ? ND : 1][BLK ? tr_slots<R>() : 1];
+    __shared__ u32x4 s_tr[BLK ? ND : 1][BLK ? tr_slots<R * G::K>() : 1];
     __shared__ uint32_t s_trh[BLKH ? ND : 1][BLKH ? tr_slots<R>() : 1];
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;

@@ -17,8 +17,10 @@
  *     results (and device-side errors, see scan_get_device_error) are visible
  *     after the stream is synchronised.
  *   - n is an element count (pairs for the U32X2 and I32_U32 dtypes,
- *     matrices for U32X4).  n == 0 returns SCAN_OK and launches nothing.
- *   - Pointers must be aligned to the element size; 16-byte alignment selects
+ *     matrices for U32X4 and U32X9).  n == 0 returns SCAN_OK and launches
+ *     nothing.
+ *   - Pointers must be aligned to the element size (4 bytes for the 36-byte
+ *     U32X9 matrices, which are arrays of uint32); 16-byte alignment selects
  *     the vector path, anything else a slower scalar path with the same
  *     results.  `out` may equal `in` (in-place); partial overlap is rejected.
  *   - Errors are returned, never raised: argument errors (null pointer with
@@ -28,7 +30,7 @@
  *     SCAN_ERR_HIP (hipGetLastError has the HIP code); failure to get
  *     workspace memory gives SCAN_ERR_NOMEM.
  *   - Workspace: the multi-tile path keeps a status array (17 eight-byte
- *     words per tile of 1920-15360 elements for each 4 bytes of carry) and
+ *     words per tile of 3584-15360 elements for each 4 bytes of carry) and
  *     three counters per (device, stream); reduce-then-scan and the radix
  *     pass add a plain buffer each (the tile carries; 256 uint32 counts per
  *     8192-key tile).  Each is allocated on first use, grown when needed
@@ -43,7 +45,8 @@
  * Valid combinations:
  *   scan_inclusive / scan_exclusive: ADD, MAX, MIN with I32, U32, F32;
  *                                    AFFINE with U32X2; MAX_COUNT with
- *                                    I32_U32; MAT2 with U32X4.
+ *                                    I32_U32; MAT2 with U32X4; MAT3 with
+ *                                    U32X9.
  *   segmented_scan:                  ADD, MAX, MIN with I32, U32, F32.
  *   compact:                         I32, U32, F32.
  * Integer ADD wraps modulo 2^32.  F32 ADD results may differ from an exact
@@ -76,7 +79,8 @@ typedef enum {
     SCAN_OP_MIN = 2,
     SCAN_OP_AFFINE = 3,    /* x -> a*x + b maps composed, later map applied after */
     SCAN_OP_MAX_COUNT = 4, /* (maximum, number of occurrences) composite */
-    SCAN_OP_MAT2 = 5       /* 2x2 matrix product, later factor on the left */
+    SCAN_OP_MAT2 = 5,      /* 2x2 matrix product, later factor on the left */
+    SCAN_OP_MAT3 = 6       /* 3x3 matrix product, later factor on the left */
 } scan_op_t;
 
 typedef enum {
@@ -85,7 +89,8 @@ typedef enum {
     SCAN_F32 = 2,
     SCAN_U32X2 = 3,   /* (a, b) pairs of uint32, 8 bytes per element */
     SCAN_I32_U32 = 4, /* (int32 value, uint32 count) pairs, 8 bytes per element */
-    SCAN_U32X4 = 5    /* 2x2 uint32 matrices [[a, b], [c, d]] stored a, b, c, d: 16 bytes */
+    SCAN_U32X4 = 5,   /* 2x2 uint32 matrices [[a, b], [c, d]] stored a, b, c, d: 16 bytes */
+    SCAN_U32X9 = 6    /* 3x3 uint32 matrices stored row-major: 36 bytes, 4-byte aligned */
 } scan_dtype_t;
 
 /*
@@ -100,8 +105,9 @@ typedef enum {
  * MAX_COUNT and MAT2 are the composite and matrix operators [L7 concept 1,
  * operator generalisation]: (v1,c1) (+) (v2,c2) keeps the larger value and,
  * on a tie, adds the counts (mod 2^32) -- fed (x_i, 1) it gives the maximum
- * so far and how often it occurred; MAT2 multiplies 2x2 matrices mod 2^32
- * with the later factor on the left (affine maps are [[a, b], [0, 1]]).
+ * so far and how often it occurred; MAT2 and MAT3 multiply 2x2 and 3x3
+ * matrices mod 2^32 with the later factor on the left (affine maps are
+ * [[a, b], [0, 1]]; 2x2 matrices A are the 3x3 [[A, 0], [0, 1]]).
  */
 scan_status_t scan_inclusive(scan_op_t op, scan_dtype_t dtype, const void* in, void* out,
                              size_t n, void* stream);
@@ -110,7 +116,8 @@ scan_status_t scan_inclusive(scan_op_t op, scan_dtype_t dtype, const void* in, v
  * Exclusive scan: out[0] = identity, out[i] = in[0] (+) ... (+) in[i-1].
  * [L7 concept 1; PMPP9 §9.1 (identity table); YLY §2.2]  Identities: ADD 0,
  * MAX the type's lowest value (-inf for F32), MIN its highest (+inf),
- * AFFINE (1, 0), MAX_COUNT (INT32_MIN, 0), MAT2 the identity matrix.
+ * AFFINE (1, 0), MAX_COUNT (INT32_MIN, 0), MAT2 and MAT3 the identity
+ * matrix.
  */
 scan_status_t scan_exclusive(scan_op_t op, scan_dtype_t dtype, const void* in, void* out,
                              size_t n, void* stream);

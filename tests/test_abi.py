@@ -76,6 +76,18 @@ def test_argument_checks_before_any_launch():
     assert L.scan_inclusive(6, MAT, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
     assert L.scan_inclusive(MAT2, 6, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
     assert L.segmented_scan(MC, MCPAIR, 1024, 4096, 2048, 10, 0, None) == binding.SCAN_ERR_UNSUPPORTED
+    MAT3, MAT9 = 6, 6
+    assert L.scan_inclusive(MAT3, MAT, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(MAT2, MAT9, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(ADD, MAT9, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(7, MAT9, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(MAT3, 7, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.segmented_scan(MAT3, MAT9, 1024, 4096, 2048, 10, 0, None) == binding.SCAN_ERR_UNSUPPORTED
+    # 3x3 matrices are arrays of uint32: 4-byte alignment suffices, 2 does not;
+    # partial overlap is measured in 36-byte elements
+    assert L.scan_inclusive(MAT3, MAT9, 1026, 8192, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.scan_inclusive(MAT3, MAT9, 1024, 8194, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.scan_inclusive(MAT3, MAT9, 1024, 1024 + 36 * 9, 10, None) == binding.SCAN_ERR_INVALID
     # a 2x2 matrix is one 16-byte vector: 16-byte alignment; a pair needs 8
     assert L.scan_inclusive(MAT2, MAT, 1032, 8192, 10, None) == binding.SCAN_ERR_INVALID
     assert L.scan_inclusive(MAT2, MAT, 1024, 8200, 10, None) == binding.SCAN_ERR_INVALID

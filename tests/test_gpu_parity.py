@@ -182,6 +182,78 @@ def test_mat2_special_cases():
     assert_equal(np.ascontiguousarray(y[:, :2]), from_dev(dw.scan_inclusive(to_dev(ab), "affine")), "mat2 vs affine")
 
 
+TILE_M3 = 7 * 64 * 8   # 3x3 matrices per tile (512-thread workgroups: 7 data wavefronts x 64 lanes x 8)
+MAT3_SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 767, 768, 769, TILE_M3 - 1, TILE_M3, TILE_M3 + 1,
+              3 * TILE_M3 + 17, 5000, 65537, 250001]
+
+
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_mat3_parity(exclusive):
+    fn = dw.scan_exclusive if exclusive else dw.scan_inclusive
+    for k, n in enumerate(MAT3_SIZES):
+        x = si.mat3_elems(750 + k, n)
+        ref = oracle.scan_mat3(x, exclusive=exclusive)
+        for path in paths_for(n):
+            with Path(path):
+                y = from_dev(fn(to_dev(x), "mat3"))
+            assert_equal(y, ref, "mat3 excl=%s n=%d path=%s" % (exclusive, n, path))
+
+
+def test_mat3_special_cases():
+    n = 9 * TILE_M3 + 5
+    # powers of the tribonacci companion matrix
+    x = np.tile(np.array([1, 1, 1, 1, 0, 0, 0, 1, 0], np.uint32), (n, 1))
+    for path in ("multi", "fallback", "rts"):
+        with Path(path):
+            assert_equal(from_dev(dw.scan_inclusive(to_dev(x), "mat3")), oracle.scan_mat3(x), "tribonacci " + path)
+    # 2x2 matrices A as [[A, 0], [0, 1]]: the upper-left block is the 2x2 scan
+    a = si.mat2_elems(96, n)
+    m = np.zeros((n, 9), np.uint32)
+    m[:, 0], m[:, 1], m[:, 3], m[:, 4], m[:, 8] = a[:, 0], a[:, 1], a[:, 2], a[:, 3], 1
+    y = from_dev(dw.scan_exclusive(to_dev(m), "mat3"))
+    assert_equal(np.ascontiguousarray(y[:, [0, 1, 3, 4]]), from_dev(dw.scan_exclusive(to_dev(a), "mat2")),
+                 "mat3 vs mat2")
+    # (n, 3, 3) tensors are accepted as they are
+    x3 = si.mat3_elems(97, 3000).reshape(-1, 3, 3)
+    assert_equal(from_dev(dw.scan_inclusive(to_dev(x3), "mat3")), oracle.scan_mat3(x3), "(n, 3, 3)")
+
+
+@pytest.mark.parametrize("path", ["auto", "multi", "fallback", "rts"])
+def test_mat3_unaligned_and_in_place(path):
+    """Views 4 bytes off 16-byte alignment take the word-wise path; in place is allowed."""
+    for k, n in enumerate([1, 769, 3 * TILE_M3 + 17, 250001]):
+        flat = si.mat3_elems(760 + k, n + 1).reshape(-1)
+        x = flat[1:1 + 9 * n].reshape(n, 9)  # the matrices that start one word in
+        ref = oracle.scan_mat3(x)
+        with Path(path):
+            xd = to_dev(flat)[1:1 + 9 * n].view(n, 9)  # 4 bytes off 16-byte alignment
+            assert xd.data_ptr() % 16 == 4
+            assert_equal(from_dev(dw.scan_inclusive(xd, "mat3")), ref, "unaligned n=%d path=%s" % (n, path))
+            dw.scan_inclusive(xd, "mat3", out=xd)
+            assert_equal(from_dev(xd), ref, "unaligned in place n=%d path=%s" % (n, path))
+            t = to_dev(x)
+            dw.scan_exclusive(t, "mat3", out=t)
+            assert_equal(from_dev(t), oracle.scan_mat3(x, exclusive=True), "in place n=%d path=%s" % (n, path))
+
+
+@pytest.mark.parametrize("op,logn", [("maxcount", 27), ("mat2", 25), ("mat3", 24)])
+def test_composite_and_matrix_full_size(op, logn):
+    """The benchmarked sizes of the composite and matrix operators, compared whole."""
+    n = 1 << logn
+    print("%s inclusive n=2^%d" % (op, logn), flush=True)
+    if op == "maxcount":
+        x, ref_fn = si.maxcount_pairs(8, n), oracle.scan_maxcount
+    elif op == "mat2":
+        x, ref_fn = si.mat2_elems(9, n), oracle.scan_mat2
+    else:
+        x, ref_fn = si.mat3_elems(10, n), oracle.scan_mat3
+    xd = to_dev(x)
+    y = from_dev(dw.scan_inclusive(xd, op))
+    assert_equal(y, ref_fn(x), "%s full size" % op)
+    del xd
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- segmented scans
 HEAD_MIXES = {
     "mean1000": lambda s, n: si.segment_heads(s, n, 1000.0),
