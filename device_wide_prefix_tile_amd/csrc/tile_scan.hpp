@@ -12,7 +12,9 @@
 //   2. load the tile with 16-byte loads: data wavefront w owns 64 * ITEMS
 //      consecutive elements, in R = ITEMS / VEC rounds of 64 * VEC elements,
 //      lane l holding VEC consecutive elements of each round, so every load
-//      instruction of a wavefront reads 1 KiB of contiguous memory;
+//      instruction of a wavefront reads 1 KiB of contiguous memory
+//      (elements wider than 16 bytes: K 16-byte loads per lane and round,
+//      which the persistent kernel issues chunk by chunk instead);
 //   3. scan each lane's VEC elements serially in registers (thread
 //      coarsening, [L7 concept 6 and its kernel-2 register array]);
 //   4. scan the lane totals across the wavefront with DPP (wave_ops.hpp);
@@ -572,11 +574,12 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //  * Pipeline.  Every data wavefront keeps WAIT + 1 of its tiles in flight
 //    as raw elements in registers: while it waits for the prefix of its
 //    oldest tile, the totals of the next WAIT - 1 are already published and
-//    the loads of the newest are on their way.  WAIT is 3 for plain 4-byte
-//    scans and compaction (measured: 430 us against 466 us at WAIT = 2 for
-//    the float32 add at 2^28; a second loading stage or WAIT = 4 gave nothing
-//    more) and 2 for the wider segmented and affine values, which would not
-//    fit in 128 registers at 3.  The in-register scan is cheap, so a tile is
+//    the loads of the newest are on their way.  WAIT is set per class of
+//    scan with the tile shape (scan_api.hip): 3 for the plain 4-byte scans
+//    (measured: 430 us against 466 us at WAIT = 2 for the float32 add at
+//    2^28), 4 for compaction, 2 for segmented scans, 1 for 3x3 matrices --
+//    the deepest pipeline the registers hold, then the fastest measured.
+//    The in-register scan is cheap, so a tile is
 //    reduced once for its total and scanned again when its prefix arrives.
 //    The last wavefront of a data workgroup only fetches the prefixes the
 //    resolver publishes, one word per tile.  Wavefront 0 asks for the next

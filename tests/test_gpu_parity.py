@@ -406,6 +406,29 @@ def test_workspace_reuse_across_calls_and_streams():
     assert dw.scan_get_device_error() == 0
 
 
+def test_concurrent_streams_share_the_gpu():
+    """Persistent launches on two streams at once, each sized for the whole GPU: the second
+    kernel's workgroups start only as the first one's retire, and neither may wait on a
+    workgroup that has not started (tile numbers go out in start order)."""
+    n = 1 << 25
+    a, b = si.int32_full(91, n), si.float32_01(92, n)
+    ra, (rb, sb) = oracle.scan("max", a), oracle.scan("add", b)
+    xa, xb = to_dev(a), to_dev(b)
+    ya, yb = torch.empty_like(xa), torch.empty_like(xb)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with Path("multi"):
+        for rep in range(4):
+            with torch.cuda.stream(s1):
+                dw.scan_inclusive(xa, "max", out=ya, stream=s1)
+            with torch.cuda.stream(s2):
+                dw.scan_inclusive(xb, "add", out=yb, stream=s2)
+        torch.cuda.synchronize()
+    assert_equal(from_dev(ya), ra, "stream 1")
+    assert_f32_close(from_dev(yb), rb, sb, "stream 2")
+    assert dw.scan_get_device_error() == 0
+
+
 def test_repeat_runs_bit_exact():
     # one passing run proves little for a protocol with races: repeat and compare
     n = (1 << 22) + 123
