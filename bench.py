@@ -24,7 +24,8 @@ Also reported:
 
 --suite FILE additionally times every workload (int32 exclusive add at 2^20
 and 2^28, int32 max, compaction, affine, segmented add, (maximum, count),
-2x2 and 3x3 matrices, CSR row offsets, radix split passes and a four-pass sort, the
+2x2 and 3x3 matrices, CSR row offsets, a 256-bin histogram, radix split passes and a
+four-pass sort, the
 max-scan size sweep with reduce-then-scan beside it) and writes one JSON line
 per workload to FILE.
 
@@ -97,6 +98,8 @@ WORKLOADS = [
     ("3x3 matrix product inclusive 2^24 matrices", "tile_scan_persistent<dwpt::OpMat3, false", 1 << 24,
      lambda n, kept: 72 * n),
     ("CSR row counts, 2^27 sorted COO row indices (indices read once)", "csr_count_kernel", 1 << 27,
+     lambda n, kept: 4 * n),
+    ("histogram counts, 2^27 uniform indices over 256 bins (indices read once)", "csr_count_lds_kernel", 1 << 27,
      lambda n, kept: 4 * n),
     ("radix split histogram pass, 2^28 uint32 keys (keys read once)", "radix_hist_kernel", 1 << 28,
      lambda n, kept: 4 * n),
@@ -400,6 +403,11 @@ def workloads_once(dw, torch, si, steps):
     for _ in range(steps):
         dw.csr_row_offsets(rows, n_rows, out=rp)
     del rows, rp
+    bins = torch.from_numpy((si.uint32_full(11, nnz) % 256).astype(np.uint32)).cuda()
+    bp = torch.empty(257, dtype=torch.uint32, device="cuda")
+    for _ in range(steps):
+        dw.csr_row_offsets(bins, 256, out=bp)
+    del bins, bp
     k = torch.from_numpy(si.uint32_full(11, 1 << 28)).cuda()
     ko = torch.empty_like(k)
     for _ in range(steps):
@@ -534,6 +542,12 @@ def suite(dw, torch, si, out_path, steps):
     rec("CSR row offsets, 2^27 sorted COO entries over 2^23 rows", nnz, 4 + 4 * (n_rows + 1) / nnz,
         lambda: dw.csr_row_offsets(rows, n_rows, out=rp))
     del rows, rp
+    # histogram bin offsets of 2^27 uniform bin indices over 256 bins (per-workgroup LDS counts)
+    bins = torch.from_numpy((si.uint32_full(11, nnz) % 256).astype(np.uint32)).cuda()
+    bp = torch.empty(257, dtype=torch.uint32, device="cuda")
+    rec("histogram bin offsets, 2^27 uniform indices over 256 bins", nnz, 4 + 4 * 257 / nnz,
+        lambda: dw.csr_row_offsets(bins, 256, out=bp))
+    del bins, bp
     # one radix-sort pass (stable split by the digit (key >> 8) & 255): algorithmic bytes are
     # one read and one write of every key (and value); the three launches move 12 B per key
     # plus the scan of 256 counts per 8192-key tile

@@ -3,8 +3,9 @@
 // of the uses of a prefix sum listed in the introduction of
 // "CUDA编程并行前缀和扫描详解"; the row pointer array has N + 1 entries
 // ("UIUC ECE 408 应用并行编程", L09).  Two steps: count the entries of every
-// row into row_ptr (csr_count_kernel, after row_ptr is zeroed), then an
-// exclusive add scan of the n_rows + 1 counts in place (the library's scan).
+// row into row_ptr (csr_count_kernel, or csr_count_lds_kernel for few rows,
+// after row_ptr is zeroed), then an exclusive add scan of the n_rows + 1
+// counts in place (the library's scan).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,15 +28,15 @@ __global__ __launch_bounds__(kCsrBlock) void zero_u32_kernel(uint32_t* p, uint64
 // entries, one entry per lane (coalesced 4-byte loads, all issued before any
 // is used).  In a window, a lane whose row differs from its left neighbour's
 // starts a run; the ballot of run starts gives each run's length, and the
-// lane that starts it adds the whole run with one atomic.  Sorted input thus
-// costs about one atomic per row and window, unsorted input one per entry at
-// worst; both count exactly.  Rows >= n_rows are skipped.
-__global__ __launch_bounds__(kCsrBlock) void csr_count_kernel(const uint32_t* __restrict__ rows, uint64_t nnz,
-                                                              uint32_t n_rows, uint32_t* counts)
+// lane that starts it adds the whole run with one add(row, length).  Sorted
+// input thus costs about one add per row and window, unsorted input one per
+// entry at worst; both count exactly.  Rows >= n_rows are skipped.
+template <int BLOCK, class Add>
+__device__ __forceinline__ void count_runs(const uint32_t* __restrict__ rows, uint64_t nnz, uint32_t n_rows, Add add)
 {
     const int lane = lane_id();
-    const uint64_t wave = (blockIdx.x * (uint64_t)kCsrBlock + threadIdx.x) >> 6;
-    const uint64_t waves = (gridDim.x * (uint64_t)kCsrBlock) >> 6;
+    const uint64_t wave = (blockIdx.x * (uint64_t)BLOCK + threadIdx.x) >> 6;
+    const uint64_t waves = (gridDim.x * (uint64_t)BLOCK) >> 6;
     constexpr uint64_t kChunk = 64 * kCsrSteps;
     for (uint64_t base = wave * kChunk; base < nnz; base += waves * kChunk) {
         uint32_t r[kCsrSteps];
@@ -52,9 +53,42 @@ __global__ __launch_bounds__(kCsrBlock) void csr_count_kernel(const uint32_t* __
             // the next run start above this lane, or the end of the window
             const uint64_t above = lane == 63 ? 0ull : starts & (~0ull << (lane + 1));
             const uint32_t len = (uint32_t)((above ? __builtin_ctzll(above) : 64) - lane);
-            if (start && r[s] < n_rows)
-                __hip_atomic_fetch_add(&counts[r[s]], len, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (start && r[s] < n_rows) add(r[s], len);
         }
+    }
+}
+
+// Any number of rows: the runs are added to the counts in memory with
+// device-wide atomics.
+__global__ __launch_bounds__(kCsrBlock) void csr_count_kernel(const uint32_t* __restrict__ rows, uint64_t nnz,
+                                                              uint32_t n_rows, uint32_t* counts)
+{
+    count_runs<kCsrBlock>(rows, nnz, n_rows, [&](uint32_t row, uint32_t len) {
+        __hip_atomic_fetch_add(&counts[row], len, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    });
+}
+
+// Up to kCsrLdsBins rows (a histogram of few bins): each workgroup counts
+// into its own copy of the counts in LDS and adds its nonzero counts to
+// memory once at the end.  With many entries per bin the device-wide
+// atomics would otherwise be one per entry for unsorted input, all on a few
+// addresses.
+constexpr uint32_t kCsrLdsBins = 4096;
+constexpr int kCsrLdsBlock = 1024;  // one workgroup per CU, 16 wavefronts
+
+__global__ __launch_bounds__(kCsrLdsBlock) void csr_count_lds_kernel(const uint32_t* __restrict__ rows, uint64_t nnz,
+                                                                     uint32_t n_rows, uint32_t* counts)
+{
+    __shared__ uint32_t s_cnt[kCsrLdsBins];
+    for (uint32_t i = threadIdx.x; i < n_rows; i += kCsrLdsBlock) s_cnt[i] = 0u;
+    __syncthreads();
+    count_runs<kCsrLdsBlock>(rows, nnz, n_rows, [&](uint32_t row, uint32_t len) {
+        __hip_atomic_fetch_add(&s_cnt[row], len, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    });
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < n_rows; i += kCsrLdsBlock) {
+        const uint32_t c = s_cnt[i];
+        if (c) __hip_atomic_fetch_add(&counts[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

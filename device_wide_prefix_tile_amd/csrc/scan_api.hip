@@ -23,12 +23,14 @@ namespace {
 
 // ------------------------------------------------------------ tile shapes
 // Workgroup size, elements per lane and pipeline depth per class of scan
-// (defaults: 1024 threads = 15 data wavefronts + 1 prefix wavefront).  ITEMS
-// sets the tile (15 * 64 * ITEMS elements); WAIT is the number of tiles per
-// data wavefront that wait on their prefix in the persistent kernel.  Each
-// class takes the deepest pipeline that fits in 128 registers without
-// spilling, and the measured best tile.  Build-time switches, so that shapes
-// can be compared by measurement.
+// (defaults: 1024 threads = 15 data wavefronts + 1 prefix wavefront; the 3x3
+// matrices take 512).  ITEMS sets the tile ((BLOCK / 64 - 1) * 64 * ITEMS
+// elements); WAIT is the number of tiles per data wavefront that wait on
+// their prefix in the persistent kernel.  Each class takes the deepest
+// pipeline that fits in the registers (128 per lane at 1024 threads), then
+// the measured best tile; the matrix classes spill some registers at their
+// fastest measured shape.  Build-time switches, so that shapes can be
+// compared by measurement.
 #ifndef DWPT_BLOCK
 #define DWPT_BLOCK 1024
 #endif
@@ -250,6 +252,23 @@ struct Call {
 };
 
 bool is_aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Compute units of the current device (cached; called with g_mu held).
+int device_cus()
+{
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1;
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+        (void)hipGetLastError();
+        cus = 1;
+    }
+    cache[dev] = cus;
+    return cus;
+}
 
 // Resident workgroups of kernel `f` on the current device (cached).
 int resident_capacity(const void* f, int block)
@@ -509,9 +528,23 @@ scan_status_t csr_row_offsets(const uint32_t* row_idx, size_t nnz, uint32_t n_ro
         hipLaunchKernelGGL(zero_u32_kernel, dim3(zgrid), dim3(kCsrBlock), 0, s, row_ptr, (uint64_t)np);
         if (nnz > 0) {
             const size_t chunks = (nnz + 64 * kCsrSteps - 1) / (64 * kCsrSteps);  // one per wavefront
-            const unsigned grid = (unsigned)std::min<size_t>((chunks + kCsrBlock / 64 - 1) / (kCsrBlock / 64), 4096);
-            hipLaunchKernelGGL(csr_count_kernel, dim3(grid), dim3(kCsrBlock), 0, s, row_idx, (uint64_t)nnz, n_rows,
-                               row_ptr);
+            if (n_rows <= kCsrLdsBins) {
+                // at most one workgroup per CU: each adds its n_rows counts to memory once
+                int cus = 1;
+                {
+                    std::lock_guard<std::mutex> lock(g_mu);
+                    cus = device_cus();
+                }
+                const unsigned grid = (unsigned)std::min<size_t>((chunks + kCsrLdsBlock / 64 - 1) / (kCsrLdsBlock / 64),
+                                                                 (size_t)cus);
+                hipLaunchKernelGGL(csr_count_lds_kernel, dim3(grid), dim3(kCsrLdsBlock), 0, s, row_idx,
+                                   (uint64_t)nnz, n_rows, row_ptr);
+            } else {
+                const unsigned grid =
+                    (unsigned)std::min<size_t>((chunks + kCsrBlock / 64 - 1) / (kCsrBlock / 64), 4096);
+                hipLaunchKernelGGL(csr_count_kernel, dim3(grid), dim3(kCsrBlock), 0, s, row_idx, (uint64_t)nnz,
+                                   n_rows, row_ptr);
+            }
         }
         if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
         // row_ptr = exclusive scan of the counts, in place

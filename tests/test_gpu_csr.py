@@ -41,6 +41,25 @@ def test_unsorted(n_rows, nnz):
     check(rows, n_rows, "unsorted n_rows=%d nnz=%d" % (n_rows, nnz))
 
 
+@pytest.mark.parametrize("n_rows", [1, 2, 16, 256, 4095, 4096, 4097])
+def test_few_bins(n_rows):
+    """Histogram offsets of few bins (at most 4096 take the per-workgroup LDS counts):
+    uniform bin indices, sorted ones, and a skewed mix with most entries in one bin."""
+    nnz = (1 << 22) + 77
+    rows = (si.uint32_full(950 + n_rows % 83, nnz) % n_rows).astype(np.uint32)
+    check(rows, n_rows, "uniform bins n_rows=%d" % n_rows)
+    check(np.sort(rows), n_rows, "sorted bins n_rows=%d" % n_rows)
+    skew = np.where(si.uint32_full(960, nnz) % 10 == 0, rows, np.uint32(n_rows - 1)).astype(np.uint32)
+    check(skew, n_rows, "skewed bins n_rows=%d" % n_rows)
+
+
+def test_few_bins_full_size():
+    """2^27 uniform indices over 256 bins, the benchmarked histogram."""
+    nnz = 1 << 27
+    rows = (si.uint32_full(11, nnz) % 256).astype(np.uint32)
+    check(rows, 256, "2^27 entries over 256 bins")
+
+
 def test_edge_cases():
     check(np.zeros(0, np.uint32), 5, "no entries")
     check(np.zeros(0, np.uint32), 0, "no rows, no entries")
