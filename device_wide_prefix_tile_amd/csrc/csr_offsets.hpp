@@ -69,17 +69,17 @@ __global__ __launch_bounds__(kCsrBlock) void csr_count_kernel(const uint32_t* __
 }
 
 // Up to kCsrLdsBins rows (a histogram of few bins): each workgroup counts
-// into its own copy of the counts in LDS and adds its nonzero counts to
-// memory once at the end.  With many entries per bin the device-wide
-// atomics would otherwise be one per entry for unsorted input, all on a few
-// addresses.
-constexpr uint32_t kCsrLdsBins = 4096;
-constexpr int kCsrLdsBlock = 1024;  // one workgroup per CU, 16 wavefronts
+// into its own copy of the counts in LDS (n_rows words of dynamic LDS) and
+// adds its nonzero counts to memory once at the end.  With many entries per
+// bin the device-wide atomics would otherwise be one per entry for unsorted
+// input, all on a few addresses; here they are at most n_rows per workgroup.
+constexpr uint32_t kCsrLdsBins = 16384;  // 64 KiB of counts
+constexpr int kCsrLdsBlock = 1024;       // one workgroup per CU, 16 wavefronts
 
 __global__ __launch_bounds__(kCsrLdsBlock) void csr_count_lds_kernel(const uint32_t* __restrict__ rows, uint64_t nnz,
                                                                      uint32_t n_rows, uint32_t* counts)
 {
-    __shared__ uint32_t s_cnt[kCsrLdsBins];
+    extern __shared__ uint32_t s_cnt[];  // n_rows words
     for (uint32_t i = threadIdx.x; i < n_rows; i += kCsrLdsBlock) s_cnt[i] = 0u;
     __syncthreads();
     count_runs<kCsrLdsBlock>(rows, nnz, n_rows, [&](uint32_t row, uint32_t len) {

@@ -537,8 +537,8 @@ scan_status_t csr_row_offsets(const uint32_t* row_idx, size_t nnz, uint32_t n_ro
                 }
                 const unsigned grid = (unsigned)std::min<size_t>((chunks + kCsrLdsBlock / 64 - 1) / (kCsrLdsBlock / 64),
                                                                  (size_t)cus);
-                hipLaunchKernelGGL(csr_count_lds_kernel, dim3(grid), dim3(kCsrLdsBlock), 0, s, row_idx,
-                                   (uint64_t)nnz, n_rows, row_ptr);
+                hipLaunchKernelGGL(csr_count_lds_kernel, dim3(grid), dim3(kCsrLdsBlock), (size_t)n_rows * 4, s,
+                                   row_idx, (uint64_t)nnz, n_rows, row_ptr);
             } else {
                 const unsigned grid =
                     (unsigned)std::min<size_t>((chunks + kCsrBlock / 64 - 1) / (kCsrBlock / 64), 4096);

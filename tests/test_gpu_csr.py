@@ -41,9 +41,9 @@ def test_unsorted(n_rows, nnz):
     check(rows, n_rows, "unsorted n_rows=%d nnz=%d" % (n_rows, nnz))
 
 
-@pytest.mark.parametrize("n_rows", [1, 2, 16, 256, 4095, 4096, 4097])
+@pytest.mark.parametrize("n_rows", [1, 2, 16, 256, 4096, 16383, 16384, 16385])
 def test_few_bins(n_rows):
-    """Histogram offsets of few bins (at most 4096 take the per-workgroup LDS counts):
+    """Histogram offsets of few bins (at most 16384 take the per-workgroup LDS counts):
     uniform bin indices, sorted ones, and a skewed mix with most entries in one bin."""
     nnz = (1 << 22) + 77
     rows = (si.uint32_full(950 + n_rows % 83, nnz) % n_rows).astype(np.uint32)
