@@ -114,15 +114,32 @@ __device__ __forceinline__ void hist_count(uint32_t* cnt, const uint32_t (&k)[kR
 }
 
 // Pass 1: hist[d * T + t] = number of keys of digit d in tile t.
+// (Counting does not depend on the keys' order, so a whole tile is read with
+// one 16-byte load per lane and four keys, when the keys are 16-byte aligned:
+// four times fewer load instructions than one key per lane.)
 __global__ __launch_bounds__(kRsBlock) void radix_hist_kernel(const uint32_t* __restrict__ keys, uint64_t n,
-                                                              uint32_t shift, uint32_t T, uint32_t* __restrict__ hist)
+                                                              uint32_t shift, uint32_t T, uint32_t* __restrict__ hist,
+                                                              int vec)
 {
     __shared__ uint32_t s_cnt[kRsDigits * kRsCopies];
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
     const uint32_t t = rs_tile(blockIdx.x, T);
     uint32_t k[kRsItems];
-    load_tile(keys, t, n, w, lane, k);
+    if (vec && (uint64_t)(t + 1) * kRsTile <= n) {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(keys + (uint64_t)t * kRsTile + (uint64_t)w * kRsWaveKeys);
+#pragma unroll
+        for (int v = 0; v < kRsItems / 4; ++v) {
+            const u32x4_t q = src[v * 64 + lane];
+            k[4 * v] = q.x;
+            k[4 * v + 1] = q.y;
+            k[4 * v + 2] = q.z;
+            k[4 * v + 3] = q.w;
+        }
+    } else {
+        load_tile(keys, t, n, w, lane, k);
+    }
     for (int i = threadIdx.x; i < kRsDigits * kRsCopies; i += kRsBlock) s_cnt[i] = 0u;
     __syncthreads();
     const uint64_t base = (uint64_t)t * kRsTile + (uint64_t)w * kRsWaveKeys;

@@ -64,6 +64,18 @@ def test_skewed_digits():
     check(np.arange(n, dtype=np.uint32)[::-1].copy() << np.uint32(24), 24, what="descending top digit")
 
 
+def test_unaligned_keys():
+    """Keys 4 bytes off 16-byte alignment (element loads in every kernel), with values."""
+    n = 6 * TILE + 321
+    keys, vals = si.uint32_full(45, n + 1), si.uint32_full(46, n + 1)
+    ref_k, ref_v = oracle.radix_split(keys[1:], 16, vals[1:])
+    kd, vd = to_dev(keys)[1:], to_dev(vals)[1:]
+    assert kd.data_ptr() % 16 == 4
+    ko, vo = dw.radix_split(kd, 16, vd)
+    assert_equal(from_dev(ko), ref_k, "unaligned keys")
+    assert_equal(from_dev(vo), ref_v, "unaligned values")
+
+
 def test_four_passes_sort():
     """Four passes with shift = 0, 8, 16, 24 sort the keys, values following (stable)."""
     n = 3 * TILE * 7 + 5
