@@ -161,9 +161,6 @@ __device__ __forceinline__ uint32_t take_tile(const ScanParams& p, uint32_t* s_t
 }
 
 // ------------------------------------------------------------------ pieces
-// Tile geometry: ND data wavefronts of 64 lanes, each lane holding R rounds
-// of VEC consecutive elements (ITEMS = R * VEC per lane); the last wavefront
-// of the workgroup does the look-back.
 // Elements per lane and round: one 16-byte chunk's worth, or for elements
 // larger than 16 bytes the fewest that fill whole chunks (K of them).
 template <typename E>
@@ -175,6 +172,9 @@ struct VecShape {
     static_assert(sizeof(E) % 4 == 0 && sizeof(E) * VEC % 16 == 0, "whole 16-byte chunks");
 };
 
+// Tile geometry: ND data wavefronts of 64 lanes, each lane holding R rounds
+// of VEC consecutive elements (ITEMS = R * VEC per lane); the last wavefront
+// of the workgroup does the look-back.
 template <class Op, int BLOCK, int ITEMS>
 struct Geometry {
     using E = typename Op::elem_t;
@@ -579,8 +579,8 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //    (measured: 430 us against 466 us at WAIT = 2 for the float32 add at
 //    2^28), 4 for compaction, 2 for segmented scans, 1 for 3x3 matrices --
 //    the deepest pipeline the registers hold, then the fastest measured.
-//    The in-register scan is cheap, so a tile is
-//    reduced once for its total and scanned again when its prefix arrives.
+//    The in-register scan is cheap, so a tile is reduced once for its total
+//    and scanned again when its prefix arrives.
 //    The last wavefront of a data workgroup only fetches the prefixes the
 //    resolver publishes, one word per tile.  Wavefront 0 asks for the next
 //    tile number one iteration before it is needed.
