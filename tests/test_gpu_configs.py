@@ -75,6 +75,25 @@ def test_config2_f32_inclusive_add_2p28():
     assert dw.scan_get_device_error() == 0
 
 
+def test_f32_add_mixed_signs_2p28():
+    """float32 add over values uniform in [-1, 1) and over N(0, 1): the running sums cancel,
+    so the tolerance, scaled by the prefix of |x|, is far above the value itself; exclusive too."""
+    n = 1 << 28
+    for name, x in (("uniform[-1,1)", si.float32_sym(7, n)), ("normal", si.float32_normal(3, n))):
+        xd = to_dev(x)
+        yi = from_dev(dw.scan_inclusive(xd, "add"))
+        ye = from_dev(dw.scan_exclusive(xd, "add"))
+        del xd
+        ref, s = oracle.scan("add", x)
+        worst = assert_f32_close(yi, ref, s, "mixed signs inclusive " + name)
+        print("%s inclusive worst error/tolerance = %.4f" % (name, worst))
+        del ref
+        ref_e, s_e = oracle.scan("add", x, exclusive=True)
+        assert_f32_close(ye, ref_e, s_e, "mixed signs exclusive " + name)
+        del yi, ye, ref_e, s_e, x
+    assert dw.scan_get_device_error() == 0
+
+
 def test_config3_compact_2p28():
     n = 1 << 28
     x = si.float32_normal(3, n)

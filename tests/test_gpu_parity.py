@@ -429,6 +429,41 @@ def test_concurrent_streams_share_the_gpu():
     assert dw.scan_get_device_error() == 0
 
 
+def test_host_threads_on_their_own_streams():
+    """Two host threads call the library at the same time, each on its own stream (the
+    library's calls release the interpreter lock): workspaces are per stream, and the
+    settings and workspace table are guarded."""
+    import threading
+    n = (1 << 24) + 999
+    a, b = si.int32_full(93, n), si.int32_0_15(94, n)
+    ra, rb = oracle.scan("max", a, exclusive=True), oracle.scan("add", b)
+    errors = []
+
+    def work(x, ref, op, excl, name):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                xd = to_dev(x)
+                yd = torch.empty_like(xd)
+                for _ in range(20):
+                    (dw.scan_exclusive if excl else dw.scan_inclusive)(xd, op, out=yd, stream=st)
+                st.synchronize()
+                if not np.array_equal(yd.cpu().numpy(), ref):
+                    errors.append(name)
+        except Exception as e:  # reported below, in the main thread
+            errors.append("%s: %r" % (name, e))
+
+    ts = [threading.Thread(target=work, args=(a, ra, "max", True, "max")),
+          threading.Thread(target=work, args=(b, rb, "add", False, "add"))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in ts), "a thread did not finish"
+    assert not errors, errors
+    assert dw.scan_get_device_error() == 0
+
+
 def test_repeat_runs_bit_exact():
     # one passing run proves little for a protocol with races: repeat and compare
     n = (1 << 22) + 123
