@@ -578,9 +578,10 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //    scan with the tile shape (scan_api.hip): 3 for the plain 4-byte scans
 //    (measured: 430 us against 466 us at WAIT = 2 for the float32 add at
 //    2^28), 4 for compaction, 2 for segmented scans, 1 for 3x3 matrices --
-//    the deepest pipeline the registers hold, then the fastest measured.
-//    The in-register scan is cheap, so a tile is reduced once for its total
-//    and scanned again when its prefix arrives.
+//    the deepest pipeline the registers hold, then the fastest measured
+//    (3x3 matrices hold their waiting tile in LDS instead; see
+//    persistent_reload_loop).  The in-register scan is cheap, so a tile is
+//    reduced once for its total and scanned again when its prefix arrives.
 //    The last wavefront of a data workgroup only fetches the prefixes the
 //    resolver publishes, one word per tile.  Wavefront 0 asks for the next
 //    tile number one iteration before it is needed.
@@ -606,6 +607,9 @@ template <class Op> struct ResolveSpan { static constexpr int value = 1; };
 template <class B> struct ResolveSpan<OpSeg<B>> { static constexpr int value = 2; };
 template <> struct ResolveSpan<OpMaxCount> { static constexpr int value = 4; };
 template <> struct ResolveSpan<OpMat2> { static constexpr int value = 4; };
+#ifndef DWPT_RELOAD36
+#define DWPT_RELOAD36 1
+#endif
 #ifndef DWPT_RESOLVE_SPAN36
 #define DWPT_RESOLVE_SPAN36 2
 #endif
@@ -1001,6 +1005,35 @@ __device__ __forceinline__ void transpose_words(uint32_t* trh, int lane, uint32_
     __builtin_amdgcn_wave_barrier();
 }
 
+// A tile's chunks in blocked order again, from the LDS area that its
+// transposition (transpose_chunks, to_blocked) filled; the wavefront's LDS
+// operations take effect in order, so no barrier.
+template <int R, int VEC, typename E>
+__device__ __forceinline__ void reload_blocked(const u32x4* tr, int lane, E (&e)[R][VEC])
+{
+    constexpr int C = R * (int)(sizeof(E) * VEC / 16);
+    u32x4 v[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) v[c] = tr[tr_slot<C>(lane * C + c)];
+    __builtin_memcpy(e, v, 16 * C);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+}
+
+// The opposite: a tile held in blocked order written back to the LDS area in
+// the same layout, so that reload_blocked finds it there.
+template <int R, int VEC, typename E>
+__device__ __forceinline__ void park_blocked(u32x4* tr, int lane, const E (&e)[R][VEC])
+{
+    constexpr int C = R * (int)(sizeof(E) * VEC / 16);
+    u32x4 v[C];
+    __builtin_memcpy(v, e, 16 * C);
+#pragma unroll
+    for (int c = 0; c < C; ++c) tr[tr_slot<C>(lane * C + c)] = v[c];
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Head bits of the lane's chunks in blocked order (bit j of hb[r]: element j
 // of chunk lane * R + r starts a segment; element 0 of the input always does).
 template <class Op, int R, int VEC>
@@ -1040,6 +1073,55 @@ __device__ __forceinline__ typename Op::value_t reduce_blocked(uint64_t wave_bas
     const V incl = wave_inclusive_scan(t, ident, comb);
     lane_excl = wave_shift_up(incl, ident);
     return read_lane(incl, 63);
+}
+
+// A scanned tile in blocked order (y, changed in place) back to round order
+// through LDS, stored like apply_store.
+template <class Op, int R, int VEC>
+__device__ __forceinline__ void store_blocked_tile(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
+                                                   u32x4* tr, typename Op::elem_t (&y)[R][VEC])
+{
+    using E = typename Op::elem_t;
+    transpose_chunks<R, VEC, E>(tr, lane, y, false);
+    constexpr int K = VecShape<E>::K;
+    if constexpr (K > 1) {  // chunk c goes to chunk c * 64 + lane of the share (see issue_loads)
+        constexpr int C = R * K, W = (int)sizeof(E) / 4;
+        u32x4 v[C];
+        __builtin_memcpy(v, y, 16 * C);
+        uint32_t* __restrict__ dst = static_cast<uint32_t*>(p.out) + wave_base * W;
+        if (vec) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+#if DWPT_NT_STORES
+                __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4*>(dst) + c * 64 + lane);
+#else
+                reinterpret_cast<u32x4*>(dst)[c * 64 + lane] = v[c];
+#endif
+            }
+        } else {
+            const uint64_t words_in = wave_base < p.n ? (p.n - wave_base) * W : 0;
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t wq = (uint32_t)((c * 64 + lane) * 4 + q);
+                    if (wq < words_in) dst[wq] = v[c][q];
+                }
+        }
+        return;
+    }
+    E* __restrict__ out = static_cast<E*>(p.out);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
+        if (vec) {
+            store_vec<E, VEC>(out + i0, y[r]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j)
+                if (i0 + j < p.n) out[i0 + j] = y[r][j];
+        }
+    }
 }
 
 // Scan of a tile held in blocked order, prefix applied, back to round order
@@ -1085,46 +1167,7 @@ __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t
                 y[r][j] = elem_of<Op>(Op::apply(pc, x[r][j]));
             }
         }
-    transpose_chunks<R, VEC, E>(tr, lane, y, false);
-    constexpr int K = VecShape<E>::K;
-    if constexpr (K > 1) {  // chunk c goes to chunk c * 64 + lane of the share (see issue_loads)
-        constexpr int C = R * K, W = (int)sizeof(E) / 4;
-        u32x4 v[C];
-        __builtin_memcpy(v, y, 16 * C);
-        uint32_t* __restrict__ dst = static_cast<uint32_t*>(p.out) + wave_base * W;
-        if (vec) {
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-#if DWPT_NT_STORES
-                __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4*>(dst) + c * 64 + lane);
-#else
-                reinterpret_cast<u32x4*>(dst)[c * 64 + lane] = v[c];
-#endif
-            }
-        } else {
-            const uint64_t words_in = wave_base < p.n ? (p.n - wave_base) * W : 0;
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t wq = (uint32_t)((c * 64 + lane) * 4 + q);
-                    if (wq < words_in) dst[wq] = v[c][q];
-                }
-        }
-        return;
-    }
-    E* __restrict__ out = static_cast<E*>(p.out);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
-        if (vec) {
-            store_vec<E, VEC>(out + i0, y[r]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < VEC; ++j)
-                if (i0 + j < p.n) out[i0 + j] = y[r][j];
-        }
-    }
+    store_blocked_tile<Op, R, VEC>(p, wave_base, vec, lane, tr, y);
 }
 
 // A wavefront's total of the tile in e; in the blocked layout, e is first
@@ -1146,6 +1189,77 @@ __device__ __forceinline__ typename Op::value_t tile_wave_total(uint64_t wave_ba
         (void)lane_excl;
         return reduce_wave<Op, R, VEC>(wave_base, lane, e, h4);
     }
+}
+
+// Elements wider than 16 bytes with one tile waiting (3x3 matrices): a
+// data wavefront holds only its newest tile in registers.  The waiting
+// tile's data stay in the wavefront's LDS transposition area from its
+// hand-over until its prefix is in, and are read back from there for the
+// scan -- instead of keeping a second tile in registers across the wait,
+// which at 72 words per tile spilled.  The first two tiles' totals are both
+// published before any wait (the second one's first, so that the LDS area
+// then holds the first tile); the second tile is written back to the area in
+// its turn.
+template <class Op> struct ReloadAfterWait { static constexpr bool value = false; };
+template <> struct ReloadAfterWait<OpMat3> { static constexpr bool value = DWPT_RELOAD36; };
+
+template <class Op, bool EXCL, class G, class Slot>
+__device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot* s_slot, TileIdRing* s_ids, u32x4* tr,
+                                                       int w, int lane, bool exhausted)
+{
+    using E = typename Op::elem_t;
+    using V = typename Op::value_t;
+    constexpr int R = G::R, VEC = G::VEC, ND = G::ND;
+    E e0[R][VEC], e1[R][VEC];  // the tile to finish (round order, until it is transposed), the next one
+    uint32_t h0[R], h1[R];
+    V lx;
+    WaveTile<G> t0, t1;
+    t0.set(p, get_id(s_ids, 0), w);
+    t1.set(p, get_id(s_ids, 1), w);
+    if (t0.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t0.base, t0.vec, lane, e0, h0);
+    if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t1.base, t1.vec, lane, e1, h1);
+    if (t1.tile < p.num_tiles)
+        hand_over_slot<Op, Slot, ND>(p, t1.tile, 1, w, lane,
+                                     tile_wave_total<Op, R, VEC, true>(t1.base, lane, tr, nullptr, e1, h1, lx),
+                                     &s_slot[1]);
+    if (t0.tile < p.num_tiles)
+        hand_over_slot<Op, Slot, ND>(p, t0.tile, 0, w, lane,
+                                     tile_wave_total<Op, R, VEC, true>(t0.base, lane, tr, nullptr, e0, h0, lx),
+                                     &s_slot[0]);
+    for (uint32_t k = 0; t0.tile < p.num_tiles; ++k) {
+        uint32_t next_id = p.num_tiles;
+        if (w == 0) next_id = ask_id(p, exhausted);
+        if (k >= 1) {
+            // e0 holds tile k: raw, and its total is published now; or, for
+            // the second tile, in blocked order with its total out
+            if (k >= 2)
+                hand_over_slot<Op, Slot, ND>(p, t0.tile, k, w, lane,
+                                             tile_wave_total<Op, R, VEC, true>(t0.base, lane, tr, nullptr, e0, h0, lx),
+                                             &s_slot[k % kPipeSlots]);
+            else
+                park_blocked<R, VEC, E>(tr, lane, e0);
+            if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t1.base, t1.vec, lane, e1, h1);
+        }
+        Slot* slot = &s_slot[k % kPipeSlots];
+        wait_seq(&slot->prefix_seq, k + 1);
+        V wave_prefix = Op::identity();
+#pragma unroll
+        for (int q = 0; q < ND; ++q)
+            if (q < w) wave_prefix = Op::combine(wave_prefix, slot->wave_total[q]);
+        reload_blocked<R, VEC, E>(tr, lane, e0);
+        scan_store_blocked<Op, EXCL, R, VEC>(p, t0.base, t0.vec, lane, tr, slot->prefix, wave_prefix, e0, h0, lx,
+                                             false);
+        t0 = t1;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            h0[r] = h1[r];
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) e0[r][j] = e1[r][j];
+        }
+        if (w == 0) post_id(p, s_ids, k + 2, next_id, exhausted);
+        t1.set(p, get_id(s_ids, k + 2), w);
+    }
+    if (w == 0 && lane == 0) retire_workgroup(p);
 }
 
 template <class Op, bool EXCL, int BLOCK, int ITEMS, int WAIT>
@@ -1184,6 +1298,11 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     if (w == 0) exhausted = take_first_batch<kPipeTiles>(p, &s_ids);
     if (w == ND) {
         fetch_prefixes<Op>(p, &s_ids, s_slot);
+        return;
+    }
+    if constexpr (ReloadAfterWait<Op>::value) {
+        static_assert(WAIT == 1 && BLK && !IsSeg<Op>::value, "one waiting tile, blocked layout");
+        persistent_reload_loop<Op, EXCL, G, Slot>(p, s_slot, &s_ids, tr, w, lane, exhausted);
         return;
     }
 
