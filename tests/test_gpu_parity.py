@@ -236,6 +236,35 @@ def test_mat3_unaligned_and_in_place(path):
             assert_equal(from_dev(t), oracle.scan_mat3(x, exclusive=True), "in place n=%d path=%s" % (n, path))
 
 
+def odd_det_matrices(seed, n, k):
+    """(n, k*k) uint32 matrices I + 2R: odd determinant, so invertible mod 2^32 -- their
+    products never collapse to zero, unlike products of uniform matrices, and every
+    output depends on the whole prefix (a wrong carry between tiles cannot go unseen)."""
+    m = (si.uint32_full(seed, k * k * n).reshape(n, k * k) * np.uint32(2)).astype(np.uint32)
+    for i in range(k):
+        m[:, i * k + i] += np.uint32(1)
+    return m
+
+
+@pytest.mark.parametrize("op,k", [("mat2", 2), ("mat3", 3)])
+def test_matrix_products_nondegenerate_large(op, k):
+    """2^22 matrices with odd determinants: the persistent kernel's steady state (several
+    tiles per workgroup), the one-tile kernel and reduce-then-scan, inclusive and exclusive."""
+    n = (1 << 22) + 3
+    x = odd_det_matrices(720 + k, n, k)
+    ref_fn = oracle.scan_mat2 if k == 2 else oracle.scan_mat3
+    xd = to_dev(x)
+    for excl in (False, True):
+        ref = ref_fn(x, exclusive=excl)
+        for path in ("auto", "multi", "fallback", "rts"):
+            print("%s excl=%s path=%s" % (op, excl, path), flush=True)
+            with Path(path):
+                y = from_dev((dw.scan_exclusive if excl else dw.scan_inclusive)(xd, op))
+            assert_equal(y, ref, "%s excl=%s path=%s" % (op, excl, path))
+    assert not np.any(np.all(ref_fn(x)[-5:] == 0, axis=1))  # nothing collapsed
+    assert dw.scan_get_device_error() == 0
+
+
 @pytest.mark.parametrize("op,logn", [("maxcount", 27), ("mat2", 25), ("mat3", 24)])
 def test_composite_and_matrix_full_size(op, logn):
     """The benchmarked sizes of the composite and matrix operators, compared whole."""
