@@ -31,7 +31,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "scan_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-OPS = {"add": 0, "max": 1, "min": 2}
+OPS = {"add": 0, "max": 1, "min": 2, "and": 3, "or": 4}
 
 _lib = None
 
@@ -95,7 +95,8 @@ def _contig(x: np.ndarray, dtype) -> np.ndarray:
 
 
 def scan(op: str, x: np.ndarray, exclusive: bool = False):
-    """Inclusive (default) or exclusive scan of a 1-D int32/uint32/float32 array.
+    """Inclusive (default) or exclusive scan of a 1-D int32/uint32/float32 array;
+    op in add, max, min, and (bitwise) or "and", "or" (bitwise, integers only).
 
     Returns y in the input dtype, except for float32 add, which returns the
     pair (y, s) of float64 arrays: y is the prefix sum accumulated in double
@@ -114,6 +115,8 @@ def scan(op: str, x: np.ndarray, exclusive: bool = False):
         lib.oracle_scan_u32(OPS[op], ex, _ptr(_contig(x, np.uint32)), _ptr(y), n)
         return y
     if x.dtype == np.float32:
+        if op in ("and", "or"):
+            raise TypeError("bitwise scans take int32 or uint32")
         xc = _contig(x, np.float32)
         if op == "add":
             y = np.empty(n, np.float64)
@@ -243,6 +246,8 @@ def segmented_scan(op: str, x: np.ndarray, heads: np.ndarray, exclusive: bool = 
         lib.oracle_segscan_u32(OPS[op], ex, _ptr(_contig(x, np.uint32)), _ptr(h), _ptr(y), n)
         return y
     if x.dtype == np.float32:
+        if op in ("and", "or"):
+            raise TypeError("bitwise scans take int32 or uint32")
         xc = _contig(x, np.float32)
         if op == "add":
             y = np.empty(n, np.float64)

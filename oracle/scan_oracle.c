@@ -52,6 +52,8 @@
 #define OP_ADD 0
 #define OP_MAX 1
 #define OP_MIN 2
+#define OP_AND 3 /* bitwise AND and OR [L7 concept 1, operator generalisation]; */
+#define OP_OR 4  /* identities: all bits set, no bits set                        */
 
 /* ------------------------------------------------------------------ */
 /* int32: add wraps modulo 2^32 (two's complement); max/min as usual.  */
@@ -60,6 +62,7 @@ static int32_t i32_identity(int op)
 {
     if (op == OP_MAX) return INT32_MIN;
     if (op == OP_MIN) return INT32_MAX;
+    if (op == OP_AND) return -1; /* all 32 bits set */
     return 0;
 }
 
@@ -67,6 +70,8 @@ static int32_t i32_combine(int op, int32_t earlier, int32_t later)
 {
     if (op == OP_MAX) return (later > earlier) ? later : earlier;
     if (op == OP_MIN) return (later < earlier) ? later : earlier;
+    if (op == OP_AND) return earlier & later;
+    if (op == OP_OR) return earlier | later;
     return (int32_t)((uint32_t)earlier + (uint32_t)later);
 }
 
@@ -89,14 +94,16 @@ void oracle_scan_i32(int op, int exclusive, const int32_t *x, int32_t *y, int64_
 /* ------------------------------------------------------------------ */
 static uint32_t u32_identity(int op)
 {
-    if (op == OP_MIN) return UINT32_MAX;
-    return 0; /* add: 0, max: smallest value 0 */
+    if (op == OP_MIN || op == OP_AND) return UINT32_MAX;
+    return 0; /* add: 0, max: smallest value 0, or: no bits */
 }
 
 static uint32_t u32_combine(int op, uint32_t earlier, uint32_t later)
 {
     if (op == OP_MAX) return (later > earlier) ? later : earlier;
     if (op == OP_MIN) return (later < earlier) ? later : earlier;
+    if (op == OP_AND) return earlier & later;
+    if (op == OP_OR) return earlier | later;
     return earlier + later;
 }
 

@@ -157,6 +157,46 @@ def test_bruteforce_scan(op, dtype, exclusive):
             assert float(y[i]) == float(want), (op, dtype, exclusive, n, i)
 
 
+# Bitwise AND / OR scans ([L7] concept 1 lists them among scan operators):
+# identities all bits set / no bits set.
+@pytest.mark.parametrize("dtype", [np.int32, np.uint32])
+@pytest.mark.parametrize("op", ["and", "or"])
+@pytest.mark.parametrize("exclusive", [False, True])
+def test_bruteforce_bitwise(op, dtype, exclusive):
+    rng = np.random.default_rng(21)
+    f = (lambda a, b: a & b) if op == "and" else (lambda a, b: a | b)
+    ident = -1 if op == "and" else 0  # all bits / none, as a Python int
+    for n in (1, 2, 3, 7, 33):
+        # mostly-set words for AND, mostly-clear ones for OR, so prefixes stay varied
+        r = rng.integers(0, 2**32, (3, n), dtype=np.uint64)
+        w = (r[0] | r[1] | r[2]) if op == "and" else (r[0] & r[1] & r[2])
+        x = w.astype(np.uint32).view(np.int32) if dtype == np.int32 else w.astype(np.uint32)
+        y = oracle.scan(op, x, exclusive=exclusive)
+        for i in range(n):
+            acc = ident
+            for k in range(i if exclusive else i + 1):
+                acc = f(acc, int(x[k]))
+            want = np.array(acc & 0xFFFFFFFF, dtype=np.uint64).astype(np.uint32)
+            assert int(y.view(np.uint32)[i]) == int(want), (op, exclusive, n, i)
+
+
+def test_bitwise_against_numpy_and_monotone():
+    n = 100000
+    u = si.uint32_full(22, 3 * n).reshape(3, n)
+    xa = u[0] | u[1] | u[2] | (si.uint32_full(23, n) & np.uint32(0xFFFF0FFF))
+    xo = u[0] & u[1] & u[2] & (si.uint32_full(24, n) >> np.uint32(3))
+    ya, yo = oracle.scan("and", xa), oracle.scan("or", xo)
+    np.testing.assert_array_equal(ya, np.bitwise_and.accumulate(xa))
+    np.testing.assert_array_equal(yo, np.bitwise_or.accumulate(xo))
+    assert np.all(ya[1:] & ~ya[:-1] == 0) and np.all(yo[:-1] & ~yo[1:] == 0)  # bits only leave / only join
+    np.testing.assert_array_equal(oracle.scan("and", xa, exclusive=True)[1:], ya[:-1])
+    assert oracle.scan("and", xa, exclusive=True)[0] == np.uint32(0xFFFFFFFF)
+    assert oracle.scan("or", xo, exclusive=True)[0] == 0
+    np.testing.assert_array_equal(oracle.scan("or", xo.view(np.int32)).view(np.uint32), yo)
+    with pytest.raises(TypeError):
+        oracle.scan("and", np.zeros(3, np.float32))
+
+
 def test_bruteforce_exercise_input():
     # exercise array of the PMPP chapter-9 notes (§八 "Scan定义"); the page prints no answer
     x = np.array([3, 1, 4, 1, 5, 9, 2, 6], np.int32)
