@@ -23,7 +23,7 @@ Also reported:
                 achievable bandwidth of a one-read-one-write kernel.
 
 --suite FILE additionally times every workload (int32 exclusive add at 2^20
-and 2^28, int32 max, compaction, affine, segmented add, (maximum, count),
+and 2^28, int32 max, uint32 bitwise or, compaction, affine, segmented add, (maximum, count),
 2x2 and 3x3 matrices, CSR row offsets, a 256-bin histogram, radix split passes and a
 four-pass sort, the
 max-scan size sweep with reduce-then-scan beside it) and writes one JSON line
@@ -502,6 +502,10 @@ def suite(dw, torch, si, out_path, steps):
     rec("int32 exclusive add 2^28", 1 << 28, 8, lambda: dw.scan_exclusive(x, "add", out=y))
     rec("int32 inclusive max 2^28", 1 << 28, 8, lambda: dw.scan_inclusive(x, "max", out=y))
     del x, y
+    xb = torch.from_numpy(si.uint32_full(12, 1 << 28)).cuda()
+    yb = torch.empty_like(xb)
+    rec("uint32 inclusive bitwise or 2^28", 1 << 28, 8, lambda: dw.scan_inclusive(xb, "or", out=yb))
+    del xb, yb
     xc = torch.from_numpy(si.float32_normal(3, 1 << 28)).cuda()
     yc = torch.empty_like(xc)
     cnt = torch.zeros(1, dtype=torch.uint32, device="cuda")

@@ -16,7 +16,7 @@ import torch
 from . import build as _build
 
 SCAN_OK, SCAN_ERR_INVALID, SCAN_ERR_UNSUPPORTED, SCAN_ERR_NOMEM, SCAN_ERR_HIP, SCAN_ERR_TIMEOUT = range(6)
-OPS = {"add": 0, "max": 1, "min": 2, "affine": 3, "maxcount": 4, "mat2": 5, "mat3": 6}
+OPS = {"add": 0, "max": 1, "min": 2, "affine": 3, "maxcount": 4, "mat2": 5, "mat3": 6, "and": 7, "or": 8}
 SCAN_I32, SCAN_U32, SCAN_F32, SCAN_U32X2, SCAN_I32_U32, SCAN_U32X4, SCAN_U32X9 = range(7)
 _DTYPES = {torch.int32: SCAN_I32, torch.uint32: SCAN_U32, torch.float32: SCAN_F32}
 
@@ -111,6 +111,8 @@ def _dtype_code(x: torch.Tensor, op: str) -> int:
         return SCAN_U32X9
     if x.dtype not in _DTYPES:
         raise TypeError("unsupported dtype %s" % x.dtype)
+    if op in ("and", "or") and x.dtype == torch.float32:
+        raise TypeError("bitwise scans take int32 or uint32")
     return _DTYPES[x.dtype]
 
 
@@ -127,7 +129,7 @@ def _prep(x: torch.Tensor, out):
 
 
 def scan_inclusive(x: torch.Tensor, op: str = "add", out: torch.Tensor | None = None, stream=None):
-    """out[i] = x[0] (+) ... (+) x[i]; op in add/max/min (1-D), affine or maxcount ((n, 2)
+    """out[i] = x[0] (+) ... (+) x[i]; op in add/max/min/and/or (1-D), affine or maxcount ((n, 2)
     pairs), mat2 ((n, 4) matrices), mat3 ((n, 9) or (n, 3, 3) matrices)."""
     dt = _dtype_code(x, op)
     out = _prep(x, out)

@@ -409,6 +409,10 @@ Runner plain_runner(int op, int dt)
     if (op == SCAN_OP_MAX_COUNT && dt == SCAN_I32_U32) return run_scan<OpMaxCount, EXCL>;
     if (op == SCAN_OP_MAT2 && dt == SCAN_U32X4) return run_scan<OpMat2, EXCL>;
     if (op == SCAN_OP_MAT3 && dt == SCAN_U32X9) return run_scan<OpMat3, EXCL>;
+    if (op == SCAN_OP_AND && dt == SCAN_I32) return run_scan<OpAnd<int32_t>, EXCL>;
+    if (op == SCAN_OP_AND && dt == SCAN_U32) return run_scan<OpAnd<uint32_t>, EXCL>;
+    if (op == SCAN_OP_OR && dt == SCAN_I32) return run_scan<OpOr<int32_t>, EXCL>;
+    if (op == SCAN_OP_OR && dt == SCAN_U32) return run_scan<OpOr<uint32_t>, EXCL>;
     return nullptr;
 }
 
@@ -452,7 +456,7 @@ bool ranges_partially_overlap(const void* a, const void* b, size_t bytes_a, size
 scan_status_t plain_scan(bool excl, scan_op_t op, scan_dtype_t dt, const void* in, void* out, size_t n,
                          void* stream)
 {
-    if ((unsigned)op > SCAN_OP_MAT3 || (unsigned)dt > SCAN_U32X9) return SCAN_ERR_UNSUPPORTED;
+    if ((unsigned)op > SCAN_OP_OR || (unsigned)dt > SCAN_U32X9) return SCAN_ERR_UNSUPPORTED;
     const Runner r = excl ? plain_runner<true>(op, dt) : plain_runner<false>(op, dt);
     if (!r) return SCAN_ERR_UNSUPPORTED;
     if (n == 0) return SCAN_OK;

@@ -147,6 +147,18 @@ template <typename T> struct OpMin : SameCarry<T, OpMin<T>> {
     __device__ __forceinline__ static T combine(T a, T b) { return (b < a) ? b : a; }
 };
 
+// ---------------------------------------------------------------- bitwise
+// Bitwise AND / OR, also scan operators [L7 concept 1, operator
+// generalisation]; identities: all bits set / no bits set.
+template <typename T> struct OpAnd : SameCarry<T, OpAnd<T>> {
+    __device__ __forceinline__ static T identity() { return (T)~0u; }
+    __device__ __forceinline__ static T combine(T a, T b) { return a & b; }
+};
+template <typename T> struct OpOr : SameCarry<T, OpOr<T>> {
+    __device__ __forceinline__ static T identity() { return (T)0; }
+    __device__ __forceinline__ static T combine(T a, T b) { return a | b; }
+};
+
 // ---------------------------------------------------------------- affine
 // Composition of maps x -> a*x + b over uint32 (mod 2^32).  The later map is
 // applied after the earlier one: (a2,b2) o (a1,b1) = (a2*a1, a2*b1 + b2).
@@ -175,7 +187,7 @@ struct OpMaxCount : SameCarry<MaxCount, OpMaxCount> {
 
 // ---------------------------------------------------------------- commutativity
 // Operators whose result does not depend on the order of the operands, bit
-// for bit: integer add/max/min, float add (exact per operation; only the
+// for bit: integer add/max/min/and/or, float add (exact per operation; only the
 // rounding of a longer sum depends on its association, which the float
 // tolerance already allows) and (maximum, count).  Not float max/min (the
 // earlier of +0 and -0 wins), affine maps, matrices or segmented pairs.  A
@@ -189,6 +201,10 @@ template <> struct IsCommutative<OpMax<uint32_t>> { static constexpr bool value 
 template <> struct IsCommutative<OpMin<int32_t>> { static constexpr bool value = true; };
 template <> struct IsCommutative<OpMin<uint32_t>> { static constexpr bool value = true; };
 template <> struct IsCommutative<OpMaxCount> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpAnd<int32_t>> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpAnd<uint32_t>> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpOr<int32_t>> { static constexpr bool value = true; };
+template <> struct IsCommutative<OpOr<uint32_t>> { static constexpr bool value = true; };
 
 // ---------------------------------------------------------------- 2x2 matrices
 // Matrix multiplication [L7 concept 1] over uint32 (mod 2^32), the later

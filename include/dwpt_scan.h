@@ -46,7 +46,7 @@
  *   scan_inclusive / scan_exclusive: ADD, MAX, MIN with I32, U32, F32;
  *                                    AFFINE with U32X2; MAX_COUNT with
  *                                    I32_U32; MAT2 with U32X4; MAT3 with
- *                                    U32X9.
+ *                                    U32X9; AND, OR with I32, U32.
  *   segmented_scan:                  ADD, MAX, MIN with I32, U32, F32.
  *   compact:                         I32, U32, F32.
  * Integer ADD wraps modulo 2^32.  F32 ADD results may differ from an exact
@@ -80,7 +80,9 @@ typedef enum {
     SCAN_OP_AFFINE = 3,    /* x -> a*x + b maps composed, later map applied after */
     SCAN_OP_MAX_COUNT = 4, /* (maximum, number of occurrences) composite */
     SCAN_OP_MAT2 = 5,      /* 2x2 matrix product, later factor on the left */
-    SCAN_OP_MAT3 = 6       /* 3x3 matrix product, later factor on the left */
+    SCAN_OP_MAT3 = 6,      /* 3x3 matrix product, later factor on the left */
+    SCAN_OP_AND = 7,       /* bitwise AND */
+    SCAN_OP_OR = 8         /* bitwise OR */
 } scan_op_t;
 
 typedef enum {
@@ -108,6 +110,7 @@ typedef enum {
  * so far and how often it occurred; MAT2 and MAT3 multiply 2x2 and 3x3
  * matrices mod 2^32 with the later factor on the left (affine maps are
  * [[a, b], [0, 1]]; 2x2 matrices A are the 3x3 [[A, 0], [0, 1]]).
+ * AND and OR are the bitwise operators, also named as scan operators there.
  */
 scan_status_t scan_inclusive(scan_op_t op, scan_dtype_t dtype, const void* in, void* out,
                              size_t n, void* stream);
@@ -117,7 +120,7 @@ scan_status_t scan_inclusive(scan_op_t op, scan_dtype_t dtype, const void* in, v
  * [L7 concept 1; PMPP9 §9.1 (identity table); YLY §2.2]  Identities: ADD 0,
  * MAX the type's lowest value (-inf for F32), MIN its highest (+inf),
  * AFFINE (1, 0), MAX_COUNT (INT32_MIN, 0), MAT2 and MAT3 the identity
- * matrix.
+ * matrix, AND all bits set, OR no bits set.
  */
 scan_status_t scan_exclusive(scan_op_t op, scan_dtype_t dtype, const void* in, void* out,
                              size_t n, void* stream);

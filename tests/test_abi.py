@@ -77,6 +77,13 @@ def test_argument_checks_before_any_launch():
     assert L.scan_inclusive(MAT2, 6, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
     assert L.segmented_scan(MC, MCPAIR, 1024, 4096, 2048, 10, 0, None) == binding.SCAN_ERR_UNSUPPORTED
     MAT3, MAT9 = 6, 6
+    AND, OR = 7, 8
+    assert L.scan_inclusive(AND, F32, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_exclusive(OR, F32, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(AND, PAIR, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(9, U32, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.segmented_scan(OR, U32, 1024, 4096, 2048, 10, 0, None) == binding.SCAN_ERR_UNSUPPORTED
+    assert L.scan_inclusive(AND, U32, 1026, 2048, 10, None) == binding.SCAN_ERR_INVALID
     assert L.scan_inclusive(MAT3, MAT, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
     assert L.scan_inclusive(MAT2, MAT9, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED
     assert L.scan_inclusive(ADD, MAT9, 1024, 2048, 10, None) == binding.SCAN_ERR_UNSUPPORTED

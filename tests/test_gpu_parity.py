@@ -121,6 +121,38 @@ def test_scan_parity(op, dt, exclusive):
             check_scan(op, x, y, exclusive, "%s %s excl=%s n=%d path=%s" % (op, dt, exclusive, n, path))
 
 
+def bitwise_input(seed, n, op, dt):
+    """AND: all bits set except where rare events clear one; OR: no bits except where rare
+    events set one -- about 16 events over the array, so the scan keeps changing late
+    and every tile's carry matters (uniform words would saturate within a few elements)."""
+    u = si.uint32_full(seed, n).astype(np.uint64)
+    v = si.uint32_full(seed + 1, n)
+    event = (u % np.uint64(max(64, n // 16))) == 0
+    bit = (np.uint32(1) << (v % np.uint32(32))).astype(np.uint32)
+    w = np.where(event, ~bit if op == "and" else bit,
+                 np.uint32(0xFFFFFFFF) if op == "and" else np.uint32(0)).astype(np.uint32)
+    return w.view(np.int32) if dt == "i32" else w
+
+
+@pytest.mark.parametrize("dt", ["i32", "u32"])
+@pytest.mark.parametrize("op", ["and", "or"])
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_bitwise_parity(op, dt, exclusive):
+    fn = dw.scan_exclusive if exclusive else dw.scan_inclusive
+    for k, n in enumerate(SIZES + [(1 << 26) + 5]):
+        x = bitwise_input(800 + k, n, op, dt)
+        ref = oracle.scan(op, x, exclusive=exclusive)
+        for path in paths_for(n):
+            with Path(path):
+                y = from_dev(fn(to_dev(x), op))
+            assert_equal(y, ref, "%s %s excl=%s n=%d path=%s" % (op, dt, exclusive, n, path))
+
+
+def test_bitwise_rejects_floats():
+    with pytest.raises(TypeError):
+        dw.scan_inclusive(torch.zeros(10, dtype=torch.float32, device="cuda"), "and")
+
+
 @pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
 @pytest.mark.parametrize("odd", [False, True], ids=["any_a", "odd_a"])
 def test_affine_parity(exclusive, odd):
