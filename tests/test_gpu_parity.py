@@ -601,6 +601,32 @@ def test_bounded_waits_report_timeout_and_recover():
         assert dw.scan_get_device_error() == 0
 
 
+@pytest.mark.parametrize("op", ["mat3", "mat2", "affine"])
+def test_bounded_waits_blocked_operators(op):
+    """The same for the blocked-layout pipelines (3x3 matrices: the waiting tile held in
+    LDS), persistent kernel forced."""
+    n = (1 << 22) + 7
+    x = {"mat3": lambda: odd_det_matrices(731, n, 3), "mat2": lambda: odd_det_matrices(732, n, 2),
+         "affine": lambda: si.affine_pairs(733, n, odd_a=True)}[op]()
+    ref = {"mat3": oracle.scan_mat3, "mat2": oracle.scan_mat2, "affine": oracle.scan_affine}[op](x)
+    xd = to_dev(x)
+    old_mode = dw.scan_set_multi_tile_mode(2)
+    try:
+        old = dw.scan_set_spin_limit(0)
+        try:
+            for _ in range(3):
+                dw.scan_inclusive(xd, op)
+            st = dw.scan_get_device_error()
+        finally:
+            dw.scan_set_spin_limit(old)
+        assert st in (0, 5), st
+        assert dw.scan_get_device_error() == 0
+        assert_equal(from_dev(dw.scan_inclusive(xd, op)), ref, "%s after timeout" % op)
+    finally:
+        dw.scan_set_multi_tile_mode(old_mode)
+    assert dw.scan_get_device_error() == 0
+
+
 @pytest.mark.parametrize("path", ["multi", "auto"])
 def test_blocked_layout_unaligned_and_in_place(path):
     """The persistent kernel's blocked lane layout (affine, (maximum, count), 2x2 matrices,
