@@ -510,10 +510,13 @@ def suite(dw, torch, si, out_path, steps):
 
     def rec(name, n, bytes_per_elem, fn):
         log("suite: " + name)
-        # the clocks settle over the first ~100 launches
+        # the clocks settle over the first ~100 launches; median_us: one call's time,
+        # each launch between its own event pair (latency); the rates: the same number
+        # of launches back to back (throughput, gaps between launches included)
         elapsed, ms = time_launches(fn, steps, 100, torch)
-        t = statistics.median(ms) * 1e-3
-        lines.append({"workload": name, "n": n, "median_us": round(t * 1e6, 2),
+        _, t = time_back_to_back(fn, steps, 0, torch)
+        lines.append({"workload": name, "n": n, "median_us": round(statistics.median(ms) * 1e3, 2),
+                      "back_to_back_us": round(t * 1e6, 2),
                       "gelem_s": round(n / t / 1e9, 2),
                       "effective_GBps": round(n * bytes_per_elem / t / 1e9, 1),
                       "pct_of_peak": round(100 * n * bytes_per_elem / t / 1e9 / PEAK_GBPS, 1),
