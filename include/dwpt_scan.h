@@ -224,8 +224,11 @@ uint32_t scan_set_spin_limit(uint32_t polls);
 
 /*
  * Measurement helper, not part of the scan: copies nbytes (a multiple of 16,
- * 16-byte aligned pointers) from in to out with a plain streaming kernel, to
- * calibrate achievable HBM bandwidth and the traffic counters.
+ * 16-byte aligned pointers) from in to out with a plain streaming kernel
+ * (its stores carry the same cache policy as the scan's whole-tile stores), to
+ * calibrate achievable HBM bandwidth and the traffic counters.  Returns
+ * SCAN_ERR_INVALID for null pointers, misalignment or a size not a multiple
+ * of 16; nbytes == 0 does nothing.
  */
 scan_status_t scan_copy_probe(const void* in, void* out, size_t nbytes, void* stream);
 
