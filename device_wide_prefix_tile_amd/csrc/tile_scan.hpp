@@ -146,9 +146,8 @@ __device__ __forceinline__ void store_vec(E* p, const E (&e)[VEC])
 // hint alone (float32 add at 2^28: 340.0 against 345.6 us; int32 add 335.9
 // against 340.4), with identical results; nt alone through the same path
 // gained nothing.  The descriptor's base is made wavefront-uniform, so it
-// lives in scalar registers.  The blocked-layout and compaction stores keep
-// the plain streaming hint: there the descriptor added register spills at the
-// 128-VGPR limit and the same policy cost 9-19%.
+// lives in scalar registers.  Compaction's packed stores and most
+// blocked-layout stores keep the plain streaming hint (see BlockedStorePolicy).
 #ifndef DWPT_STORE_POLICY
 #define DWPT_STORE_POLICY (DWPT_NT_STORES ? 18 : 0)  // cache-policy bits: 2 nt, 16 sc1 (1 sc0)
 #endif
@@ -1109,6 +1108,16 @@ __device__ __forceinline__ typename Op::value_t reduce_blocked(uint64_t wave_bas
     return read_lane(incl, 63);
 }
 
+// Blocked-layout operators whose tile stores take the buffer-descriptor path
+// with the streaming + sc1 policy (as apply_store).  Measured per operator,
+// identical outputs: affine 2^26 187.5 -> 183.8 us, 3x3 matrices 2^24
+// 528.6 -> 505.1 us.  The others keep the plain streaming hint: with the
+// descriptor they spill more at the 128-VGPR limit and were 9-19% slower
+// (segmented, (maximum, count), 2x2 matrices).
+template <class Op> struct BlockedStorePolicy { static constexpr bool value = false; };
+template <> struct BlockedStorePolicy<OpAffine> { static constexpr bool value = true; };
+template <> struct BlockedStorePolicy<OpMat3> { static constexpr bool value = true; };
+
 // A scanned tile in blocked order (y, changed in place) back to round order
 // through LDS, stored like apply_store.
 template <class Op, int R, int VEC>
@@ -1123,7 +1132,13 @@ __device__ __forceinline__ void store_blocked_tile(const ScanParams& p, uint64_t
         u32x4 v[C];
         __builtin_memcpy(v, y, 16 * C);
         uint32_t* __restrict__ dst = static_cast<uint32_t*>(p.out) + wave_base * W;
-        if (vec) {
+        if (vec && BlockedStorePolicy<Op>::value) {
+            const __amdgpu_buffer_rsrc_t rsrc = wave_rsrc(dst);
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                __builtin_amdgcn_raw_buffer_store_b128(v[c], rsrc, (uint32_t)(c * 64 + lane) * 16u, 0,
+                                                       DWPT_STORE_POLICY);
+        } else if (vec) {
 #pragma unroll
             for (int c = 0; c < C; ++c) {
 #if DWPT_NT_STORES
@@ -1145,6 +1160,15 @@ __device__ __forceinline__ void store_blocked_tile(const ScanParams& p, uint64_t
         return;
     }
     E* __restrict__ out = static_cast<E*>(p.out);
+    if constexpr (BlockedStorePolicy<Op>::value) {
+        if (vec) {
+            const __amdgpu_buffer_rsrc_t rsrc = wave_rsrc(out + wave_base);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                store_vec_buf<E, VEC>(rsrc, (uint32_t)((r * 64 + lane) * VEC * sizeof(E)), y[r]);
+            return;
+        }
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
