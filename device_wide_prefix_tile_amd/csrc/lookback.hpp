@@ -7,10 +7,12 @@
 // The lecture's hierarchical scan [L7 concept 6 "层次化扫描（Hierarchical
 // Scan）"] writes each block's total to a global array and scans it in a
 // second kernel, because blocks only see each other's global writes across a
-// kernel boundary.  It names the single-kernel alternative: block totals plus
-// global flags, with careful memory ordering and spinning ("decoupled
-// look-back", as published by Merrill and Garland, 2016).  This file is that
-// mechanism, reorganised for a GPU that keeps ~2000 tiles in flight:
+// kernel boundary.  It mentions a single-kernel alternative in which blocks
+// publish their totals and flags in global memory and wait on each other,
+// which works only with deliberate ordering of the memory operations and
+// spin-waiting (the method published by Merrill and Garland in 2016 as
+// decoupled look-back).  This file is that mechanism, reorganised for a GPU
+// that keeps ~2000 tiles in flight:
 //
 //  * Status words.  Every tile, and every group of 64 consecutive tiles, owns
 //    kWords 64-bit words.  A word holds one 32-bit payload word and a 32-bit
@@ -44,7 +46,11 @@
 //    every awaited tile has started, and an AGGREGATE never waits for
 //    anything but loads and lower tiles.  Waits are bounded: past
 //    `spin_limit` polls a tile records an error and carries on with what it
-//    has, so every wave always exits.
+//    has, so every wave always exits.  A wait that gives up also marks the
+//    launch as aborted (the abort word takes the launch's epoch); every other
+//    wait of the launch, on status words or on LDS, looks at that word now
+//    and then and gives up at once when it is set, so one lost total ends the
+//    launch in microseconds per remaining wait, not a full budget each.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -85,9 +91,51 @@ struct Lookback {
     uint64_t* status;    // kWords words per tile
     uint64_t* groups;    // kWords words per group of 64 tiles
     uint32_t* err;       // device error word (bit flags)
+    uint32_t* abort;     // epoch of the last launch that gave up a wait
     uint32_t epoch;      // 1 .. 2^29 - 1
     uint32_t spin_limit; // polls before giving up
 };
+
+// Bounded waits.  Every failed poll counts; past the budget the wait gives
+// up, records the timeout in the error word and marks the launch aborted.
+// Every kAbortCheck polls a wait also reads the abort word and gives up at
+// once if another wait of this launch already did (waits that succeed
+// normally take far fewer polls than that, so the check costs nothing then).
+// LDS waits poll about 16 times as often as status-word waits (no memory
+// round trip, a shorter sleep), so their budget is 16 times larger: about
+// the same wall time.
+enum : uint32_t { kAbortCheck = 64u, kLdsPollScale = 16u };
+
+// Called by the whole wavefront (the result is uniform).
+__device__ __forceinline__ bool launch_aborted(const Lookback& lb)
+{
+    const uint32_t a = __hip_atomic_load(lb.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)a) == lb.epoch;
+}
+
+// One failed poll of a wavefront's bounded wait (wave-uniform `polls`):
+// true once the wait must give up.
+__device__ __forceinline__ bool give_up(const Lookback& lb, uint64_t& polls, uint64_t limit)
+{
+    ++polls;
+    if (polls > limit) {
+        if (lane_id() == 0) {
+            __hip_atomic_fetch_or(lb.err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(lb.abort, lb.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return true;
+    }
+    if (polls % kAbortCheck == 0 && launch_aborted(lb)) {
+        polls = limit + 1;  // sticky: later waits sharing this counter give up at once
+        return true;
+    }
+    return false;
+}
+
+__device__ __forceinline__ uint64_t lds_poll_limit(const Lookback& lb)
+{
+    return (uint64_t)lb.spin_limit * kLdsPollScale;
+}
 
 __device__ __forceinline__ uint32_t make_tag(uint32_t epoch, uint32_t flag, uint32_t state)
 {
@@ -119,7 +167,7 @@ enum : int { kWinFound = 0, kWinBoundary = 1, kWinNone = 2, kWinTimeout = 3 };
 // fold ended; `out` is the same in every lane.
 template <class Op>
 __device__ int fold_window(const Lookback& lb, const uint64_t* arr, int64_t top, int64_t lo,
-                           typename Op::carry_t& out, uint32_t& polls)
+                           typename Op::carry_t& out, uint64_t& polls)
 {
     using C = typename Op::carry_t;
     const int lane = lane_id();
@@ -154,9 +202,7 @@ __device__ int fold_window(const Lookback& lb, const uint64_t* arr, int64_t top,
         const int p = tmask ? 63 - __builtin_clzll(tmask) : -1;  // highest terminal lane
         const uint64_t from_p = (p < 0) ? ~0ull : (~0ull << p);
         if (wave_ballot(!have) & from_p) {
-            if (++polls > lb.spin_limit) {
-                if (lane == 0)
-                    __hip_atomic_fetch_or(lb.err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (give_up(lb, polls, lb.spin_limit)) {
                 out = ident;
                 return kWinTimeout;
             }
@@ -177,7 +223,7 @@ __device__ int fold_window(const Lookback& lb, const uint64_t* arr, int64_t top,
 // round trip however wide it is.  Same results as fold_window.
 template <class Op, int SPAN>
 __device__ int fold_window_wide(const Lookback& lb, const uint64_t* arr, int64_t top, int64_t lo,
-                                typename Op::carry_t& out, uint32_t& polls)
+                                typename Op::carry_t& out, uint64_t& polls)
 {
     using C = typename Op::carry_t;
     const int lane = lane_id();
@@ -233,9 +279,7 @@ __device__ int fold_window_wide(const Lookback& lb, const uint64_t* arr, int64_t
         const int p = tmask ? 63 - __builtin_clzll(tmask) : -1;  // lane with the nearest terminal entry
         const uint64_t from_p = (p < 0) ? ~0ull : (~0ull << p);
         if (wave_ballot(!ok) & from_p) {
-            if (++polls > lb.spin_limit) {
-                if (lane == 0)
-                    __hip_atomic_fetch_or(lb.err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (give_up(lb, polls, lb.spin_limit)) {
                 out = ident;
                 return kWinTimeout;
             }
@@ -258,7 +302,7 @@ __device__ int fold_window_wide(const Lookback& lb, const uint64_t* arr, int64_t
 // Exclusive prefix of `tile` from tile statuses alone: fold windows of
 // 64 * SPAN predecessors back to the nearest PREFIX (or the start).
 template <class Op, int SPAN>
-__device__ typename Op::carry_t walk_tiles(const Lookback& lb, int64_t tile, uint32_t& polls)
+__device__ typename Op::carry_t walk_tiles(const Lookback& lb, int64_t tile, uint64_t& polls)
 {
     using C = typename Op::carry_t;
     C acc = Op::carry_identity();
@@ -288,7 +332,7 @@ __device__ typename Op::carry_t resolve_stream(const Lookback& lb, const uint64_
     const int lane = lane_id();
     const C ident = Op::carry_identity();
     C carry = ident;
-    uint32_t polls = 0;
+    uint64_t polls = 0;  // not reset per window: once the resolver gave up, it gives up at once
     for (uint64_t B = 0; B < num_tiles; B += W) {
         const uint64_t j0 = B + (uint64_t)lane * SPAN;
         bool have[SPAN];
@@ -356,14 +400,11 @@ __device__ typename Op::carry_t resolve_stream(const Lookback& lb, const uint64_
                     break;
                 }
             }
-            if (++polls > lb.spin_limit) {
-                // give up: count the missing totals as the identity, so that
-                // every waiting tile still gets a (wrong) prefix and exits
-                if (lane == 0)
-                    __hip_atomic_fetch_or(lb.err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (give_up(lb, polls, lb.spin_limit)) {
+                // count the missing totals as the identity, so that every
+                // waiting tile still gets a (wrong) prefix and exits
 #pragma unroll
                 for (int k = 0; k < SPAN; ++k) have[k] = true;
-                polls = 0;
                 continue;
             }
             __builtin_amdgcn_s_sleep(DWPT_LB_SLEEP);
@@ -398,33 +439,28 @@ __device__ __forceinline__ bool prefix_ready(const Lookback& lb, const uint64_t 
     return true;
 }
 
-__device__ __forceinline__ bool spin_exhausted(const Lookback& lb, uint32_t& polls)
-{
-    if (++polls <= lb.spin_limit) return false;
-    if (lane_id() == 0) __hip_atomic_fetch_or(lb.err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
-}
-
 // The exclusive prefix of `tile` published by the resolver (every lane
-// reads the same words; the result is uniform).
+// reads the same words; the result is uniform).  `polls` is the caller's
+// counter: reset per tile while within budget, so each tile has the whole
+// budget, but once a wait gave up every later one gives up after one read.
 template <class Op>
-__device__ typename Op::carry_t wait_excl(const Lookback& lb, const uint64_t* excl, uint64_t tile)
+__device__ typename Op::carry_t wait_excl(const Lookback& lb, const uint64_t* excl, uint64_t tile, uint64_t& polls)
 {
     const uint64_t* src = excl + tile * (Op::kWords * DWPT_PREFIX_PAD);
     typename Op::carry_t out;
-    uint32_t polls = 0;
+    if (polls <= lb.spin_limit) polls = 0;
     while (true) {
         uint64_t raw[Op::kWords];
         read_words<Op>(src, raw);
         if (prefix_ready<Op>(lb, raw, out)) return out;
-        if (spin_exhausted(lb, polls)) return Op::carry_identity();
+        if (give_up(lb, polls, lb.spin_limit)) return Op::carry_identity();
         __builtin_amdgcn_s_sleep(DWPT_FETCH_SLEEP);
     }
 }
 
 // Fold of the groups g-1, g-2, ... back to the nearest PREFIX (or the start).
 template <class Op>
-__device__ typename Op::carry_t walk_groups(const Lookback& lb, int64_t g, uint32_t& polls)
+__device__ typename Op::carry_t walk_groups(const Lookback& lb, int64_t g, uint64_t& polls)
 {
     using C = typename Op::carry_t;
     C acc = Op::carry_identity();
@@ -463,10 +499,16 @@ struct TileHandover {
     uint32_t total_ready;  // set once the tile total is stored and published
 };
 
-__device__ __forceinline__ void wait_total(TileHandover* h)
+// Bounded like every other wait; on giving up the caller goes on with
+// whatever the LDS holds (the launch's results are then wrong and flagged).
+__device__ __forceinline__ void wait_total(const Lookback& lb, TileHandover* h)
 {
-    while (__hip_atomic_load(&h->total_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
+    uint64_t polls = 0;
+    const uint64_t limit = lds_poll_limit(lb);
+    while (__hip_atomic_load(&h->total_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u) {
+        if (give_up(lb, polls, limit)) return;
         __builtin_amdgcn_s_sleep(1);
+    }
 }
 
 // Look-back wavefront of tile `tile` (a full wavefront; result uniform).
@@ -484,18 +526,18 @@ __device__ typename Op::carry_t lookback_wave(const Lookback& lb, uint32_t tile,
     const int lane = lane_id();
     const int64_t g = (int64_t)(tile >> kGroupShift);
     const bool last_in_group = (tile & 63u) == 63u;
-    uint32_t polls = 0;
+    uint64_t polls = 0;
 
     C acc;
     const int r = fold_window<Op>(lb, lb.status, (int64_t)tile - 1, g << kGroupShift, acc, polls);
     if (r == kWinBoundary && g > 0) {
         if (last_in_group) {
-            wait_total(h);
+            wait_total(lb, h);
             if (lane == 0) publish<Op>(lb, lb.groups, (uint64_t)g, Op::combine_carry(acc, *total), kStateAggregate);
         }
         acc = Op::combine_carry(walk_groups<Op>(lb, g, polls), acc);
     }
-    wait_total(h);
+    wait_total(lb, h);
     if (lane == 0) {
         const C incl = Op::combine_carry(acc, *total);
         if (!*known) publish<Op>(lb, lb.status, tile, incl, kStatePrefix);

@@ -123,6 +123,7 @@ struct Workspace {
     uint32_t* ctr = nullptr;
     uint32_t* pipe_ctr = nullptr;  // persistent kernel's self-resetting counters (one 128-byte line each)
     uint32_t* err = nullptr;
+    uint32_t* abort = nullptr;     // epoch of the last launch that gave up a wait (its own line)
     uint32_t ctr_base = 0;
     uint32_t epoch = 0;
     // reduce-then-scan's plain carries, in memory of their own: status words
@@ -136,7 +137,8 @@ struct Workspace {
     size_t hist_bytes = 0;
 };
 std::map<std::pair<int, void*>, Workspace> g_ws;
-constexpr size_t kHeaderBytes = 512;  // line 0: err word, tile counter; lines 1-3: persistent-kernel counters
+// line 0: err word, tile counter; lines 1-3: persistent-kernel counters; line 4: abort word
+constexpr size_t kHeaderBytes = 640;
 
 __global__ void zero_words_kernel(uint64_t* p, size_t nwords)
 {
@@ -186,14 +188,16 @@ scan_status_t acquire_workspace(hipStream_t s, size_t words, Workspace** out)
         ws.err = static_cast<uint32_t*>(mem);
         ws.ctr = static_cast<uint32_t*>(mem) + 1;
         ws.pipe_ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + 128);
+        ws.abort = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + 512);
         ws.status = reinterpret_cast<uint64_t*>(static_cast<char*>(mem) + kHeaderBytes);
         ws.ctr_base = 0;
         ws.epoch = 0;
     }
     ws.epoch += 1;
     if (ws.epoch >= (1u << kEpochBits)) {
-        // every tag of the array could now alias the new epoch: clear it
+        // every tag of the array (and the abort word) could now alias the new epoch: clear them
         if (zero_async(ws.status, ws.status_words * 8, s) != hipSuccess) return SCAN_ERR_HIP;
+        if (zero_async(ws.abort, 128, s) != hipSuccess) return SCAN_ERR_HIP;
         ws.epoch = 1;
     }
     *out = &ws;
@@ -304,10 +308,13 @@ struct RtsKernels {
 // three reduce-then-scan kernels, as the mode and the number of tiles
 // select.  TILE is the tile size and kWords the status words per tile;
 // `grand` receives the fold of all tiles in reduce-then-scan (compaction's
-// count), or nullptr.
+// count), or nullptr.  rts_ok == false makes reduce-then-scan mode take the
+// single-pass kernels instead (in-place compaction: its last pass writes a
+// tile's kept elements below the tile, where earlier tiles of the same launch
+// may not have read theirs yet).
 template <int BLOCK, int TILE, int kWords, class C>
 scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(ScanParams),
-                     const RtsKernels<C>& rts, C* grand, const Call& c, bool vec_ok)
+                     const RtsKernels<C>& rts, C* grand, const Call& c, bool vec_ok, bool rts_ok = true)
 {
     ScanParams p{};
     p.in = c.in;
@@ -331,7 +338,7 @@ scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(
     // kernel, PREFIX_PAD entries apart: one prefix per 128-byte line)
     const scan_status_t st = acquire_workspace(c.stream, (size_t)tiles * kWords * (DWPT_AGG_PAD + DWPT_PREFIX_PAD), &ws);
     if (st != SCAN_OK) return st;
-    if (g_multi_mode == 3) {
+    if (g_multi_mode == 3 && rts_ok) {
         // 2T + 1 plain carries: the tile totals, the grand total, the prefixes
         const scan_status_t sr = acquire_rts(c.stream, *ws, (2 * (size_t)tiles + 1) * sizeof(C));
         if (sr != SCAN_OK) return sr;
@@ -350,6 +357,7 @@ scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(
     p.lb.status = ws->status;
     p.lb.groups = ws->status + (size_t)tiles * kWords * DWPT_AGG_PAD;
     p.lb.err = ws->err;
+    p.lb.abort = ws->abort;
     p.lb.epoch = ws->epoch;
     p.lb.spin_limit = g_spin_limit;
     if (g_multi_mode != 1) {
@@ -389,7 +397,7 @@ scan_status_t run_compact(const Call& c, bool vec_ok)
                                    compact_seeded_kernel<T, BLOCK, ITEMS>};
     return launch<BLOCK, Geometry<OpAdd<uint32_t>, BLOCK, ITEMS>::TILE, 1, uint32_t>(
         compact_kernel<T, BLOCK, ITEMS, true>, compact_kernel<T, BLOCK, ITEMS, false>,
-        compact_persistent<T, BLOCK, ITEMS, DWPT_WAIT_COMPACT>, rts, c.count, c, vec_ok);
+        compact_persistent<T, BLOCK, ITEMS, DWPT_WAIT_COMPACT>, rts, c.count, c, vec_ok, c.in != (const void*)c.out);
 }
 
 typedef scan_status_t (*Runner)(const Call&, bool);
@@ -619,6 +627,8 @@ scan_status_t compact(scan_dtype_t dtype, const void* in, void* out, uint32_t* d
         if (n >= ((size_t)1 << 32)) return SCAN_ERR_INVALID;
         if (n > 0 && ranges_partially_overlap(in, out, n * 4, n * 4)) return SCAN_ERR_INVALID;
         if (ranges_partially_overlap(d_count, out, 4, n * 4) || (void*)d_count == out) return SCAN_ERR_INVALID;
+        if (n > 0 && (ranges_partially_overlap(d_count, in, 4, n * 4) || (const void*)d_count == in))
+            return SCAN_ERR_INVALID;
         const Call c{in, out, nullptr, d_count, n, static_cast<hipStream_t>(stream)};
         const bool vec_ok = is_aligned(in, 16);
         switch (dtype) {

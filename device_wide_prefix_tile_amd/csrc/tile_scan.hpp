@@ -628,7 +628,9 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //    early; the tile-number ring is safe by the same argument.
 //  * Progress.  Every wait is on lower tiles or on the resolver, which only
 //    waits for totals; a total is published before its workgroup waits for
-//    any later prefix; every wait is bounded by the spin limit.
+//    any later prefix; every wait, on status words and on the LDS rings, is
+//    bounded by the spin limit, and a wait that gives up makes the others of
+//    the launch give up too (lookback.hpp, give_up).
 constexpr int kPipeSlots = 16;  // >= 2 * WAIT (see the ring note above)
 // Tiles per lane of the resolver's window (64 * span tiles per poll round),
 // as measured at full size: windows of 64 tiles against 128 and 256 —
@@ -807,10 +809,17 @@ __device__ __forceinline__ void hand_over_slot(const ScanParams& p, uint32_t til
     if (lane == 0) publish<Op>(p.lb, p.lb.status, (uint64_t)tile * DWPT_AGG_PAD, Op::to_carry(total), kStateAggregate);
 }
 
-__device__ __forceinline__ void wait_seq(uint32_t* seq, uint32_t want)
+// LDS waits are bounded like the status-word waits (lookback.hpp, give_up):
+// on giving up the wavefront goes on with what the slot holds, so every wave
+// still exits (the launch's results are then wrong and flagged).
+__device__ __forceinline__ void wait_seq(const Lookback& lb, uint32_t* seq, uint32_t want)
 {
-    while (__hip_atomic_load(seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < want)
+    uint64_t polls = 0;
+    const uint64_t limit = lds_poll_limit(lb);
+    while (__hip_atomic_load(seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < want) {
+        if (give_up(lb, polls, limit)) return;
         __builtin_amdgcn_s_sleep(1);
+    }
 }
 
 
@@ -833,10 +842,16 @@ __device__ __forceinline__ void put_id(TileIdRing* r, uint32_t k, uint32_t id)
     __hip_atomic_store(&r->seq[k % kPipeSlots], k + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ uint32_t get_id(TileIdRing* r, uint32_t k)
+// The k-th tile number of the workgroup; UINT32_MAX (past every tile: the
+// caller's loop ends) if the wait gives up.
+__device__ __forceinline__ uint32_t get_id(const Lookback& lb, TileIdRing* r, uint32_t k)
 {
-    while (__hip_atomic_load(&r->seq[k % kPipeSlots], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < k + 1)
+    uint64_t polls = 0;
+    const uint64_t limit = lds_poll_limit(lb);
+    while (__hip_atomic_load(&r->seq[k % kPipeSlots], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < k + 1) {
+        if (give_up(lb, polls, limit)) return UINT32_MAX;
         __builtin_amdgcn_s_sleep(1);
+    }
     return r->id[k % kPipeSlots];
 }
 
@@ -936,10 +951,11 @@ __device__ __forceinline__ void post_id(const ScanParams& p, TileIdRing* ids, ui
 template <class Op, class Slot>
 __device__ __forceinline__ void fetch_prefixes(const ScanParams& p, TileIdRing* ids, Slot* slots)
 {
+    uint64_t polls = 0;
     for (uint32_t k = 0;; ++k) {
-        const uint32_t tile = get_id(ids, k);
+        const uint32_t tile = get_id(p.lb, ids, k);
         if (tile >= p.num_tiles) break;
-        const typename Op::carry_t excl = wait_excl<Op>(p.lb, p.lb.groups, tile);
+        const typename Op::carry_t excl = wait_excl<Op>(p.lb, p.lb.groups, tile, polls);
         Slot* slot = &slots[k % kPipeSlots];
         if (lane_id() == 0) {
             slot->prefix = excl;
@@ -1272,8 +1288,8 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
     uint32_t h0[R], h1[R];
     V lx;
     WaveTile<G> t0, t1;
-    t0.set(p, get_id(s_ids, 0), w);
-    t1.set(p, get_id(s_ids, 1), w);
+    t0.set(p, get_id(p.lb, s_ids, 0), w);
+    t1.set(p, get_id(p.lb, s_ids, 1), w);
     if (t0.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t0.base, t0.vec, lane, e0, h0);
     if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t1.base, t1.vec, lane, e1, h1);
     if (t1.tile < p.num_tiles)
@@ -1299,7 +1315,7 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
             if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t1.base, t1.vec, lane, e1, h1);
         }
         Slot* slot = &s_slot[k % kPipeSlots];
-        wait_seq(&slot->prefix_seq, k + 1);
+        wait_seq(p.lb, &slot->prefix_seq, k + 1);
         V wave_prefix = Op::identity();
 #pragma unroll
         for (int q = 0; q < ND; ++q)
@@ -1315,7 +1331,7 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
             for (int j = 0; j < VEC; ++j) e0[r][j] = e1[r][j];
         }
         if (w == 0) post_id(p, s_ids, k + 2, next_id, exhausted);
-        t1.set(p, get_id(s_ids, k + 2), w);
+        t1.set(p, get_id(p.lb, s_ids, k + 2), w);
     }
     if (w == 0 && lane == 0) retire_workgroup(p);
 }
@@ -1375,7 +1391,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     V lx[kPipeTiles];
     WaveTile<G> t[kPipeTiles];
 #pragma unroll
-    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id(&s_ids, q), w);
+    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id(p.lb, &s_ids, q), w);
     // the first batch: every tile loaded and its total published up front
 #pragma unroll
     for (int q = 0; q < kPipeTiles; ++q)
@@ -1400,7 +1416,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
                                          &s_slot[(k + PUB) % kPipeSlots]);
 
         Slot* slot = &s_slot[k % kPipeSlots];
-        wait_seq(&slot->prefix_seq, k + 1);
+        wait_seq(p.lb, &slot->prefix_seq, k + 1);
         if constexpr (BLK) {
             V wave_prefix = Op::identity();
 #pragma unroll
@@ -1433,7 +1449,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
             }
         }
         if (w == 0) post_id(p, &s_ids, k + kPipeTiles, next_id, exhausted);
-        t[NEW].set(p, get_id(&s_ids, k + kPipeTiles), w);
+        t[NEW].set(p, get_id(p.lb, &s_ids, k + kPipeTiles), w);
     }
     if (w == 0 && lane == 0) retire_workgroup(p);
 }
@@ -1508,7 +1524,7 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
     uint32_t hu[R];
     WaveTile<G> t[kPipeTiles];
 #pragma unroll
-    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id(&s_ids, q), w);
+    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id(p.lb, &s_ids, q), w);
 #pragma unroll
     for (int q = 0; q < kPipeTiles - 1; ++q)
         if (t[q].tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, t[q].base, t[q].vec, lane, e[q], hu);
@@ -1528,7 +1544,7 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
         uint32_t kept[R];
         kept_bits(e[0], t[0].base, kept);
         const uint32_t cnt = pack_wave<T, R, VEC>(e[0], kept, region);
-        wait_seq(&slot->prefix_seq, k + 1);
+        wait_seq(p.lb, &slot->prefix_seq, k + 1);
         uint32_t wave_prefix = 0;
 #pragma unroll
         for (int q = 0; q < ND; ++q)
@@ -1544,7 +1560,7 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
                 for (int j = 0; j < VEC; ++j) e[q][r][j] = e[q + 1][r][j];
         }
         if (w == 0) post_id(p, &s_ids, k + kPipeTiles, next_id, exhausted);
-        t[NEW].set(p, get_id(&s_ids, k + kPipeTiles), w);
+        t[NEW].set(p, get_id(p.lb, &s_ids, k + kPipeTiles), w);
     }
     if (w == 0 && lane == 0) retire_workgroup(p);
 }

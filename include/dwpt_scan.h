@@ -52,7 +52,15 @@
  * Integer ADD wraps modulo 2^32.  F32 ADD results may differ from an exact
  * sum by rounding (any association is allowed); the prefix carried between
  * tiles is kept in double so the error stays well inside
- * 1e-5 * sum_{k<=i} |x_k| + 1e-6.  MAX/MIN keep the earlier value on ties.
+ * 1e-5 * sum_{k<=i} |x_k| + 1e-6.  MAX/MIN keep the earlier value on ties
+ * (for F32: of +0 and -0, whichever comes first).  F32 MAX/MIN inputs must
+ * not hold NaN: NaN is unordered, the operator is then not associative, and
+ * results would depend on the kernel path (unsupported, unspecified).
+ *
+ * Bounded waits: tiles wait for one another on the device.  Every such wait
+ * gives up after a poll budget (scan_set_spin_limit); the first one that does
+ * records SCAN_ERR_TIMEOUT (see scan_get_device_error) and makes every other
+ * wait of the same call give up at its next check, so a call always finishes.
  */
 #ifndef DWPT_SCAN_H
 #define DWPT_SCAN_H
@@ -143,7 +151,12 @@ scan_status_t segmented_scan(scan_op_t op, scan_dtype_t dtype, const void* in,
  * out[count .. n) is left untouched.  The write position of a kept element
  * is the exclusive scan of the 0/1 predicate flags [L7 concept 2 compaction
  * figure; PMPP9 §9.6 array compaction; YLY §2.2 flag/pos example].  -0.0
- * and NaN are not kept.  Requires n < 2^32.
+ * and NaN are not kept.  Requires n < 2^32.  out may equal in (in place);
+ * d_count must overlap neither in nor out (SCAN_ERR_INVALID).  In place, the
+ * reduce-then-scan mode (scan_set_multi_tile_mode(3)) is not used: its last
+ * pass would write a tile's kept elements over input that earlier tiles of
+ * the same launch may not have read yet, so the call runs the single-pass
+ * kernels instead.
  */
 scan_status_t compact(scan_dtype_t dtype, const void* in, void* out, uint32_t* d_count, size_t n,
                       void* stream);

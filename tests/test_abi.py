@@ -110,6 +110,11 @@ def test_argument_checks_before_any_launch():
     assert L.segmented_scan(ADD, I32, 1024, 8192, 8192, 10, 0, None) == binding.SCAN_ERR_INVALID
     assert L.compact(F32, 1024, 8192, None, 10, None) == binding.SCAN_ERR_INVALID
     assert L.compact(F32, 1024, 8192, 1 << 20, 1 << 32, None) == binding.SCAN_ERR_INVALID
+    # the count may not overlap the input (nor the output): reduce-then-scan writes it
+    # before its last pass reads the input again
+    assert L.compact(F32, 1024, 8192, 1024 + 8, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.compact(F32, 1024, 8192, 1024, 10, None) == binding.SCAN_ERR_INVALID
+    assert L.compact(F32, 1024, 8192, 8192 + 36, 10, None) == binding.SCAN_ERR_INVALID
     assert L.scan_copy_probe(1024, 2048, 10, None) == binding.SCAN_ERR_INVALID
     # CSR row offsets: row_ptr required and aligned, indices required when nnz > 0,
     # no overlap at all, nnz below 2^32

@@ -406,6 +406,122 @@ def test_compact_leaves_tail_untouched():
     assert np.all(o[cnt:] == 12345.0)
 
 
+@pytest.mark.parametrize("kept", ["none", "all"])
+@pytest.mark.parametrize("path", ["auto", "multi", "fallback", "rts"])
+def test_compact_none_or_all_kept_large(kept, path):
+    """Compaction that keeps nothing or everything at a size that runs the persistent kernel
+    by default ([L7] concept 2 compaction figure: the count is the last exclusive flag
+    position plus the last flag): count 0 with the output untouched, or count n with the
+    output equal to the input."""
+    n = (1 << 24) + 17
+    base = np.abs(si.float32_normal(66, n))
+    if kept == "none":
+        x = -base
+        x[::7] = -0.0
+        x[3::11] = 0.0
+    else:
+        x = base + np.float32(1e-30)
+        x[5::13] = np.float32(1e-45)  # the smallest subnormal is > 0 and kept
+    xd = to_dev(x)
+    out = torch.full((n,), 7.0, dtype=torch.float32, device="cuda")
+    with Path(path):
+        o, cnt = dw.compact(xd, out=out)
+        o, cnt = from_dev(o), int(from_dev(cnt)[0])
+    ref, rc, _ = oracle.compact(x)
+    assert rc == (0 if kept == "none" else n)
+    assert cnt == rc, "compact %s path=%s: count %d" % (kept, path, cnt)
+    if kept == "none":
+        assert np.all(o == np.float32(7.0)), "output written although nothing was kept"
+    else:
+        assert_equal(o, ref, "compact all path=%s" % path)
+    assert dw.scan_get_device_error() == 0
+
+
+# ---------------------------------------------------------------- float max/min ties
+# The tie reading for float max and min: a later value replaces the running one only when
+# strictly greater (smaller), so of +0 and -0 the earlier one stays ([PMPP9] §9.1 identity
+# table; [L7] concept 1: the order of operands is fixed, commutativity is not assumed).
+# +0 and -0 are the only distinct floats that compare equal, so they are the only inputs
+# that can show an operand swap in a float max/min combine.  The arrays below put the first
+# zero at positions on lane (4 elements), round (256), wavefront (1024) and tile (15360)
+# boundaries and follow it with zeros of both signs, so that any level of the kernel that
+# folded a later zero before an earlier one (lanes, DPP steps, wavefronts, tile totals, the
+# carry between tiles) would change the sign of some output.
+TIE_FIRSTS = [0, 1, 3, 4, 5, 255, 256, 1023, 1024, 1025, 4096, TILE - 1, TILE, TILE + 1, 2 * TILE - 3,
+              3 * TILE + 1000]
+
+
+def signed_zero_input(seed, n, first, op, sign):
+    """Values that never win before `first`; a zero of the given sign at `first`; after it,
+    zeros of both signs (3 of 4) mixed with values that never win."""
+    u = si.uint32_full(seed, n)
+    lose = np.float32(-1.0) if op == "max" else np.float32(1.0)
+    x = np.where(u % 4 == 0, lose * (1 + (u >> 8) % 5).astype(np.float32),
+                 np.where((u >> 2) % 2 == 0, np.float32(0.0), np.float32(-0.0))).astype(np.float32)
+    x[:first] = lose * np.float32(3.0)
+    x[first] = np.float32(0.0) if sign > 0 else np.float32(-0.0)
+    return x
+
+
+@pytest.mark.parametrize("op", ["max", "min"])
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_float_minmax_signed_zero_ties(op, exclusive):
+    fn = dw.scan_exclusive if exclusive else dw.scan_inclusive
+    n = 4 * TILE + 17
+    for k, first in enumerate(TIE_FIRSTS):
+        for sign in (1, -1):
+            x = signed_zero_input(1000 + 2 * k + (sign < 0), n, first, op, sign)
+            ref = oracle.scan(op, x, exclusive=exclusive)
+            assert np.signbit(ref[-1]) == (sign < 0)
+            xd = to_dev(x)
+            for path in ("single", "multi", "fallback", "rts", "auto"):
+                with Path(path):
+                    y = from_dev(fn(xd, op))
+                assert_equal(y.view(np.uint32), ref.view(np.uint32),
+                             "%s excl=%s first=%d sign=%d path=%s" % (op, exclusive, first, sign, path))
+
+
+@pytest.mark.parametrize("op", ["max", "min"])
+def test_float_minmax_signed_zero_ties_large(op):
+    """The same at a size the persistent kernel takes by default, the first zero deep in the
+    array (thousands of tiles of carry before and after it)."""
+    n = (1 << 24) + 17
+    first = (1 << 24) - 3 * TILE + 5
+    for sign in (1, -1):
+        x = signed_zero_input(1100 + (sign < 0), n, first, op, sign)
+        xd = to_dev(x)
+        for exclusive in (False, True):
+            ref = oracle.scan(op, x, exclusive=exclusive)
+            for path in ("auto", "multi", "fallback", "rts"):
+                with Path(path):
+                    y = from_dev((dw.scan_exclusive if exclusive else dw.scan_inclusive)(xd, op))
+                assert_equal(y.view(np.uint32), ref.view(np.uint32),
+                             "%s excl=%s sign=%d path=%s" % (op, exclusive, sign, path))
+    assert dw.scan_get_device_error() == 0
+
+
+@pytest.mark.parametrize("op", ["max", "min"])
+@pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
+def test_segmented_float_minmax_signed_zero_ties(op, exclusive):
+    """Segmented float max/min: every segment restarts, so every segment's first zero is a
+    tie decision -- thousands per array, at segment heads spread over lanes, wavefronts and
+    tiles (mean segment length 37, plus heads at every tile start)."""
+    for k, n in enumerate([TILE_SEG - 1, 3 * TILE_SEG + 17, 250001, (1 << 24) + 17]):
+        u = si.uint32_full(1200 + k, n)
+        lose = np.float32(-1.0) if op == "max" else np.float32(1.0)
+        x = np.where(u % 3 == 0, lose, np.where((u >> 2) % 2 == 0, np.float32(0.0),
+                                                np.float32(-0.0))).astype(np.float32)
+        h = si.segment_heads(1300 + k, n, 37.0)
+        h[::TILE_SEG] = 1
+        ref = oracle.segmented_scan(op, x, h, exclusive=exclusive)
+        xd, hd = to_dev(x), to_dev(h)
+        for path in (paths_for(n) if n < (1 << 24) else ["auto", "multi", "rts"]):
+            with Path(path):
+                y = from_dev(dw.segmented_scan(xd, hd, op, exclusive=exclusive))
+            assert_equal(y.view(np.uint32), ref.view(np.uint32),
+                         "seg %s excl=%s n=%d path=%s" % (op, exclusive, n, path))
+
+
 # ---------------------------------------------------------------- closed forms, layouts
 def test_all_ones_float_is_bit_exact():
     # every prefix of ones is an integer <= 2^24: exact in float32 under any association
@@ -417,23 +533,30 @@ def test_all_ones_float_is_bit_exact():
     np.testing.assert_array_equal(yi, np.arange(1, n + 1, dtype=np.float32))
 
 
+@pytest.mark.parametrize("path", ["auto", "single", "multi", "fallback", "rts"])
 @pytest.mark.parametrize("n", [5000, 1000003])
-def test_in_place(n):
-    x = si.int32_full(61, n)
-    t = to_dev(x)
-    dw.scan_inclusive(t, "add", out=t)
-    assert_equal(from_dev(t), oracle.scan("add", x), "in-place scan n=%d" % n)
-    h = si.segment_heads(62, n, 50.0)
-    t = to_dev(x)
-    dw.segmented_scan(t, to_dev(h), "max", exclusive=True, out=t)
-    assert_equal(from_dev(t), oracle.segmented_scan("max", x, h, exclusive=True), "in-place seg n=%d" % n)
-    f = si.float32_normal(63, n)
-    t = to_dev(f)
-    _, cnt = dw.compact(t, out=t)
-    ref, rc, _ = oracle.compact(f)
-    cnt = int(from_dev(cnt)[0])
-    assert cnt == rc
-    assert_equal(from_dev(t)[:cnt], ref, "in-place compact n=%d" % n)
+def test_in_place(n, path):
+    """out == in on every kernel path.  Reduce-then-scan compaction would write a tile's kept
+    elements below the tile while earlier tiles of the same launch may not have read theirs
+    yet, so in place it runs the single-pass kernel instead; the scans are safe there (each
+    tile reads, then writes, only its own range)."""
+    with Path(path):
+        x = si.int32_full(61, n)
+        t = to_dev(x)
+        dw.scan_inclusive(t, "add", out=t)
+        assert_equal(from_dev(t), oracle.scan("add", x), "in-place scan n=%d path=%s" % (n, path))
+        h = si.segment_heads(62, n, 50.0)
+        t = to_dev(x)
+        dw.segmented_scan(t, to_dev(h), "max", exclusive=True, out=t)
+        assert_equal(from_dev(t), oracle.segmented_scan("max", x, h, exclusive=True),
+                     "in-place seg n=%d path=%s" % (n, path))
+        for k, f in enumerate([si.float32_normal(63, n), np.abs(si.float32_normal(64, n)) + np.float32(1)]):
+            t = to_dev(f)
+            _, cnt = dw.compact(t, out=t)
+            ref, rc, _ = oracle.compact(f)
+            cnt = int(from_dev(cnt)[0])
+            assert cnt == rc, "in-place compact %d n=%d path=%s" % (k, n, path)
+            assert_equal(from_dev(t)[:cnt], ref, "in-place compact %d n=%d path=%s" % (k, n, path))
 
 
 @pytest.mark.parametrize("n", [4097, 1000003])
