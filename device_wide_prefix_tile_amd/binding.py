@@ -23,7 +23,7 @@ _DTYPES = {torch.int32: SCAN_I32, torch.uint32: SCAN_U32, torch.float32: SCAN_F3
 EXPORTS = ("scan_inclusive", "scan_exclusive", "segmented_scan", "compact", "scan_status_string",
            "scan_get_device_error", "scan_release_workspace", "scan_set_small_n_max",
            "scan_set_spin_limit", "scan_set_multi_tile_mode", "scan_copy_probe", "csr_row_offsets",
-           "radix_split")
+           "radix_split", "scan_noalloc")
 
 _lib = None
 
@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         "scan_copy_probe": ([P, P, S, P], I),
         "csr_row_offsets": ([P, S, U, P, P], I),
         "radix_split": ([P, P, S, U, P, P, P], I),
+        "scan_noalloc": ([I, I, P, P, S, I, P], I),
     }
     for name, (argtypes, restype) in sig.items():
         fn = getattr(L, name)
@@ -144,6 +145,18 @@ def scan_exclusive(x: torch.Tensor, op: str = "add", out: torch.Tensor | None = 
     out = _prep(x, out)
     _check(lib().scan_exclusive(OPS[op], dt, x.data_ptr(), out.data_ptr(), x.shape[0], _stream(stream)),
            "scan_exclusive")
+    return out
+
+
+def scan_noalloc(x: torch.Tensor, op: str = "add", exclusive: bool = False, out: torch.Tensor | None = None,
+                 stream=None):
+    """scan_inclusive / scan_exclusive without any device allocation by the library (its status
+    words live in a static per-GPU array; calls overlapping on one GPU race).  `out` must be
+    given by callers that cannot allocate."""
+    dt = _dtype_code(x, op)
+    out = _prep(x, out)
+    _check(lib().scan_noalloc(OPS[op], dt, x.data_ptr(), out.data_ptr(), x.shape[0], 1 if exclusive else 0,
+                              _stream(stream)), "scan_noalloc")
     return out
 
 

@@ -157,6 +157,74 @@ hipError_t zero_async(void* p, size_t bytes, hipStream_t s)
     return hipGetLastError();
 }
 
+// Header words and status array of a workspace whose memory starts at mem.
+void lay_out(Workspace& ws, void* mem, size_t status_words)
+{
+    ws.mem = mem;
+    ws.status_words = status_words;
+    ws.err = static_cast<uint32_t*>(mem);
+    ws.ctr = static_cast<uint32_t*>(mem) + 1;
+    ws.pipe_ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + 128);
+    ws.abort = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + 512);
+    ws.status = reinterpret_cast<uint64_t*>(static_cast<char*>(mem) + kHeaderBytes);
+    ws.ctr_base = 0;
+    ws.epoch = 0;
+}
+
+// Called with g_mu held: the next call's epoch.  At the wrap every tag of the
+// array (and the abort word) could alias the new epoch: they are cleared.
+scan_status_t next_epoch(Workspace& ws, hipStream_t s)
+{
+    ws.epoch += 1;
+    if (ws.epoch >= (1u << kEpochBits)) {
+        if (zero_async(ws.status, ws.status_words * 8, s) != hipSuccess) return SCAN_ERR_HIP;
+        if (zero_async(ws.abort, 128, s) != hipSuccess) return SCAN_ERR_HIP;
+        ws.epoch = 1;
+    }
+    return SCAN_OK;
+}
+
+// ------------------------------------------------------------ static scratch
+// Device memory of the allocation-free entry point (scan_noalloc): the same
+// header and status words as a stream workspace, in a static array that each
+// GPU the library runs on holds until the process ends.  In host code the
+// array's name is not a device address: each device's address comes from
+// hipGetSymbolAddress, once, at that device's first call (with the device
+// current), and is kept in g_static; kernels receive that address.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+constexpr size_t kScratchStatusWords = (kScratchBytes - kHeaderBytes) / 8;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+struct StaticScratch {
+    bool ready = false;
+    Workspace ws;
+};
+StaticScratch g_static[kMaxDevices];
+
+// Called with g_mu held: the current device's scratch (set up and cleared on
+// its first call, with a fill kernel on the call's stream), epoch advanced.
+scan_status_t static_workspace(hipStream_t s, Workspace** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SCAN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SCAN_ERR_UNSUPPORTED;
+    StaticScratch& st = g_static[dev];
+    if (!st.ready) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return SCAN_ERR_HIP;
+        }
+        if (zero_async(ptr, kScratchBytes, s) != hipSuccess) return SCAN_ERR_HIP;
+        lay_out(st.ws, ptr, kScratchStatusWords);
+        st.ready = true;
+    }
+    const scan_status_t e = next_epoch(st.ws, s);
+    if (e != SCAN_OK) return e;
+    *out = &st.ws;
+    return SCAN_OK;
+}
+
 // Called with g_mu held.  Makes sure the (device, stream) workspace holds at
 // least `words` status words and advances its epoch for a new call.
 scan_status_t acquire_workspace(hipStream_t s, size_t words, Workspace** out)
@@ -183,23 +251,10 @@ scan_status_t acquire_workspace(hipStream_t s, size_t words, Workspace** out)
             (void)hipFree(mem);
             return SCAN_ERR_HIP;
         }
-        ws.mem = mem;
-        ws.status_words = cap;
-        ws.err = static_cast<uint32_t*>(mem);
-        ws.ctr = static_cast<uint32_t*>(mem) + 1;
-        ws.pipe_ctr = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + 128);
-        ws.abort = reinterpret_cast<uint32_t*>(static_cast<char*>(mem) + 512);
-        ws.status = reinterpret_cast<uint64_t*>(static_cast<char*>(mem) + kHeaderBytes);
-        ws.ctr_base = 0;
-        ws.epoch = 0;
+        lay_out(ws, mem, cap);
     }
-    ws.epoch += 1;
-    if (ws.epoch >= (1u << kEpochBits)) {
-        // every tag of the array (and the abort word) could now alias the new epoch: clear them
-        if (zero_async(ws.status, ws.status_words * 8, s) != hipSuccess) return SCAN_ERR_HIP;
-        if (zero_async(ws.abort, 128, s) != hipSuccess) return SCAN_ERR_HIP;
-        ws.epoch = 1;
-    }
+    const scan_status_t e = next_epoch(ws, s);
+    if (e != SCAN_OK) return e;
     *out = &ws;
     return SCAN_OK;
 }
@@ -253,36 +308,51 @@ struct Call {
     uint32_t* count;
     size_t n;
     hipStream_t stream;
+    bool noalloc = false;  // status words in the static scratch; nothing allocated
 };
 
 bool is_aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Compute units of the current device (cached; called with g_mu held).
+// Compute units of the current device (cached in a fixed table, so that no
+// call allocates host memory either; called with g_mu held).
 int device_cus()
 {
-    static std::map<int, int> cache;
+    static int cache[kMaxDevices];  // 0: not asked yet
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 1;
-    auto it = cache.find(dev);
-    if (it != cache.end()) return it->second;
+    if (dev >= 0 && dev < kMaxDevices && cache[dev] > 0) return cache[dev];
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
         (void)hipGetLastError();
         cus = 1;
     }
-    cache[dev] = cus;
+    if (dev >= 0 && dev < kMaxDevices) cache[dev] = cus;
     return cus;
 }
 
-// Resident workgroups of kernel `f` on the current device (cached).
+// Resident workgroups of kernel `f` on the current device (cached in a fixed
+// open-addressing table keyed by device and kernel; called with g_mu held).
 int resident_capacity(const void* f, int block)
 {
-    static std::map<std::pair<int, const void*>, int> cache;
+    struct Entry {
+        const void* f;
+        int dev;
+        int cap;
+    };
+    constexpr int kEntries = 1024;
+    static Entry cache[kEntries];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    const auto key = std::make_pair(dev, f);
-    auto it = cache.find(key);
-    if (it != cache.end()) return it->second;
+    const size_t h = ((uintptr_t)f >> 4) * 31u + (size_t)dev;
+    int slot = -1;
+    for (int i = 0; i < kEntries; ++i) {
+        Entry& e = cache[(h + i) % kEntries];
+        if (e.f == f && e.dev == dev) return e.cap;
+        if (e.f == nullptr) {
+            slot = (int)((h + i) % kEntries);
+            break;
+        }
+    }
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, block, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
@@ -290,7 +360,7 @@ int resident_capacity(const void* f, int block)
         per_cu = 0;
     }
     const int cap = per_cu * cus;
-    cache[key] = cap;
+    if (slot >= 0) cache[slot] = Entry{f, dev, cap};
     return cap;
 }
 
@@ -326,6 +396,11 @@ scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(
     if (tiles > 0xFFFFFFFFull) return SCAN_ERR_INVALID;
     p.num_tiles = (uint32_t)tiles;
     p.vec_ok = vec_ok ? 1 : 0;
+    // per tile: its status (AGG_PAD entries apart), then a second array for group statuses
+    // (one-tile-per-workgroup kernel) or the resolver's published prefixes (persistent
+    // kernel, PREFIX_PAD entries apart: one prefix per 128-byte line)
+    const size_t words = (size_t)tiles * kWords * (DWPT_AGG_PAD + DWPT_PREFIX_PAD);
+    if (c.noalloc && words > kScratchStatusWords) return SCAN_ERR_INVALID;  // beyond the static scratch
 
     std::lock_guard<std::mutex> lock(g_mu);
     if (c.n <= g_small_n_max) {
@@ -333,12 +408,10 @@ scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(
         return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
     }
     Workspace* ws = nullptr;
-    // per tile: its status (AGG_PAD entries apart), then a second array for group statuses
-    // (one-tile-per-workgroup kernel) or the resolver's published prefixes (persistent
-    // kernel, PREFIX_PAD entries apart: one prefix per 128-byte line)
-    const scan_status_t st = acquire_workspace(c.stream, (size_t)tiles * kWords * (DWPT_AGG_PAD + DWPT_PREFIX_PAD), &ws);
+    const scan_status_t st = c.noalloc ? static_workspace(c.stream, &ws) : acquire_workspace(c.stream, words, &ws);
     if (st != SCAN_OK) return st;
-    if (g_multi_mode == 3 && rts_ok) {
+    // reduce-then-scan needs a carry buffer: not on the allocation-free path
+    if (g_multi_mode == 3 && rts_ok && !c.noalloc) {
         // 2T + 1 plain carries: the tile totals, the grand total, the prefixes
         const scan_status_t sr = acquire_rts(c.stream, *ws, (2 * (size_t)tiles + 1) * sizeof(C));
         if (sr != SCAN_OK) return sr;
@@ -462,7 +535,7 @@ bool ranges_partially_overlap(const void* a, const void* b, size_t bytes_a, size
 }
 
 scan_status_t plain_scan(bool excl, scan_op_t op, scan_dtype_t dt, const void* in, void* out, size_t n,
-                         void* stream)
+                         void* stream, bool noalloc = false)
 {
     if ((unsigned)op > SCAN_OP_OR || (unsigned)dt > SCAN_U32X9) return SCAN_ERR_UNSUPPORTED;
     const Runner r = excl ? plain_runner<true>(op, dt) : plain_runner<false>(op, dt);
@@ -473,7 +546,7 @@ scan_status_t plain_scan(bool excl, scan_op_t op, scan_dtype_t dt, const void* i
     if (!is_aligned(in, elem_align(dt)) || !is_aligned(out, elem_align(dt))) return SCAN_ERR_INVALID;
     if (n > ((size_t)1 << 40)) return SCAN_ERR_INVALID;
     if (ranges_partially_overlap(in, out, n * es, n * es)) return SCAN_ERR_INVALID;
-    const Call c{in, out, nullptr, nullptr, n, static_cast<hipStream_t>(stream)};
+    const Call c{in, out, nullptr, nullptr, n, static_cast<hipStream_t>(stream), noalloc};
     return r(c, is_aligned(in, 16) && is_aligned(out, 16));
 }
 
@@ -497,6 +570,16 @@ scan_status_t scan_exclusive(scan_op_t op, scan_dtype_t dtype, const void* in, v
 {
     try {
         return plain_scan(true, op, dtype, in, out, n, stream);
+    } catch (const std::bad_alloc&) {
+        return SCAN_ERR_NOMEM;
+    }
+}
+
+scan_status_t scan_noalloc(scan_op_t op, scan_dtype_t dtype, const void* in, void* out, size_t n, int exclusive,
+                          void* stream)
+{
+    try {
+        return plain_scan(exclusive != 0, op, dtype, in, out, n, stream, true);
     } catch (const std::bad_alloc&) {
         return SCAN_ERR_NOMEM;
     }
@@ -663,13 +746,25 @@ scan_status_t scan_get_device_error(void* stream)
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SCAN_ERR_HIP;
         std::lock_guard<std::mutex> lock(g_mu);
+        // the stream's workspace and the device's static scratch (scan_noalloc calls)
+        uint32_t* words[2] = {nullptr, nullptr};
         auto it = g_ws.find(std::make_pair(dev, (void*)s));
-        if (it == g_ws.end() || !it->second.mem) return SCAN_OK;
+        if (it != g_ws.end() && it->second.mem) words[0] = it->second.err;
+        if (dev >= 0 && dev < kMaxDevices && g_static[dev].ready) {
+            // its calls may sit on any stream of the device
+            if (hipDeviceSynchronize() != hipSuccess) return SCAN_ERR_HIP;
+            words[1] = g_static[dev].ws.err;
+        }
         uint32_t err = 0;
-        if (hipMemcpy(&err, it->second.err, 4, hipMemcpyDeviceToHost) != hipSuccess) return SCAN_ERR_HIP;
-        if (err) {
-            const uint32_t zero = 0;
-            if (hipMemcpy(it->second.err, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return SCAN_ERR_HIP;
+        for (uint32_t* w : words) {
+            if (!w) continue;
+            uint32_t e = 0;
+            if (hipMemcpy(&e, w, 4, hipMemcpyDeviceToHost) != hipSuccess) return SCAN_ERR_HIP;
+            if (e) {
+                const uint32_t zero = 0;
+                if (hipMemcpy(w, &zero, 4, hipMemcpyHostToDevice) != hipSuccess) return SCAN_ERR_HIP;
+            }
+            err |= e;
         }
         if (err & kErrTimeout) return SCAN_ERR_TIMEOUT;
         return err ? SCAN_ERR_HIP : SCAN_OK;

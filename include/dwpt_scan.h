@@ -196,15 +196,41 @@ scan_status_t csr_row_offsets(const uint32_t* row_idx, size_t nnz, uint32_t n_ro
 scan_status_t radix_split(const uint32_t* keys, const uint32_t* vals, size_t n, uint32_t shift,
                           uint32_t* keys_out, uint32_t* vals_out, void* stream);
 
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the plain
+ * inclusive (exclusive == 0) or exclusive scan, as scan_inclusive /
+ * scan_exclusive (same operators, types, results, alignment and overlap
+ * rules), that allocates nothing.  The tiles' status words and counters live
+ * in a static device array of the library, 16 MiB on each GPU it runs on,
+ * held until the process ends (set up and cleared on a GPU's first call, with
+ * a fill kernel on that call's stream).  Inputs whose status words do not fit
+ * are rejected with SCAN_ERR_INVALID before anything is launched: tiles *
+ * words * 17 * 8 bytes must fit in 16 MiB - 640 bytes, with tiles = ceil(n /
+ * tile) and (tile, words) = (15360, 1) for 4-byte integer ops, (15360, 2)
+ * for F32 ADD, (15360, 1) for F32 MAX/MIN, (7680, 2) AFFINE, (5760, 2)
+ * MAX_COUNT, (3840, 4) MAT2, (3584, 9) MAT3 -- e.g. n up to 947,374,080 for
+ * F32 ADD and 1,894,763,520 for I32 ADD.  Every call on a GPU shares that
+ * GPU's array (the last call's contents stay in it): calls that overlap in
+ * time on one GPU, e.g. on two streams, race and give wrong results; calls
+ * in one stream's order, or separated by synchronisation, are safe.  The
+ * reduce-then-scan mode (scan_set_multi_tile_mode(3)) is not used here (the
+ * automatic choice runs instead).  Device errors of these calls are reported
+ * by scan_get_device_error on the same device.
+ */
+scan_status_t scan_noalloc(scan_op_t op, scan_dtype_t dtype, const void* in, void* out, size_t n,
+                           int exclusive, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* scan_status_string(scan_status_t s);
 
 /*
  * Synchronises `stream`, then reads and clears the device error word of its
- * workspace: SCAN_ERR_TIMEOUT if a look-back wait gave up since the last
- * check (the results of that call are then wrong), SCAN_ERR_HIP if a
- * workgroup found the tile counter out of step with its launch (it then
- * skipped its tile), SCAN_OK otherwise.
+ * workspace (and, once scan_noalloc has run on the current device, after
+ * synchronising the device, that of its static array): SCAN_ERR_TIMEOUT if a
+ * look-back wait gave up since the last check (the results of that call are
+ * then wrong), SCAN_ERR_HIP if a workgroup found the tile counter out of
+ * step with its launch (it then skipped its tile), SCAN_OK otherwise.
  */
 scan_status_t scan_get_device_error(void* stream);
 
