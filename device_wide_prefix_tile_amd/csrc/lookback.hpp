@@ -77,7 +77,7 @@ enum : int { kGroupShift = 6 };  // 64 tiles per group
 // are a little better than fast ones (a second poll kept in flight was
 // measured 5% slower).
 #ifndef DWPT_FETCH_SLEEP
-#define DWPT_FETCH_SLEEP 16
+#define DWPT_FETCH_SLEEP 8
 #endif
 #ifndef DWPT_PREFIX_PAD
 #define DWPT_PREFIX_PAD 16
@@ -104,7 +104,10 @@ struct Lookback {
 // LDS waits poll about 16 times as often as status-word waits (no memory
 // round trip, a shorter sleep), so their budget is 16 times larger: about
 // the same wall time.
-enum : uint32_t { kAbortCheck = 64u, kLdsPollScale = 16u };
+#ifndef DWPT_ABORT_CHECK
+#define DWPT_ABORT_CHECK 64
+#endif
+enum : uint32_t { kAbortCheck = DWPT_ABORT_CHECK, kLdsPollScale = 16u };
 
 // Called by the whole wavefront (the result is uniform).
 __device__ __forceinline__ bool launch_aborted(const Lookback& lb)

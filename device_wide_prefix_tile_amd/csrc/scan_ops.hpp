@@ -91,10 +91,13 @@ template <> struct OpAdd<uint32_t> : SameCarry<uint32_t, OpAdd<uint32_t>> {
 };
 
 // float32 add: tiles are summed in float32, but the prefix carried from tile
-// to tile is a double, and each output is rounded once from
-// (carry in double) + (in-tile float partial).  The carry is split into a
-// float pair hi + lo once per thread so that the per-element work stays two
-// float32 adds: y = hi + (lo + local).
+// to tile is a double.  Each lane rounds the double prefix of its elements
+// (carry plus the in-tile prefix before them) to float once, and each output
+// is that float plus the element's in-lane float partial: two roundings per
+// output instead of one (a float pair hi + (lo + local) would round once),
+// well inside the tolerance, and one float32 add per element instead of two
+// (measured: 340.5 -> 339.2 us at 2^28 with identical worst error/tolerance).
+// The error that grows with n -- the carry's -- stays in double.
 struct F32Split {
     float hi, lo;
 };
@@ -109,13 +112,24 @@ template <> struct OpAdd<float> {
     __device__ __forceinline__ static double carry_identity() { return 0.0; }
     __device__ __forceinline__ static double to_carry(float v) { return (double)v; }
     __device__ __forceinline__ static double combine_carry(double a, double b) { return a + b; }
+#ifndef DWPT_F32_APPLY_HI
+#define DWPT_F32_APPLY_HI 1  // 0: the single-rounding hi + (lo + local)
+#endif
     __device__ __forceinline__ static F32Split prepare(double c)
     {
         float hi = (float)c;
+#if DWPT_F32_APPLY_HI
+        return {hi, 0.0f};
+#else
         float lo = (float)(c - (double)hi);
         return {hi, lo};
+#endif
     }
+#if DWPT_F32_APPLY_HI
+    __device__ __forceinline__ static float apply(F32Split c, float local) { return c.hi + local; }
+#else
     __device__ __forceinline__ static float apply(F32Split c, float local) { return c.hi + (c.lo + local); }
+#endif
     __device__ __forceinline__ static void pack(double c, uint32_t* w, uint32_t& flag) { to_words(c, w); flag = 0; }
     __device__ __forceinline__ static double unpack(const uint32_t* w, uint32_t) { return from_words<double>(w); }
 };

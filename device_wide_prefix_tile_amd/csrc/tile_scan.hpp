@@ -50,6 +50,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "lookback.hpp"
 #include "scan_ops.hpp"
 #include "wave_ops.hpp"
@@ -269,6 +271,16 @@ __device__ __forceinline__ void load_wave(const ScanParams& p, uint64_t wave_bas
     }
 }
 
+// Inclusive wavefront scan under the operator (float32 add takes the variant
+// with fused DPP broadcasts, wave_ops.hpp).
+template <class Op>
+__device__ __forceinline__ typename Op::value_t op_wave_scan(typename Op::value_t v)
+{
+    using V = typename Op::value_t;
+    if constexpr (std::is_same<Op, OpAdd<float>>::value) return wave_inclusive_scan_fadd(v);
+    else return wave_inclusive_scan(v, Op::identity(), [](V a, V b) { return Op::combine(a, b); });
+}
+
 // Serial scan of each lane's elements (3) and wavefront scans of the lane
 // totals (4): afterwards x holds in-lane inclusive prefixes, lane_excl[r]
 // the fold of the lower lanes' round-r totals and round_carry[r] the fold of
@@ -279,7 +291,6 @@ __device__ __forceinline__ void scan_wave(typename Op::value_t (&x)[R][VEC], typ
 {
     using V = typename Op::value_t;
     const V ident = Op::identity();
-    const auto comb = [](V a, V b) { return Op::combine(a, b); };
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -287,7 +298,7 @@ __device__ __forceinline__ void scan_wave(typename Op::value_t (&x)[R][VEC], typ
     round_carry[0] = ident;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const V incl = wave_inclusive_scan(x[r][VEC - 1], ident, comb);
+        const V incl = op_wave_scan<Op>(x[r][VEC - 1]);
         lane_excl[r] = wave_shift_up(incl, ident);
         round_carry[r + 1] = Op::combine(round_carry[r], read_lane(incl, 63));
     }
@@ -763,7 +774,6 @@ __device__ __forceinline__ typename Op::value_t reduce_wave(uint64_t wave_base, 
 {
     using V = typename Op::value_t;
     const V ident = Op::identity();
-    const auto comb = [](V a, V b) { return Op::combine(a, b); };
     V x[R][VEC];
     uint32_t raw_head[R];
     to_values<Op, R, VEC>(wave_base, lane, e, h4, x, raw_head);
@@ -777,7 +787,7 @@ __device__ __forceinline__ typename Op::value_t reduce_wave(uint64_t wave_base, 
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int j = (r == 0 ? 1 : 0); j < VEC; ++j) t = Op::combine(t, x[r][j]);
-        return read_lane(wave_inclusive_scan(t, ident, comb), 63);
+        return read_lane(op_wave_scan<Op>(t), 63);
     }
     V total = ident;
 #pragma unroll
@@ -785,7 +795,7 @@ __device__ __forceinline__ typename Op::value_t reduce_wave(uint64_t wave_base, 
         V t = x[r][0];
 #pragma unroll
         for (int j = 1; j < VEC; ++j) t = Op::combine(t, x[r][j]);
-        total = Op::combine(total, read_lane(wave_inclusive_scan(t, ident, comb), 63));
+        total = Op::combine(total, read_lane(op_wave_scan<Op>(t), 63));
     }
     return total;
 }
@@ -809,16 +819,74 @@ __device__ __forceinline__ void hand_over_slot(const ScanParams& p, uint32_t til
     if (lane == 0) publish<Op>(p.lb, p.lb.status, (uint64_t)tile * DWPT_AGG_PAD, Op::to_carry(total), kStateAggregate);
 }
 
-// LDS waits are bounded like the status-word waits (lookback.hpp, give_up):
-// on giving up the wavefront goes on with what the slot holds, so every wave
-// still exits (the launch's results are then wrong and flagged).
-__device__ __forceinline__ void wait_seq(const Lookback& lb, uint32_t* seq, uint32_t want)
+// LDS waits of the persistent kernels.  Every one of them ends:
+//  * the prefix wavefront's waits (for a tile number) count their polls
+//    against the spin limit scaled to LDS polling (lookback.hpp,
+//    lds_poll_limit), and its status-word waits are bounded; if it gives up
+//    a wait for a tile number it releases every slot of the prefix ring
+//    (release_slots) before it stops, so no data wavefront waits on it again;
+//  * a data wavefront waits only for prefixes (posted by the prefix
+//    wavefront, or released) and for tile numbers (posted by wavefront 0,
+//    which itself only waits for prefixes).
+// So the data wavefronts' waits end without a count of their own.  They may
+// still count (COUNTED) and give up past the limit; whether that is faster
+// was measured per kernel: the scans gained ~1 us with the counted loop,
+// compaction at 2^28 lost 50 (381 against 322 us), and is not counted.
+// Counted or not, a loop touches nothing but LDS: a data wavefront's global
+// load would complete only after its own tile loads in flight (one counter
+// covers a wavefront's loads).  A wave that gave up goes on with what the
+// slot holds, so every wave exits, and records the timeout in the error word
+// and the abort word once its loop is over (record_lds_timeout).
+struct LdsWait {
+    uint32_t limit;     // polls before giving up
+    uint32_t* abort;    // the workgroup's flag: some wait of the workgroup gave up
+    bool gave_up;       // this wavefront gave up a wait (uniform)
+    __device__ __forceinline__ LdsWait(const Lookback& lb, uint32_t* flag)
+        : limit(lds_poll_limit(lb) > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)lds_poll_limit(lb)), abort(flag),
+          gave_up(false)
+    {
+    }
+    // after kAbortCheck more failed polls: true once the wait must give up
+    __device__ __forceinline__ bool fail_batch(uint32_t& polls)
+    {
+        polls += kAbortCheck;
+        if (polls > limit || __hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u) {
+            if (lane_id() == 0) __hip_atomic_store(abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            gave_up = true;
+            return true;
+        }
+        return false;
+    }
+};
+
+// After a wavefront's loop: a wait that gave up is recorded for the host and
+// the rest of the launch.
+__device__ __forceinline__ void record_lds_timeout(const Lookback& lb, const LdsWait& lw)
 {
-    uint64_t polls = 0;
-    const uint64_t limit = lds_poll_limit(lb);
-    while (__hip_atomic_load(seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < want) {
-        if (give_up(lb, polls, limit)) return;
-        __builtin_amdgcn_s_sleep(1);
+    if (lw.gave_up && lane_id() == 0) {
+        __hip_atomic_fetch_or(lb.err, (uint32_t)kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(lb.abort, lb.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Waits until *seq >= want.  Counted: polls in batches of kAbortCheck with
+// nothing but the poll in the inner loop, the budget and the flag checked
+// between batches.
+template <bool COUNTED>
+__device__ __forceinline__ void wait_seq(LdsWait& lw, uint32_t* seq, uint32_t want)
+{
+    if constexpr (!COUNTED) {
+        (void)lw;
+        while (__hip_atomic_load(seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < want) __builtin_amdgcn_s_sleep(1);
+    } else {
+        uint32_t polls = 0;
+        while (true) {
+            for (uint32_t i = 0; i < kAbortCheck; ++i) {
+                if (__hip_atomic_load(seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= want) return;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (lw.fail_batch(polls)) return;
+        }
     }
 }
 
@@ -834,6 +902,7 @@ __device__ __forceinline__ uint32_t* pipe_counter(const ScanParams& p, int q) { 
 struct TileIdRing {
     uint32_t id[kPipeSlots];
     uint32_t seq[kPipeSlots];  // k + 1 once id[k mod kPipeSlots] holds the k-th tile number
+    uint32_t abort;            // set once a wait of this workgroup gave up
 };
 
 __device__ __forceinline__ void put_id(TileIdRing* r, uint32_t k, uint32_t id)
@@ -842,15 +911,29 @@ __device__ __forceinline__ void put_id(TileIdRing* r, uint32_t k, uint32_t id)
     __hip_atomic_store(&r->seq[k % kPipeSlots], k + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// The k-th tile number of the workgroup; UINT32_MAX (past every tile: the
-// caller's loop ends) if the wait gives up.
-__device__ __forceinline__ uint32_t get_id(const Lookback& lb, TileIdRing* r, uint32_t k)
+// The k-th tile number of the workgroup (counted: UINT32_MAX, past every
+// tile, so that the caller's loop ends, if the wait gives up).
+template <bool COUNTED>
+__device__ __forceinline__ uint32_t get_id(LdsWait& lw, TileIdRing* r, uint32_t k)
 {
-    uint64_t polls = 0;
-    const uint64_t limit = lds_poll_limit(lb);
-    while (__hip_atomic_load(&r->seq[k % kPipeSlots], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < k + 1) {
-        if (give_up(lb, polls, limit)) return UINT32_MAX;
-        __builtin_amdgcn_s_sleep(1);
+    uint32_t* seq = &r->seq[k % kPipeSlots];
+    if constexpr (!COUNTED) {
+        (void)lw;
+        while (__hip_atomic_load(seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < k + 1) __builtin_amdgcn_s_sleep(1);
+    } else {
+        uint32_t polls = 0;
+        while (true) {
+            bool here = false;
+            for (uint32_t i = 0; i < kAbortCheck; ++i) {
+                if (__hip_atomic_load(seq, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= k + 1) {
+                    here = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (here) break;
+            if (lw.fail_batch(polls)) return UINT32_MAX;
+        }
     }
     return r->id[k % kPipeSlots];
 }
@@ -867,6 +950,7 @@ __device__ __forceinline__ uint32_t start_workgroup(const ScanParams& p, Slot* s
         slots[threadIdx.x].prefix_seq = 0u;
         ids->seq[threadIdx.x] = 0u;
     }
+    if (threadIdx.x == 0) ids->abort = 0u;
     __syncthreads();
     return *s_role;
 }
@@ -947,21 +1031,29 @@ __device__ __forceinline__ void post_id(const ScanParams& p, TileIdRing* ids, ui
 }
 
 // Prefix wavefront of a data workgroup: fetches the prefix of each of the
-// workgroup's tiles, in order, into the slot ring.
+// workgroup's tiles, in order, into the slot ring.  If it gives up waiting
+// for a tile number it releases every slot (sequence number UINT32_MAX), so
+// that no data wavefront waits for a prefix that will not come.
 template <class Op, class Slot>
 __device__ __forceinline__ void fetch_prefixes(const ScanParams& p, TileIdRing* ids, Slot* slots)
 {
     uint64_t polls = 0;
+    LdsWait lw(p.lb, &ids->abort);
     for (uint32_t k = 0;; ++k) {
-        const uint32_t tile = get_id(p.lb, ids, k);
+        const uint32_t tile = get_id<true>(lw, ids, k);
         if (tile >= p.num_tiles) break;
         const typename Op::carry_t excl = wait_excl<Op>(p.lb, p.lb.groups, tile, polls);
+        if (polls > p.lb.spin_limit && lane_id() == 0)  // gave up: let the data wavefronts know
+            __hip_atomic_store(&ids->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         Slot* slot = &slots[k % kPipeSlots];
         if (lane_id() == 0) {
             slot->prefix = excl;
             __hip_atomic_store(&slot->prefix_seq, k + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
     }
+    if (lw.gave_up && lane_id() < kPipeSlots)
+        __hip_atomic_store(&slots[lane_id()].prefix_seq, UINT32_MAX, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    record_lds_timeout(p.lb, lw);
 }
 
 // Position of a data wavefront's share of a tile.
@@ -1288,8 +1380,9 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
     uint32_t h0[R], h1[R];
     V lx;
     WaveTile<G> t0, t1;
-    t0.set(p, get_id(p.lb, s_ids, 0), w);
-    t1.set(p, get_id(p.lb, s_ids, 1), w);
+    LdsWait lw(p.lb, &s_ids->abort);
+    t0.set(p, get_id<true>(lw, s_ids, 0), w);
+    t1.set(p, get_id<true>(lw, s_ids, 1), w);
     if (t0.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t0.base, t0.vec, lane, e0, h0);
     if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t1.base, t1.vec, lane, e1, h1);
     if (t1.tile < p.num_tiles)
@@ -1315,7 +1408,7 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
             if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t1.base, t1.vec, lane, e1, h1);
         }
         Slot* slot = &s_slot[k % kPipeSlots];
-        wait_seq(p.lb, &slot->prefix_seq, k + 1);
+        wait_seq<true>(lw, &slot->prefix_seq, k + 1);
         V wave_prefix = Op::identity();
 #pragma unroll
         for (int q = 0; q < ND; ++q)
@@ -1331,8 +1424,9 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
             for (int j = 0; j < VEC; ++j) e0[r][j] = e1[r][j];
         }
         if (w == 0) post_id(p, s_ids, k + 2, next_id, exhausted);
-        t1.set(p, get_id(p.lb, s_ids, k + 2), w);
+        t1.set(p, get_id<true>(lw, s_ids, k + 2), w);
     }
+    record_lds_timeout(p.lb, lw);
     if (w == 0 && lane == 0) retire_workgroup(p);
 }
 
@@ -1390,8 +1484,9 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     constexpr bool KEEP = BLK && IsSeg<Op>::value;
     V lx[kPipeTiles];
     WaveTile<G> t[kPipeTiles];
+    LdsWait lw(p.lb, &s_ids.abort);
 #pragma unroll
-    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id(p.lb, &s_ids, q), w);
+    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id<true>(lw, &s_ids, q), w);
     // the first batch: every tile loaded and its total published up front
 #pragma unroll
     for (int q = 0; q < kPipeTiles; ++q)
@@ -1416,7 +1511,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
                                          &s_slot[(k + PUB) % kPipeSlots]);
 
         Slot* slot = &s_slot[k % kPipeSlots];
-        wait_seq(p.lb, &slot->prefix_seq, k + 1);
+        wait_seq<true>(lw, &slot->prefix_seq, k + 1);
         if constexpr (BLK) {
             V wave_prefix = Op::identity();
 #pragma unroll
@@ -1449,8 +1544,9 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
             }
         }
         if (w == 0) post_id(p, &s_ids, k + kPipeTiles, next_id, exhausted);
-        t[NEW].set(p, get_id(p.lb, &s_ids, k + kPipeTiles), w);
+        t[NEW].set(p, get_id<true>(lw, &s_ids, k + kPipeTiles), w);
     }
+    record_lds_timeout(p.lb, lw);
     if (w == 0 && lane == 0) retire_workgroup(p);
 }
 
@@ -1523,8 +1619,9 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
     T e[kPipeTiles][R][VEC];
     uint32_t hu[R];
     WaveTile<G> t[kPipeTiles];
+    LdsWait lw(p.lb, &s_ids.abort);
 #pragma unroll
-    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id(p.lb, &s_ids, q), w);
+    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id<false>(lw, &s_ids, q), w);
 #pragma unroll
     for (int q = 0; q < kPipeTiles - 1; ++q)
         if (t[q].tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, t[q].base, t[q].vec, lane, e[q], hu);
@@ -1544,7 +1641,7 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
         uint32_t kept[R];
         kept_bits(e[0], t[0].base, kept);
         const uint32_t cnt = pack_wave<T, R, VEC>(e[0], kept, region);
-        wait_seq(p.lb, &slot->prefix_seq, k + 1);
+        wait_seq<false>(lw, &slot->prefix_seq, k + 1);
         uint32_t wave_prefix = 0;
 #pragma unroll
         for (int q = 0; q < ND; ++q)
@@ -1560,8 +1657,9 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
                 for (int j = 0; j < VEC; ++j) e[q][r][j] = e[q + 1][r][j];
         }
         if (w == 0) post_id(p, &s_ids, k + kPipeTiles, next_id, exhausted);
-        t[NEW].set(p, get_id(p.lb, &s_ids, k + kPipeTiles), w);
+        t[NEW].set(p, get_id<false>(lw, &s_ids, k + kPipeTiles), w);
     }
+    record_lds_timeout(p.lb, lw);
     if (w == 0 && lane == 0) retire_workgroup(p);
 }
 

@@ -74,6 +74,34 @@ __device__ __forceinline__ V wave_inclusive_scan(V v, V ident, Comb comb)
     return v;
 }
 
+// Float32 add: the same six steps, but the two row broadcasts as single
+// v_add_f32 DPP instructions.  The compiler fuses a DPP move into the add
+// only when the masked-off rows' "old" value is an identity it knows, and it
+// knows none for float add (-0.0 would be one), so the generic version costs a
+// register fill, a DPP move and a separate add per broadcast step.  Here the
+// disabled rows are simply not written (destination = source), which keeps
+// their value exactly.  The s_nop gives the two wait states a DPP read needs
+// after a VALU write of its source register.
+#ifndef DWPT_FADD_DPP
+#define DWPT_FADD_DPP 1
+#endif
+__device__ __forceinline__ float wave_inclusive_scan_fadd(float v)
+{
+    const auto add = [](float a, float b) { return a + b; };
+    v = add(dpp_move<kDppRowShr1, 0xF>(v, 0.0f), v);
+    v = add(dpp_move<kDppRowShr2, 0xF>(v, 0.0f), v);
+    v = add(dpp_move<kDppRowShr4, 0xF>(v, 0.0f), v);
+    v = add(dpp_move<kDppRowShr8, 0xF>(v, 0.0f), v);
+#if DWPT_FADD_DPP
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(v));
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf" : "+v"(v));
+#else
+    v = add(dpp_move<kDppRowBcast15, 0xA>(v, 0.0f), v);
+    v = add(dpp_move<kDppRowBcast31, 0xC>(v, 0.0f), v);
+#endif
+    return v;
+}
+
 // Value of the next lower lane (identity in lane 0): turns an inclusive
 // wavefront scan into an exclusive one without needing an inverse.
 template <typename V>
