@@ -15,16 +15,20 @@
 // that keeps ~2000 tiles in flight:
 //
 //  * Status words.  Every tile, and every group of 64 consecutive tiles, owns
-//    kWords 64-bit words.  A word holds one 32-bit payload word and a 32-bit
-//    tag = epoch << 3 | flag << 2 | state, with state EMPTY (0), AGGREGATE
-//    (1: the fold of the tile's -- or the group's -- own elements) or PREFIX
-//    (2: the fold of every element up to its end).  Words are written and
-//    read as single 64-bit agent-scope atomics, so a tag always describes the
-//    payload beside it; a payload of two words is accepted only when both
-//    tags agree.  No cache flush or fence is needed: the payload travels in
-//    the word itself.
-//  * Epochs.  The tag carries the call's sequence number; words left by
-//    earlier calls read as EMPTY, so the arrays are never cleared per call.
+//    kWords 64-bit words.  A word holds a 49-bit payload under a 15-bit tag =
+//    epoch << 3 | flag << 2 | state, with state EMPTY (0), AGGREGATE (1: the
+//    fold of the tile's -- or the group's -- own elements) or PREFIX (2: the
+//    fold of every element up to its end).  Words are written and read as
+//    single 64-bit agent-scope atomics, so a tag always describes the payload
+//    beside it; a payload of several words is accepted only when all tags
+//    agree.  No cache flush or fence is needed: the payload travels in the
+//    word itself.  Most carries put 32 bits in each word; the float32 sum's
+//    double carry fits one word (scan_ops.hpp, OpAdd<float>::pack), which
+//    halves the status traffic of that scan (float32 add 2^28: 336.7 ->
+//    334.7 us measured with a one-word carry).
+//  * Epochs.  The tag carries the call's sequence number modulo 2^12 (0 is
+//    never used); words left by earlier calls read as EMPTY, so the arrays
+//    are cleared only when the number wraps, every 4095 calls.
 //  * Segment heads.  The flag bit carries the segmented scan's "contains a
 //    head" bit; a word with it set ends a look-back like a PREFIX does.
 //  * Two levels.  Tile t of group g first folds the tiles of its own group
@@ -62,7 +66,9 @@
 namespace dwpt {
 
 enum : uint32_t { kStateEmpty = 0u, kStateAggregate = 1u, kStatePrefix = 2u };
-enum : uint32_t { kEpochBits = 29u };
+enum : uint32_t { kEpochBits = 12u };
+constexpr int kPayloadBits = 49;  // status word: tag << kPayloadBits | payload
+constexpr uint64_t kPayloadMask = (1ull << kPayloadBits) - 1;
 enum : uint32_t { kErrTimeout = 1u, kErrCounter = 2u };
 enum : int { kGroupShift = 6 };  // 64 tiles per group
 
@@ -92,7 +98,7 @@ struct Lookback {
     uint64_t* groups;    // kWords words per group of 64 tiles
     uint32_t* err;       // device error word (bit flags)
     uint32_t* abort;     // epoch of the last launch that gave up a wait
-    uint32_t epoch;      // 1 .. 2^29 - 1
+    uint32_t epoch;      // 1 .. 2^12 - 1
     uint32_t spin_limit; // polls before giving up
 };
 
@@ -145,19 +151,21 @@ __device__ __forceinline__ uint32_t make_tag(uint32_t epoch, uint32_t flag, uint
     return (epoch << 3) | (flag << 2) | state;
 }
 
+__device__ __forceinline__ uint32_t word_tag(uint64_t w) { return (uint32_t)(w >> kPayloadBits); }
+
 // Called by a single lane.
 template <class Op>
 __device__ __forceinline__ void publish(const Lookback& lb, uint64_t* arr, uint64_t idx, typename Op::carry_t c,
                                         uint32_t state)
 {
-    uint32_t w[Op::kWords];
+    uint64_t w[Op::kWords];
     uint32_t flag;
     Op::pack(c, w, flag);
-    const uint64_t tag = (uint64_t)make_tag(lb.epoch, flag, state) << 32;
+    const uint64_t tag = (uint64_t)make_tag(lb.epoch, flag, state) << kPayloadBits;
     uint64_t* dst = arr + idx * Op::kWords;
 #pragma unroll
     for (int k = 0; k < Op::kWords; ++k)
-        __hip_atomic_store(dst + k, tag | (uint64_t)w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + k, tag | w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 enum : int { kWinFound = 0, kWinBoundary = 1, kWinNone = 2, kWinTimeout = 3 };
@@ -181,15 +189,15 @@ __device__ int fold_window(const Lookback& lb, const uint64_t* arr, int64_t top,
     C val = ident;
     while (true) {
         if (!have) {
-            uint32_t w[Op::kWords];
+            uint64_t w[Op::kWords];
             uint32_t tag0 = 0;
             bool same = true;
             const uint64_t* src = arr + (uint64_t)j * Op::kWords;
 #pragma unroll
             for (int q = 0; q < Op::kWords; ++q) {
                 const uint64_t s = __hip_atomic_load(src + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                w[q] = (uint32_t)s;
-                const uint32_t tag = (uint32_t)(s >> 32);
+                w[q] = s & kPayloadMask;
+                const uint32_t tag = word_tag(s);
                 if (q == 0) tag0 = tag;
                 else same = same && (tag == tag0);
             }
@@ -252,13 +260,13 @@ __device__ int fold_window_wide(const Lookback& lb, const uint64_t* arr, int64_t
 #pragma unroll
         for (int k = 0; k < SPAN; ++k)
             if (!have[k]) {
-                uint32_t w[Op::kWords];
-                const uint32_t tag0 = (uint32_t)(raw[k][0] >> 32);
+                uint64_t w[Op::kWords];
+                const uint32_t tag0 = word_tag(raw[k][0]);
                 bool same = true;
 #pragma unroll
                 for (int q = 0; q < Op::kWords; ++q) {
-                    w[q] = (uint32_t)raw[k][q];
-                    same = same && (uint32_t)(raw[k][q] >> 32) == tag0;
+                    w[q] = raw[k][q] & kPayloadMask;
+                    same = same && word_tag(raw[k][q]) == tag0;
                 }
                 const uint32_t state = tag0 & 3u;
                 const uint32_t flag = (tag0 >> 2) & 1u;
@@ -359,13 +367,13 @@ __device__ typename Op::carry_t resolve_stream(const Lookback& lb, const uint64_
 #pragma unroll
             for (int k = 0; k < SPAN; ++k)
                 if (!have[k]) {
-                    uint32_t w[Op::kWords];
-                    const uint32_t tag0 = (uint32_t)(raw[k][0] >> 32);
+                    uint64_t w[Op::kWords];
+                    const uint32_t tag0 = word_tag(raw[k][0]);
                     bool same = true;
 #pragma unroll
                     for (int q = 0; q < Op::kWords; ++q) {
-                        w[q] = (uint32_t)raw[k][q];
-                        same = same && (uint32_t)(raw[k][q] >> 32) == tag0;
+                        w[q] = raw[k][q] & kPayloadMask;
+                        same = same && word_tag(raw[k][q]) == tag0;
                     }
                     if (same && (tag0 >> 3) == lb.epoch && (tag0 & 3u) != kStateEmpty) {
                         have[k] = true;
@@ -429,13 +437,13 @@ template <class Op>
 __device__ __forceinline__ bool prefix_ready(const Lookback& lb, const uint64_t (&raw)[Op::kWords],
                                              typename Op::carry_t& out)
 {
-    uint32_t w[Op::kWords];
-    const uint32_t tag0 = (uint32_t)(raw[0] >> 32);
+    uint64_t w[Op::kWords];
+    const uint32_t tag0 = word_tag(raw[0]);
     bool same = true;
 #pragma unroll
     for (int q = 0; q < Op::kWords; ++q) {
-        w[q] = (uint32_t)raw[q];
-        same = same && (uint32_t)(raw[q] >> 32) == tag0;
+        w[q] = raw[q] & kPayloadMask;
+        same = same && word_tag(raw[q]) == tag0;
     }
     if (!(same && (tag0 >> 3) == lb.epoch && (tag0 & 3u) == kStatePrefix)) return false;
     out = Op::unpack(w, (tag0 >> 2) & 1u);
@@ -483,15 +491,15 @@ template <class Op>
 __device__ __forceinline__ void publish_acked(const Lookback& lb, uint64_t* arr, uint64_t idx,
                                               typename Op::carry_t c, uint32_t state)
 {
-    uint32_t w[Op::kWords];
+    uint64_t w[Op::kWords];
     uint32_t flag;
     Op::pack(c, w, flag);
-    const uint64_t tag = (uint64_t)make_tag(lb.epoch, flag, state) << 32;
+    const uint64_t tag = (uint64_t)make_tag(lb.epoch, flag, state) << kPayloadBits;
     uint64_t* dst = arr + idx * Op::kWords;
     uint64_t sink = 0;
 #pragma unroll
     for (int k = 0; k < Op::kWords; ++k)
-        sink ^= __hip_atomic_exchange(dst + k, tag | (uint64_t)w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sink ^= __hip_atomic_exchange(dst + k, tag | w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("" ::"v"((uint32_t)sink), "v"((uint32_t)(sink >> 32)));
 }
 

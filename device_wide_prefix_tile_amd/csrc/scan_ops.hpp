@@ -19,7 +19,8 @@
 //   identity(), combine(earlier, later)            on value_t
 //   carry_identity(), to_carry(v), combine_carry(earlier, later)
 //   prepare(carry) -> prep_t, apply(prep, local) -> value_t   (= carry (+) local)
-//   kWords, pack(carry, words, flag), unpack(words, flag)     status-word codec
+//   kWords, pack(carry, payloads, flag), unpack(payloads, flag)
+//                     status-word codec: kWords payloads of at most 49 bits
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -69,8 +70,21 @@ struct SameCarry {
     __device__ __forceinline__ static carry_t combine_carry(carry_t a, carry_t b) { return Derived::combine(a, b); }
     __device__ __forceinline__ static prep_t prepare(carry_t c) { return c; }
     __device__ __forceinline__ static value_t apply(prep_t c, value_t local) { return Derived::combine(c, local); }
-    __device__ __forceinline__ static void pack(carry_t c, uint32_t* w, uint32_t& flag) { to_words(c, w); flag = 0; }
-    __device__ __forceinline__ static carry_t unpack(const uint32_t* w, uint32_t) { return from_words<carry_t>(w); }
+    __device__ __forceinline__ static void pack(carry_t c, uint64_t* w, uint32_t& flag)
+    {
+        uint32_t t[kWords];
+        to_words(c, t);
+#pragma unroll
+        for (int k = 0; k < kWords; ++k) w[k] = t[k];
+        flag = 0;
+    }
+    __device__ __forceinline__ static carry_t unpack(const uint64_t* w, uint32_t)
+    {
+        uint32_t t[kWords];
+#pragma unroll
+        for (int k = 0; k < kWords; ++k) t[k] = (uint32_t)w[k];
+        return from_words<carry_t>(t);
+    }
 };
 
 // ---------------------------------------------------------------- add
@@ -106,7 +120,7 @@ template <> struct OpAdd<float> {
     using value_t = float;
     using carry_t = double;
     using prep_t = F32Split;
-    static constexpr int kWords = 2;
+    static constexpr int kWords = 1;
     __device__ __forceinline__ static float identity() { return 0.0f; }
     __device__ __forceinline__ static float combine(float a, float b) { return a + b; }
     __device__ __forceinline__ static double carry_identity() { return 0.0; }
@@ -130,8 +144,23 @@ template <> struct OpAdd<float> {
 #else
     __device__ __forceinline__ static float apply(F32Split c, float local) { return c.hi + (c.lo + local); }
 #endif
-    __device__ __forceinline__ static void pack(double c, uint32_t* w, uint32_t& flag) { to_words(c, w); flag = 0; }
-    __device__ __forceinline__ static double unpack(const uint32_t* w, uint32_t) { return from_words<double>(w); }
+    // One 49-bit status payload: the double's sign, exponent and a 37-bit
+    // mantissa, rounded to nearest (relative error below 2^-38).  Tile totals
+    // are floats and pass exactly; a published prefix is rounded once -- the
+    // streaming resolver keeps its running carry in full double, and the
+    // carries are rounded to float before they are applied anyway.
+    __device__ __forceinline__ static void pack(double c, uint64_t* w, uint32_t& flag)
+    {
+        const uint64_t b = __builtin_bit_cast(uint64_t, c);
+        const uint64_t mag = ((b & 0x7FFFFFFFFFFFFFFFull) + (1ull << 14)) >> 15;  // 48 bits: exponent, mantissa
+        w[0] = ((b >> 63) << 48) | mag;
+        flag = 0;
+    }
+    __device__ __forceinline__ static double unpack(const uint64_t* w, uint32_t)
+    {
+        const uint64_t b = ((w[0] >> 48) << 63) | ((w[0] & 0xFFFFFFFFFFFFull) << 15);
+        return __builtin_bit_cast(double, b);
+    }
 };
 
 // ---------------------------------------------------------------- max / min
@@ -286,13 +315,13 @@ struct OpSeg {
     {
         return {local.f, local.f ? local.v : Base::apply(c, local.v)};
     }
-    __device__ __forceinline__ static void pack(carry_t c, uint32_t* w, uint32_t& flag)
+    __device__ __forceinline__ static void pack(carry_t c, uint64_t* w, uint32_t& flag)
     {
         uint32_t unused;
         Base::pack(c.v, w, unused);
         flag = c.f ? 1u : 0u;
     }
-    __device__ __forceinline__ static carry_t unpack(const uint32_t* w, uint32_t flag)
+    __device__ __forceinline__ static carry_t unpack(const uint64_t* w, uint32_t flag)
     {
         return {flag, Base::unpack(w, 0u)};
     }

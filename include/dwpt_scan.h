@@ -30,8 +30,9 @@
  *     SCAN_ERR_HIP (hipGetLastError has the HIP code); failure to get
  *     workspace memory gives SCAN_ERR_NOMEM.
  *   - Workspace: the multi-tile path keeps a status array (17 eight-byte
- *     words per tile of 3584-15360 elements for each 4 bytes of carry) and
- *     three counters per (device, stream); reduce-then-scan and the radix
+ *     words per tile of 3584-15360 elements and per status word of its
+ *     carry: 1 for 32-bit carries and the float32 sum, 2 for AFFINE and
+ *     MAX_COUNT, 4 for MAT2, 9 for MAT3) and counters per (device, stream); reduce-then-scan and the radix
  *     pass add a plain buffer each (the tile carries; 256 uint32 counts per
  *     8192-key tile).  Each is allocated on first use, grown when needed
  *     (after the stream has drained) and reused across calls without
@@ -207,10 +208,9 @@ scan_status_t radix_split(const uint32_t* keys, const uint32_t* vals, size_t n, 
  * a fill kernel on that call's stream).  Inputs whose status words do not fit
  * are rejected with SCAN_ERR_INVALID before anything is launched: tiles *
  * words * 17 * 8 bytes must fit in 16 MiB - 640 bytes, with tiles = ceil(n /
- * tile) and (tile, words) = (15360, 1) for 4-byte integer ops, (15360, 2)
- * for F32 ADD, (15360, 1) for F32 MAX/MIN, (7680, 2) AFFINE, (5760, 2)
- * MAX_COUNT, (3840, 4) MAT2, (3584, 9) MAT3 -- e.g. n up to 947,374,080 for
- * F32 ADD and 1,894,763,520 for I32 ADD.  Every call on a GPU shares that
+ * tile) and (tile, words) = (15360, 1) for ADD, MAX, MIN, AND, OR over
+ * I32, U32 and F32, (7680, 2) AFFINE, (5760, 2) MAX_COUNT, (3840, 4) MAT2,
+ * (3584, 9) MAT3 -- e.g. n up to 1,894,763,520 for the 4-byte types.  Every call on a GPU shares that
  * GPU's array (the last call's contents stay in it): calls that overlap in
  * time on one GPU, e.g. on two streams, race and give wrong results; calls
  * in one stream's order, or separated by synchronisation, are safe.  The

@@ -118,8 +118,9 @@ def test_argument_checks_before_any_launch():
     assert L.scan_copy_probe(1024, 2048, 10, None) == binding.SCAN_ERR_INVALID
     # the allocation-free scan: same checks, and inputs whose status words do not fit its
     # 16 MiB static array are rejected before anything is launched (fake, never-touched
-    # addresses); float32 add has 2 status words per 15360-element tile, int32 add 1
-    NOALLOC_F32_MAX, NOALLOC_I32_MAX = 61678 * 15360, 123357 * 15360
+    # addresses); float32 and int32 add have 1 status word per 15360-element tile, affine 2
+    # per 7680 pairs
+    NOALLOC_F32_MAX, NOALLOC_I32_MAX = 123357 * 15360, 123357 * 15360
     assert L.scan_noalloc(ADD, F32, None, None, 0, 0, None) == 0
     assert L.scan_noalloc(AFF, F32, 1024, 2048, 10, 0, None) == binding.SCAN_ERR_UNSUPPORTED
     assert L.scan_noalloc(ADD, I32, None, 2048, 10, 1, None) == binding.SCAN_ERR_INVALID
@@ -127,6 +128,7 @@ def test_argument_checks_before_any_launch():
     assert L.scan_noalloc(ADD, F32, 1 << 20, 1 << 40, NOALLOC_F32_MAX + 1, 0, None) == binding.SCAN_ERR_INVALID
     assert L.scan_noalloc(ADD, I32, 1 << 20, 1 << 40, NOALLOC_I32_MAX + 1, 1, None) == binding.SCAN_ERR_INVALID
     assert L.scan_noalloc(6, 6, 1 << 20, 1 << 40, 13706 * 3584 + 1, 0, None) == binding.SCAN_ERR_INVALID
+    assert L.scan_noalloc(AFF, PAIR, 1 << 20, 1 << 40, 61678 * 7680 + 1, 0, None) == binding.SCAN_ERR_INVALID
     # CSR row offsets: row_ptr required and aligned, indices required when nnz > 0,
     # no overlap at all, nnz below 2^32
     assert L.csr_row_offsets(1024, 10, 5, None, None) == binding.SCAN_ERR_INVALID

@@ -680,6 +680,34 @@ def test_modes_alternate_on_one_stream():
     assert dw.scan_get_device_error() == 0
 
 
+def test_epoch_wrap_clears_status_words():
+    """Status words carry the call number modulo 2^12 and the array is cleared when it
+    wraps: more than 4095 multi-tile calls on one stream, alternating a float32 sum (one
+    49-bit payload per tile) with an int32 maximum (one 32-bit payload) so that the words
+    left by one layout must read as stale for the other, checked before, around and after
+    the wrap."""
+    n = 3 * TILE + 17
+    f = si.float32_01(95, n)
+    x = si.int32_full(96, n)
+    rf, sf = oracle.scan("add", f)
+    rx = oracle.scan("max", x)
+    fd, xd = to_dev(f), to_dev(x)
+    yf, yx = torch.empty_like(fd), torch.empty_like(xd)
+    with Path("multi"):
+        for k in range(2100):
+            dw.scan_inclusive(fd, "add", out=yf)
+            dw.scan_inclusive(xd, "max", out=yx)
+            if k % 300 == 0 or 2040 <= k <= 2060:
+                assert_f32_close(from_dev(yf), rf, sf, "f32 add call %d" % k)
+                assert_equal(from_dev(yx), rx, "i32 max call %d" % k)
+    with Path("fallback"):
+        for k in range(2100):
+            dw.scan_exclusive(xd, "max", out=yx)
+            if k % 700 == 0:
+                assert_equal(from_dev(yx), oracle.scan("max", x, exclusive=True), "fallback call %d" % k)
+    assert dw.scan_get_device_error() == 0
+
+
 def test_rts_float_sum_is_reproducible():
     # Reduce-then-scan fixes the association of a float sum by n alone (tile
     # totals, then one workgroup folding them in order): repeated calls, also
