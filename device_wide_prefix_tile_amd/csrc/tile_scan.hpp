@@ -631,18 +631,24 @@ __global__ __launch_bounds__(BLOCK) void compact_kernel(ScanParams p)
 //    tile number one iteration before it is needed.
 //  * Rings.  Data and prefix wavefronts meet through rings of LDS slots (the
 //    k-th tile of the workgroup uses slot k mod 16) with sequence numbers
-//    instead of barriers.  The total of the k-th tile is handed over WAIT - 1
-//    iterations before its prefix is awaited; a wavefront that hands over
-//    tile k + S has passed the prefix wait of tile k + S - WAIT, which
-//    needed every wavefront's hand-over of that tile, i.e. every wavefront
-//    has finished tile k when S >= 2 * WAIT.  So slots are never rewritten
-//    early; the tile-number ring is safe by the same argument.
+//    instead of barriers.  In the loop the total of the k-th tile is handed
+//    over WAIT - 1 iterations before its prefix is awaited, but the first
+//    batch hands over the totals of tiles 0 .. WAIT before iteration 0.  A
+//    wavefront that hands over tile k + S has passed the prefix wait of tile
+//    k + S - WAIT, which needed every wavefront's hand-over of that tile: for
+//    a tile of the first batch that says nothing about where a slow
+//    wavefront is, and k + S - WAIT > WAIT holds for every k only when
+//    S >= 2 * WAIT + 1; then every wavefront has finished tile k.  So slots
+//    are never rewritten early; the tile-number ring (S >= WAIT + 1) is safe
+//    by the same argument.  A host model of the protocol (CPU tests) finds
+//    stale wave totals and lost tile totals with S = 2 * WAIT (e.g. WAIT 8
+//    with these 16 slots) and none from S = 2 * WAIT + 1.
 //  * Progress.  Every wait is on lower tiles or on the resolver, which only
 //    waits for totals; a total is published before its workgroup waits for
 //    any later prefix; every wait, on status words and on the LDS rings, is
 //    bounded by the spin limit, and a wait that gives up makes the others of
 //    the launch give up too (lookback.hpp, give_up).
-constexpr int kPipeSlots = 16;  // >= 2 * WAIT (see the ring note above)
+constexpr int kPipeSlots = 16;  // >= 2 * WAIT + 1 (see the ring note above)
 // Tiles per lane of the resolver's window (64 * span tiles per poll round),
 // as measured at full size: windows of 64 tiles against 128 and 256 —
 // float32 add 349.5 / 352 / 354.5 us, int32 exclusive add 346.8 / 349.5 /
@@ -1434,7 +1440,7 @@ template <class Op, bool EXCL, int BLOCK, int ITEMS, int WAIT>
 __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
 {
     constexpr int kPipeWait = WAIT, kPipeTiles = WAIT + 1;
-    static_assert(kPipeSlots >= 2 * kPipeWait, "slot ring too short for the pipeline depth");
+    static_assert(kPipeSlots >= 2 * kPipeWait + 1, "slot ring too short for the pipeline depth");
     using G = Geometry<Op, BLOCK, ITEMS>;
     using E = typename Op::elem_t;
     using V = typename Op::value_t;
@@ -1563,7 +1569,7 @@ template <typename T, int BLOCK, int ITEMS, int WAIT>
 __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
 {
     constexpr int kPipeWait = WAIT, kPipeTiles = WAIT + 1;
-    static_assert(kPipeSlots >= 2 * kPipeWait, "slot ring too short for the pipeline depth");
+    static_assert(kPipeSlots >= 2 * kPipeWait + 1, "slot ring too short for the pipeline depth");
     using Cnt = OpAdd<uint32_t>;
     using Ld = OpMax<T>;  // element loads of T (identity past n: never kept)
     using G = Geometry<Cnt, BLOCK, ITEMS>;
