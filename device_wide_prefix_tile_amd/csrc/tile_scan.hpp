@@ -836,8 +836,10 @@ __device__ __forceinline__ void hand_over_slot(const ScanParams& p, uint32_t til
 //    which itself only waits for prefixes).
 // So the data wavefronts' waits end without a count of their own.  They may
 // still count (COUNTED) and give up past the limit; whether that is faster
-// was measured per kernel: the scans gained ~1 us with the counted loop,
-// compaction at 2^28 lost 50 (381 against 322 us), and is not counted.
+// was measured per kernel class (counted_lds_waits): the 4-byte scans gain
+// 1-2 us at 2^28 with the counted loop and 2x2 matrices ~3 us at 2^26, while
+// (maximum, count) at 2^27 loses 130 us (567 against 437), segmented add 5,
+// compaction at 2^28 50 (381 against 322 us), so those are not counted.
 // Counted or not, a loop touches nothing but LDS: a data wavefront's global
 // load would complete only after its own tile loads in flight (one counter
 // covers a wavefront's loads).  A wave that gave up goes on with what the
@@ -1372,6 +1374,14 @@ __device__ __forceinline__ typename Op::value_t tile_wave_total(uint64_t wave_ba
 // published before any wait (the second one's first, so that the LDS area
 // then holds the first tile); the second tile is written back to the area in
 // its turn.
+// Counted data-wavefront waits (see LdsWait): for the unsegmented 4-byte
+// scans and 2x2 matrices.
+template <class Op>
+constexpr bool counted_lds_waits()
+{
+    return !IsSeg<Op>::value && (sizeof(typename Op::value_t) == 4 || sizeof(typename Op::value_t) == 16);
+}
+
 template <class Op> struct ReloadAfterWait { static constexpr bool value = false; };
 template <> struct ReloadAfterWait<OpMat3> { static constexpr bool value = DWPT_RELOAD36; };
 
@@ -1387,8 +1397,8 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
     V lx;
     WaveTile<G> t0, t1;
     LdsWait lw(p.lb, &s_ids->abort);
-    t0.set(p, get_id<true>(lw, s_ids, 0), w);
-    t1.set(p, get_id<true>(lw, s_ids, 1), w);
+    t0.set(p, get_id<counted_lds_waits<Op>()>(lw, s_ids, 0), w);
+    t1.set(p, get_id<counted_lds_waits<Op>()>(lw, s_ids, 1), w);
     if (t0.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t0.base, t0.vec, lane, e0, h0);
     if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t1.base, t1.vec, lane, e1, h1);
     if (t1.tile < p.num_tiles)
@@ -1414,7 +1424,7 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
             if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t1.base, t1.vec, lane, e1, h1);
         }
         Slot* slot = &s_slot[k % kPipeSlots];
-        wait_seq<true>(lw, &slot->prefix_seq, k + 1);
+        wait_seq<counted_lds_waits<Op>()>(lw, &slot->prefix_seq, k + 1);
         V wave_prefix = Op::identity();
 #pragma unroll
         for (int q = 0; q < ND; ++q)
@@ -1430,7 +1440,7 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
             for (int j = 0; j < VEC; ++j) e0[r][j] = e1[r][j];
         }
         if (w == 0) post_id(p, s_ids, k + 2, next_id, exhausted);
-        t1.set(p, get_id<true>(lw, s_ids, k + 2), w);
+        t1.set(p, get_id<counted_lds_waits<Op>()>(lw, s_ids, k + 2), w);
     }
     record_lds_timeout(p.lb, lw);
     if (w == 0 && lane == 0) retire_workgroup(p);
@@ -1492,7 +1502,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     WaveTile<G> t[kPipeTiles];
     LdsWait lw(p.lb, &s_ids.abort);
 #pragma unroll
-    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id<true>(lw, &s_ids, q), w);
+    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id<counted_lds_waits<Op>()>(lw, &s_ids, q), w);
     // the first batch: every tile loaded and its total published up front
 #pragma unroll
     for (int q = 0; q < kPipeTiles; ++q)
@@ -1517,7 +1527,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
                                          &s_slot[(k + PUB) % kPipeSlots]);
 
         Slot* slot = &s_slot[k % kPipeSlots];
-        wait_seq<true>(lw, &slot->prefix_seq, k + 1);
+        wait_seq<counted_lds_waits<Op>()>(lw, &slot->prefix_seq, k + 1);
         if constexpr (BLK) {
             V wave_prefix = Op::identity();
 #pragma unroll
@@ -1550,7 +1560,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
             }
         }
         if (w == 0) post_id(p, &s_ids, k + kPipeTiles, next_id, exhausted);
-        t[NEW].set(p, get_id<true>(lw, &s_ids, k + kPipeTiles), w);
+        t[NEW].set(p, get_id<counted_lds_waits<Op>()>(lw, &s_ids, k + kPipeTiles), w);
     }
     record_lds_timeout(p.lb, lw);
     if (w == 0 && lane == 0) retire_workgroup(p);
