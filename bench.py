@@ -10,6 +10,14 @@ the stream the launches run on, before the first and after the last, give
 the kernel's average duration for the roofline entry (gaps between launches
 included).
 
+Before the warm-up steps the step runs untimed, back to back, for about
+--settle-ms (default 200 ms): after the GPU has been idle, launches 6-40 of
+this size run 3-9% slower than the first five and than every later one (a
+clock/power transient of the chip, not of the kernel: a plain copy sees it
+too, and 100 ms of any load before the timed launches removes it).  With 5
+warm-up steps the timed region would otherwise sit inside the transient.
+The JSON line records the settle time and launch count.
+
 Prints one JSON line.  value = Gelem/s (n * K / elapsed).  Effective HBM
 traffic counts the minimal 1 read + 1 write per element (8 bytes).
 
@@ -30,10 +38,18 @@ four-pass sort, the
 max-scan size sweep with reduce-then-scan beside it) and writes one JSON line
 per workload to FILE.
 
+--latency FILE times the latency regime (config 1, int32 exclusive add at
+2^20 on every path; the one-workgroup / one-tile crossover; the int32 max
+sweep 4^5..4^13 with reduce-then-scan beside it): per-call medians with the
+inputs cache-resident and after a 512 MiB flush, and back-to-back averages,
+one JSON line per case; every case starts with a small copy-probe launch so
+that a kernel trace of the same run splits into cases
+(--summarize-latency).
+
 --workloads-once K runs each full-size workload K times (for rocprofv3
 passes); --summarize-rocprof, --summarize-traffic, --summarize-wl-trace and
---summarize-wl-insts turn rocprofv3 CSV output into the summaries under
-profiles/.
+--summarize-wl-insts, --summarize-latency and --summarize-dispatches turn
+rocprofv3 CSV output into the summaries under profiles/.
 """
 import argparse
 import hashlib
@@ -69,6 +85,12 @@ PROFILE_CMDS = {
                 "python3 bench.py --workloads-once 3",
     "wl_trace": "rocprofv3 --kernel-trace -f csv -d $OUT/prof_wl_trace -o wl -- "
                 "python3 bench.py --workloads-once 40",
+    "latency": "rocprofv3 --kernel-trace -f csv -d $OUT/prof_lat -o lat -- "
+               "python3 bench.py --latency $OUT/latency_traced.jsonl",
+    "driver": "rocprofv3 --kernel-trace --stats -f csv -d $OUT/prof_drv -o drv -- "
+              "python3 bench.py --gpus 1 --steps 20 --warmup 5",
+    "driver_nosettle": "rocprofv3 --kernel-trace --stats -f csv -d $OUT/prof_drv0 -o drv -- "
+                       "python3 bench.py --gpus 1 --steps 20 --warmup 5 --settle-ms 0",
     "wl_insts": "rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD "
                 "SQ_INSTS_VMEM_WR SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE -f csv -d $OUT/prof_wl_insts -o wl -- "
                 "python3 bench.py --workloads-once 3",
@@ -78,6 +100,25 @@ WL_INSTS_FILE = os.path.join(ROOT, "profiles", "instructions_all_workloads.txt")
 # MI355X: 256 CUs x 4 SIMDs at 2.4 GHz
 VALU_ISSUE_PER_S = 256 * 4 * 2.4e9 / 4
 WL_TRACE_FILE = os.path.join(ROOT, "profiles", "kernel_times_all_workloads.txt")
+LATENCY_FILE = os.path.join(ROOT, "profiles", "kernel_times_latency_regime.txt")
+DISPATCH_FILE = os.path.join(ROOT, "profiles", "dispatches_f32_inclusive_add_2p28_driver_command.txt")
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache (L2s: 4 MiB per XCD)
+FLUSH_BYTES = 512 << 20
+
+# Latency-regime cases: (label, op, exclusive, n, input, small_n_max, multi-tile mode).
+# small_n_max None: the library default (one tile); 0 with mode 1: one workgroup per
+# tile forced; 1 << 40: the single-workgroup kernel forced.
+_SINGLE, _AUTO = 1 << 40, None
+LATENCY_CASES = (
+    [("int32 exclusive add 2^%d, %s" % (k, path), "add", True, 1 << k, "int32_0_15", lim, mode)
+     for k in (10, 12, 13, 14, 15, 16)
+     for path, lim, mode in (("one workgroup", _SINGLE, 0), ("one workgroup per tile", 0, 1))]
+    + [("config 1: int32 exclusive add 2^20, %s" % path, "add", True, 1 << 20, "int32_0_15", lim, mode)
+       for path, lim, mode in (("auto", _AUTO, 0), ("persistent", 0, 2), ("reduce-then-scan", 0, 3))]
+    + [("int32 inclusive max 4^%d, auto" % k, "max", False, 4 ** k, "int32_full", _AUTO, 0) for k in range(5, 14)]
+    + [("int32 inclusive max 4^%d, reduce-then-scan" % k, "max", False, 4 ** k, "int32_full", 0, 3)
+       for k in range(9, 14)]
+)
 
 # Full-size workloads for per-kernel counter runs: (label, kernel-name fragment,
 # n, algorithmic bytes per launch as a function of n and the kept count).
@@ -345,6 +386,157 @@ def summarize_workload_insts(insts_dir, trace_summary=WL_TRACE_FILE):
     print(open(WL_INSTS_FILE).read())
 
 
+def _dispatches(trace_dir):
+    """(name, start ns, end ns) of every dispatch in a kernel trace, in start order."""
+    rows = sorted(_csv_rows(trace_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    return [(r.get("Kernel_Name", ""), int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+
+
+def _ours(name):
+    return "dwpt::" in name or "zero_words_kernel" in name
+
+
+def _calls(disp):
+    """Groups a case's dispatches into calls: a call starts at each dispatch of the kernel
+    that started the case (reduce-then-scan: tile totals, carries, seeded scan)."""
+    disp = [d for d in disp if _ours(d[0]) and "zero_words_kernel" not in d[0]]
+    calls = []
+    for d in disp:
+        if not calls or d[0] == disp[0][0]:
+            calls.append([])
+        calls[-1].append(d)
+    return calls
+
+
+def summarize_latency(trace_dir, jsonl_path):
+    """Per-call kernel time of each latency-regime case from a kernel trace of --latency
+    (split into cases at the copy-probe markers), beside the event timings of an unprofiled
+    --latency run."""
+    disp = _dispatches(trace_dir)
+    segs, cur = [], None
+    for d in disp:
+        if COPY_KERNEL in d[0]:
+            cur = []
+            segs.append(cur)
+        elif cur is not None:
+            cur.append(d)
+    events = {}
+    if jsonl_path and os.path.exists(jsonl_path):
+        for line in open(jsonl_path):
+            rec = json.loads(line)
+            events[rec["case"]] = rec
+    out = ["# Latency regime: kernel time per call of each case (rocprofv3 kernel trace), beside the",
+           "# event timings of the same cases in a run without the profiler",
+           "# trace: " + PROFILE_CMDS["latency"],
+           "# events: python3 bench.py --latency $OUT/latency.jsonl",
+           "# kernel_us: the call's kernels' summed durations; span_us: first kernel start to last",
+           "# kernel end (reduce-then-scan: three launches); medians over the last 200 cache-resident",
+           "# calls and over 30 calls that each follow a 512 MiB flush (cold).  event_us: one call",
+           "# between its own events (launch included); b2b_us: average of 200 calls back to back.",
+           "source_hash: " + kernel_source_hash(),
+           "# case | kernels | kernel_us | span_us | cold kernel_us | event_us | b2b_us | cold event_us"]
+    if len(segs) != 2 * len(LATENCY_CASES):
+        out.append("# trace holds %d marked segments, expected %d" % (len(segs), 2 * len(LATENCY_CASES)))
+    for i, case in enumerate(LATENCY_CASES):
+        label = case[0]
+        if 2 * i + 1 >= len(segs):
+            out.append("%s | missing" % label)
+            continue
+        hot, cold = _calls(segs[2 * i])[-200:], _calls(segs[2 * i + 1])
+        names = " + ".join(_short(d[0]).split("<")[0] for d in (hot[-1] if hot else []))
+
+        def med(calls, span):
+            if not calls:
+                return float("nan")
+            if span:
+                return statistics.median((c[-1][2] - c[0][1]) / 1e3 for c in calls)
+            return statistics.median(sum(d[2] - d[1] for d in c) / 1e3 for c in calls)
+        ev = events.get(label, {})
+        out.append("%s | %s | %.2f | %.2f | %.2f | %s | %s | %s" % (
+            label, names, med(hot, False), med(hot, True), med(cold, False), ev.get("median_us", "-"),
+            ev.get("back_to_back_us", "-"), ev.get("cold_median_us", "-")))
+    with open(LATENCY_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(open(LATENCY_FILE).read())
+
+
+def summarize_dispatches(trace_dir, trace_dir_nosettle):
+    """Per-dispatch durations of the headline scan kernel in traces of the driver's command
+    (python3 bench.py --gpus 1 --steps 20 --warmup 5), with and without the settle phase."""
+    out = ["# Per-dispatch durations of the float32 inclusive add-scan kernel, n=2^28, under the",
+           "# benchmark driver's command, after the GPU was idle",
+           "# with settle:    " + PROFILE_CMDS["driver"],
+           "# without settle: " + PROFILE_CMDS["driver_nosettle"],
+           "# The warm-up and timed launches are the last 25 scan dispatches before the first copy-probe",
+           "# dispatch; the settle launches come before them.",
+           "source_hash: " + kernel_source_hash()]
+    for title, d in (("with settle", trace_dir), ("without settle (--settle-ms 0)", trace_dir_nosettle)):
+        disp = _dispatches(d)
+        first_copy = next((i for i, x in enumerate(disp) if COPY_KERNEL in x[0]), len(disp))
+        scans = [(x[2] - x[1]) / 1e3 for x in disp[:first_copy] if SCAN_KERNEL in x[0] and "float" in x[0]]
+        settle, main = scans[:-25], scans[-25:]
+        out.append("")
+        out.append("## " + title)
+        out.append("settle_dispatches: %d" % len(settle))
+        if settle:
+            blocks = [settle[i:i + 50] for i in range(0, len(settle), 50)]
+            out.append("settle_mean_us_per_50: " + " ".join("%.1f" % (sum(b) / len(b)) for b in blocks))
+        out.append("warmup_us: " + " ".join("%.1f" % v for v in main[:5]))
+        out.append("timed_us: " + " ".join("%.1f" % v for v in main[5:]))
+        if len(main) == 25:
+            out.append("timed_mean_us: %.2f" % (sum(main[5:]) / 20))
+            out.append("timed_frac_of_8TBps: %.4f" % (8 * N_MAIN / (sum(main[5:]) / 20 * 1e-6) / 1e9 / PEAK_GBPS))
+    with open(DISPATCH_FILE, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(open(DISPATCH_FILE).read())
+
+
+def latency(dw, torch, si, out_path, steps=200):
+    """Times each latency-regime case; one JSON line per case to out_path."""
+    import numpy as np
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    mark_a = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    mark_b = torch.empty_like(mark_a)
+    lines = []
+    for label, op, excl, n, gen, lim, mode in LATENCY_CASES:
+        log("latency: " + label)
+        x_host = getattr(si, gen)(7, n)
+        x = torch.from_numpy(x_host).cuda()
+        y = torch.empty_like(x)
+        scan = dw.scan_exclusive if excl else dw.scan_inclusive
+        fn = lambda: scan(x, op, out=y)  # noqa: E731
+        old_lim = dw.scan_set_small_n_max(dw.SCAN_SMALL_N_AUTO if lim is None else lim)
+        old_mode = dw.scan_set_multi_tile_mode(mode)
+        try:
+            torch.cuda.synchronize()
+            dw.scan_copy_probe(mark_a, mark_b)  # marks the start of the case in a kernel trace
+            _, ms = time_launches(fn, steps, 100, torch)
+            _, t = time_back_to_back(fn, steps, 0, torch)
+            torch.cuda.synchronize()
+            dw.scan_copy_probe(mark_a, mark_b)  # the cold calls
+            cold = time_cold(fn, 30, flush, torch)
+        finally:
+            dw.scan_set_small_n_max(old_lim)
+            dw.scan_set_multi_tile_mode(old_mode)
+        y_host = y.cpu().numpy()
+        # the last output against a direct fold of the input
+        if op == "add":
+            v = x_host[:-1] if excl else x_host
+            want = np.array([int(np.sum(v, dtype=np.int64)) & 0xFFFFFFFF], dtype=np.uint32).view(np.int32)[0]
+        else:
+            want = x_host.max()
+        lines.append({"case": label, "n": n, "median_us": round(statistics.median(ms) * 1e3, 2),
+                      "back_to_back_us": round(t * 1e6, 2), "cold_median_us": round(cold * 1e3, 2),
+                      "last_ok": bool(y_host[-1] == want)})
+    del flush
+    torch.cuda.synchronize()
+    assert dw.scan_get_device_error() == 0, "device reported a look-back timeout"
+    with open(out_path, "w") as f:
+        for l in lines:
+            f.write(json.dumps(l) + "\n")
+    print(json.dumps({"latency_cases": len(lines), "all_last_ok": all(l["last_ok"] for l in lines)}), flush=True)
+
+
 def workloads_once(dw, torch, si, steps):
     """Each full-size workload `steps` times, one input resident at a time (for counter runs)."""
     import numpy as np
@@ -463,6 +655,34 @@ def time_back_to_back(fn, steps, warmup, torch):
     return elapsed, a.elapsed_time(b) * 1e-3 / steps
 
 
+def settle_clocks(fn, ms, torch):
+    """Run fn back to back, untimed, for about `ms` milliseconds; returns the launch count."""
+    launches = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            fn()
+        launches += 8
+        torch.cuda.synchronize()
+    return launches
+
+
+def time_cold(fn, reps, flush, torch):
+    """Median time of one call with nothing of its inputs in the caches: each call follows
+    a write of `flush` (larger than the Infinity Cache) and sits between its own events."""
+    stream = torch.cuda.current_stream()
+    ms = []
+    for _ in range(reps):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    return statistics.median(ms)
+
+
 def host_cpu():
     """CPU model and logical CPU count of the host the oracle runs on."""
     model = "unknown"
@@ -507,6 +727,7 @@ def suite(dw, torch, si, out_path, steps):
     import numpy as np
     lines = []
     copy_gbps = copy_probe(dw, torch)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
 
     def rec(name, n, bytes_per_elem, fn):
         log("suite: " + name)
@@ -515,12 +736,18 @@ def suite(dw, torch, si, out_path, steps):
         # of launches back to back (throughput, gaps between launches included)
         elapsed, ms = time_launches(fn, steps, 100, torch)
         _, t = time_back_to_back(fn, steps, 0, torch)
-        lines.append({"workload": name, "n": n, "median_us": round(statistics.median(ms) * 1e3, 2),
-                      "back_to_back_us": round(t * 1e6, 2),
-                      "gelem_s": round(n / t / 1e9, 2),
-                      "effective_GBps": round(n * bytes_per_elem / t / 1e9, 1),
-                      "pct_of_peak": round(100 * n * bytes_per_elem / t / 1e9 / PEAK_GBPS, 1),
-                      "pct_of_copy": round(100 * n * bytes_per_elem / t / 1e9 / copy_gbps, 1)})
+        line = {"workload": name, "n": n, "median_us": round(statistics.median(ms) * 1e3, 2),
+                "back_to_back_us": round(t * 1e6, 2),
+                "gelem_s": round(n / t / 1e9, 2),
+                "effective_GBps": round(n * bytes_per_elem / t / 1e9, 1),
+                "pct_of_peak": round(100 * n * bytes_per_elem / t / 1e9 / PEAK_GBPS, 1),
+                "pct_of_copy": round(100 * n * bytes_per_elem / t / 1e9 / copy_gbps, 1)}
+        if n * bytes_per_elem <= MALL_BYTES:
+            # repeated calls find input and output in the Infinity Cache: the figures above
+            # are cache-resident; cold_median_us is one call after a 512 MiB flush
+            line["cache_resident"] = True
+            line["cold_median_us"] = round(time_cold(fn, 30, flush, torch) * 1e3, 2)
+        lines.append(line)
 
     x = torch.from_numpy(si.int32_0_15(1, 1 << 20)).cuda()
     y = torch.empty_like(x)
@@ -617,7 +844,7 @@ def suite(dw, torch, si, out_path, steps):
     old = dw.scan_set_multi_tile_mode(3)
     rec("float32 inclusive add 2^28, reduce-then-scan", 1 << 28, 8, lambda: dw.scan_inclusive(xf, "add", out=yf))
     dw.scan_set_multi_tile_mode(old)
-    del xf, yf
+    del xf, yf, flush
     torch.cuda.empty_cache()
     with open(out_path, "w") as f:
         for l in lines:
@@ -631,7 +858,14 @@ def main():
     # median over launches 1-100, 356-357.6 us for every later block of 100)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed back-to-back steps for about this long before the warm-up steps")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--latency", metavar="FILE", help="time the latency-regime cases, JSON lines to FILE, and exit")
+    ap.add_argument("--summarize-latency", nargs=2, metavar=("TRACE_DIR", "JSONL"),
+                    help="write the latency-regime summary under profiles/ and exit")
+    ap.add_argument("--summarize-dispatches", nargs=2, metavar=("TRACE_DIR", "TRACE_DIR_NOSETTLE"),
+                    help="write the per-dispatch summary of the driver-command traces and exit")
     ap.add_argument("--suite", metavar="FILE", help="also time every workload, JSON lines to FILE")
     ap.add_argument("--summarize-rocprof", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output and exit")
@@ -656,6 +890,12 @@ def main():
     if args.summarize_traffic:
         summarize_workload_traffic(*args.summarize_traffic)
         return
+    if args.summarize_latency:
+        summarize_latency(*args.summarize_latency)
+        return
+    if args.summarize_dispatches:
+        summarize_dispatches(*args.summarize_dispatches)
+        return
     if args.gpus != 1:
         print("bench.py: the scan runs on one GPU; --gpus %d is not supported "
               "(the library does not shard a scan across GPUs)" % args.gpus, file=sys.stderr)
@@ -672,15 +912,19 @@ def main():
     if args.workloads_once:
         workloads_once(dw, torch, si, args.workloads_once)
         return
+    if args.latency:
+        latency(dw, torch, si, args.latency)
+        return
     log("generating input")
     x_host = si.float32_01(2, N_MAIN)
     x = torch.from_numpy(x_host).cuda()
     y = torch.empty_like(x)
     torch.cuda.synchronize()
 
-    log("timing %d steps after %d warm-up steps" % (args.steps, args.warmup))
-    elapsed, avg_kernel_s = time_back_to_back(lambda: dw.scan_inclusive(x, "add", out=y), args.steps, args.warmup,
-                                              torch)
+    step = lambda: dw.scan_inclusive(x, "add", out=y)  # noqa: E731
+    settle_launches = settle_clocks(step, args.settle_ms, torch) if args.settle_ms > 0 else 0
+    log("timing %d steps after %d warm-up steps (settle: %d launches)" % (args.steps, args.warmup, settle_launches))
+    elapsed, avg_kernel_s = time_back_to_back(step, args.steps, args.warmup, torch)
     assert dw.scan_get_device_error() == 0, "device reported a look-back timeout"
     value = N_MAIN * args.steps / elapsed / 1e9
     bytes_per_launch = 8 * N_MAIN
@@ -694,6 +938,7 @@ def main():
         "config": {"workload": "float32 inclusive add-scan, n=2^28, values uniform in [0,1) (seed 2)",
                    "n": N_MAIN, "op": "add", "variant": "inclusive", "element": "float32",
                    "kernel": "persistent single-pass tile scan, streaming prefix resolver, 15360-element tiles"},
+        "settle": {"ms": args.settle_ms, "launches": settle_launches},
         "effective_GBps": round(bytes_per_launch * args.steps / elapsed / 1e9, 1),
         "pct_of_peak": round(100 * bytes_per_launch * args.steps / elapsed / 1e9 / PEAK_GBPS, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",

@@ -16,6 +16,7 @@ import torch
 from . import build as _build
 
 SCAN_OK, SCAN_ERR_INVALID, SCAN_ERR_UNSUPPORTED, SCAN_ERR_NOMEM, SCAN_ERR_HIP, SCAN_ERR_TIMEOUT = range(6)
+SCAN_SMALL_N_AUTO = (1 << 64) - 1  # scan_set_small_n_max: one tile of the operation's shape
 OPS = {"add": 0, "max": 1, "min": 2, "affine": 3, "maxcount": 4, "mat2": 5, "mat3": 6, "and": 7, "or": 8}
 SCAN_I32, SCAN_U32, SCAN_F32, SCAN_U32X2, SCAN_I32_U32, SCAN_U32X4, SCAN_U32X9 = range(7)
 _DTYPES = {torch.int32: SCAN_I32, torch.uint32: SCAN_U32, torch.float32: SCAN_F32}

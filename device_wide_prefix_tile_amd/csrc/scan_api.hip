@@ -105,7 +105,11 @@ struct Shape {
 
 // ------------------------------------------------------------ settings
 std::mutex g_mu;
-size_t g_small_n_max = 4096;          // n at or below: single-workgroup path
+// n at or below: single-workgroup path.  SCAN_SMALL_N_AUTO: one tile of the
+// operator's shape -- measured crossover for int32 exclusive add (one
+// workgroup against one workgroup per tile, back to back): 3.8 against 4.5 us
+// at 2^12 and 2^13, 5.1 against 4.6 at 2^14 (two tiles).
+size_t g_small_n_max = SCAN_SMALL_N_AUTO;
 uint32_t g_spin_limit = 1u << 18;     // look-back polls before giving up (a fraction of a second)
 int g_multi_mode = 0;  // 0: by size; 1: one tile per workgroup; 2: persistent kernel; 3: reduce-then-scan
 // In the automatic mode the persistent kernel takes inputs of at least this
@@ -403,7 +407,7 @@ scan_status_t launch(void (*ks)(ScanParams), void (*km)(ScanParams), void (*kp)(
     if (c.noalloc && words > kScratchStatusWords) return SCAN_ERR_INVALID;  // beyond the static scratch
 
     std::lock_guard<std::mutex> lock(g_mu);
-    if (c.n <= g_small_n_max) {
+    if (c.n <= (g_small_n_max == SCAN_SMALL_N_AUTO ? (size_t)TILE : g_small_n_max)) {
         hipLaunchKernelGGL(ks, dim3(1), dim3(BLOCK), 0, c.stream, p);
         return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
     }

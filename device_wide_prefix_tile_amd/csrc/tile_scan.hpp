@@ -250,20 +250,35 @@ __device__ __forceinline__ void load_wave(const ScanParams& p, uint64_t wave_bas
             for (int j = 0; j < VEC; ++j) x[r][j] = make_value<Op>(e[j], (hb >> j) & 1u);
         }
     } else {
+        // a tile that reaches past n: lanes whose VEC elements are all below n
+        // still take one 16-byte access, the rest go element by element
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
             uint32_t hb = 0;
+            if (p.vec_ok && i0 + VEC <= p.n) {
+                E e[VEC];
+                load_vec<E, VEC>(in + i0, e);
+                if constexpr (SEG) {
+                    const uint32_t h4 = *reinterpret_cast<const uint32_t*>(p.heads + i0);
 #pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                const uint64_t i = i0 + j;
-                if (i < p.n) {
-                    uint32_t h = 0;
-                    if constexpr (SEG) h = (i == 0 || p.heads[i]) ? 1u : 0u;
-                    hb |= h << j;
-                    x[r][j] = make_value<Op>(in[i], h);
-                } else {
-                    x[r][j] = Op::identity();
+                    for (int j = 0; j < VEC; ++j) hb |= ((h4 >> (8 * j)) & 0xFFu) ? (1u << j) : 0u;
+                    if (i0 == 0) hb |= 1u;
+                }
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) x[r][j] = make_value<Op>(e[j], (hb >> j) & 1u);
+            } else {
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const uint64_t i = i0 + j;
+                    if (i < p.n) {
+                        uint32_t h = 0;
+                        if constexpr (SEG) h = (i == 0 || p.heads[i]) ? 1u : 0u;
+                        hb |= h << j;
+                        x[r][j] = make_value<Op>(in[i], h);
+                    } else {
+                        x[r][j] = Op::identity();
+                    }
                 }
             }
             raw_head[r] = hb;
@@ -339,6 +354,8 @@ __device__ __forceinline__ void apply_store(const ScanParams& p, uint64_t wave_b
         const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
         if (vec) {
             store_vec_buf<E, VEC>(rsrc, (uint32_t)((r * 64 + lane) * VEC * sizeof(E)), e);
+        } else if (p.vec_ok && i0 + VEC <= p.n) {  // partial tile, this lane's elements all below n
+            store_vec<E, VEC>(out + i0, e);
         } else {
 #pragma unroll
             for (int j = 0; j < VEC; ++j)
@@ -737,7 +754,7 @@ __device__ __forceinline__ void issue_loads(const ScanParams& p, uint64_t wave_b
     for (int r = 0; r < R; ++r) {
         const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
         h4[r] = 0;
-        if (vec) {
+        if (vec || (p.vec_ok && i0 + VEC <= p.n)) {  // whole tile, or this lane's elements all below n
             load_vec<E, VEC>(in + i0, e[r]);
             if constexpr (SEG) h4[r] = *reinterpret_cast<const uint32_t*>(p.heads + i0);
         } else {
@@ -1288,7 +1305,7 @@ __device__ __forceinline__ void store_blocked_tile(const ScanParams& p, uint64_t
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
-        if (vec) {
+        if (vec || (p.vec_ok && i0 + VEC <= p.n)) {
             store_vec<E, VEC>(out + i0, y[r]);
         } else {
 #pragma unroll

@@ -241,7 +241,10 @@ scan_status_t scan_release_workspace(void);
  * Tuning and test knobs (process-wide, thread-safe; each returns the old value).
  * scan_set_small_n_max: inputs with n at or below this size run on one
  *   workgroup that walks the tiles in order (no workspace, no atomics); larger
- *   inputs use the multi-tile look-back kernel.  Default 4096.
+ *   inputs use the multi-tile look-back kernel.  Default SCAN_SMALL_N_AUTO:
+ *   one tile of the operation's shape (15360 four-byte elements, 7680 affine
+ *   pairs, ...), where one workgroup stops being faster than one workgroup
+ *   per tile.
  * scan_set_multi_tile_mode: selects the kernel for inputs above the
  *   small-n size.  2 runs the persistent pipelined kernel (one launch of as
  *   many workgroups as fit on the GPU, each taking tile numbers from a
@@ -257,6 +260,7 @@ scan_status_t scan_release_workspace(void);
  *   gives up, records SCAN_ERR_TIMEOUT (see scan_get_device_error) and
  *   finishes with a wrong prefix instead of waiting forever.  Default 2^18.
  */
+#define SCAN_SMALL_N_AUTO ((size_t)-1)
 size_t scan_set_small_n_max(size_t n_max);
 int scan_set_multi_tile_mode(int mode);
 uint32_t scan_set_spin_limit(uint32_t polls);

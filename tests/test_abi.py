@@ -163,7 +163,8 @@ def test_radix_split_argument_checks():
 
 def test_tuning_knobs_round_trip():
     old = binding.scan_set_small_n_max(12345)
-    assert binding.scan_set_small_n_max(old) == 12345
+    assert binding.scan_set_small_n_max(binding.SCAN_SMALL_N_AUTO) == 12345
+    assert binding.scan_set_small_n_max(old) == binding.SCAN_SMALL_N_AUTO
     old = binding.scan_set_spin_limit(77)
     assert binding.scan_set_spin_limit(old) == 77
     old = binding.scan_set_multi_tile_mode(2)

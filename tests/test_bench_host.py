@@ -55,3 +55,58 @@ def test_traffic_summary_scales_by_the_copy_probe(tmp_path, monkeypatch):
 def test_source_hash_is_stable_and_covers_the_kernels():
     h = bench.kernel_source_hash()
     assert h == bench.kernel_source_hash() and len(h) == 16
+
+
+def _write_trace(directory, rows):
+    os.makedirs(directory, exist_ok=True)
+    with open(os.path.join(directory, "x_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 1000
+        for name, dur_ns in rows:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur_ns})
+            t += dur_ns + 500
+
+
+def test_dispatch_summary_takes_the_last_25_scans_before_the_copy_probe(tmp_path, monkeypatch):
+    out = tmp_path / "disp.txt"
+    monkeypatch.setattr(bench, "DISPATCH_FILE", str(out))
+    scan = "void dwpt::tile_scan_persistent<dwpt::OpAdd<float>, false, 1024, 16, 3>(dwpt::ScanParams)"
+    # 60 settle launches at 400 us, 5 warm-up at 350, 20 timed at 300, then the copy probe
+    # and a later scan launch that is not counted
+    rows = [(scan, 400000)] * 60 + [(scan, 350000)] * 5 + [(scan, 300000)] * 20
+    rows += [("(anonymous namespace)::copy_probe_kernel(x)", 1000), (scan, 1)]
+    _write_trace(tmp_path / "a", rows)
+    _write_trace(tmp_path / "b", rows[60:])
+    bench.summarize_dispatches(str(tmp_path / "a"), str(tmp_path / "b"))
+    text = out.read_text()
+    a, b = text.split("## without settle")
+    assert "settle_dispatches: 60" in a and "timed_mean_us: 300.00" in a
+    assert "settle_dispatches: 0" in b and "timed_mean_us: 300.00" in b
+    assert "warmup_us: 350.0 350.0 350.0 350.0 350.0" in b
+
+
+def test_latency_summary_splits_cases_at_the_markers(tmp_path, monkeypatch):
+    out = tmp_path / "lat.txt"
+    monkeypatch.setattr(bench, "LATENCY_FILE", str(out))
+    cases = [("case A", "add", True, 100, "int32_0_15", None, 0), ("case B", "max", False, 100, "int32_full", 0, 3)]
+    monkeypatch.setattr(bench, "LATENCY_CASES", cases)
+    mark = ("(anonymous namespace)::copy_probe_kernel(x)", 100)
+    single = ("void dwpt::tile_scan_kernel<dwpt::OpAdd<int>, true, 1024, 16, true>(dwpt::ScanParams)", 3000)
+    rts = [("void dwpt::tile_reduce_kernel<dwpt::OpMax<int>>(p)", 1000),
+           ("void dwpt::carry_scan_kernel<dwpt::OpMax<int>>(p)", 2000),
+           ("void dwpt::tile_scan_seeded_kernel<dwpt::OpMax<int>>(p)", 4000)]
+    flush = ("void at::native::vectorized_elementwise_kernel<fill>(x)", 90000)
+    rows = [single] * 3 + [mark] + [single] * 10 + [mark] + [flush, ("void dwpt::tile_scan_kernel<dwpt::OpAdd<int>, "
+                                                                    "true, 1024, 16, true>(dwpt::ScanParams)", 5000)] * 4
+    rows += [mark] + rts * 10 + [mark] + (([flush] + rts) * 3)
+    _write_trace(tmp_path / "t", rows)
+    jl = tmp_path / "lat.jsonl"
+    jl.write_text('{"case": "case A", "median_us": 6.1, "back_to_back_us": 5.0, "cold_median_us": 7.0}\n')
+    bench.summarize_latency(str(tmp_path / "t"), str(jl))
+    lines = {l.split(" | ")[0]: l.split(" | ") for l in out.read_text().splitlines() if " | " in l}
+    a, b = lines["case A"], lines["case B"]
+    assert a[1] == "tile_scan_kernel" and float(a[2]) == 3.0 and float(a[4]) == 5.0 and a[5] == "6.1"
+    assert b[1] == "tile_reduce_kernel + carry_scan_kernel + tile_scan_seeded_kernel"
+    assert float(b[2]) == 7.0 and float(b[3]) == 8.0 and float(b[4]) == 7.0  # span: three kernels + two 0.5 us gaps
+    assert b[5] == "-"

@@ -34,8 +34,9 @@ NP = {"i32": np.int32, "u32": np.uint32, "f32": np.float32}
 def gpu():
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
     dw.lib()
+    old = dw.scan_set_small_n_max(dw.SCAN_SMALL_N_AUTO)
     yield
-    dw.scan_set_small_n_max(4096)
+    dw.scan_set_small_n_max(old)
 
 
 class Path:

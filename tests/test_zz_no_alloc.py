@@ -54,7 +54,7 @@ class Mode:
 
 # small-n bound and multi-tile mode: automatic, persistent forced, one tile per workgroup
 # forced, single workgroup forced, and reduce-then-scan requested (not used without a buffer)
-PATHS = {"auto": (4096, 0), "multi": (0, 2), "fallback": (0, 1), "single": (1 << 40, 0), "rts": (0, 3)}
+PATHS = {"auto": (dw.SCAN_SMALL_N_AUTO, 0), "multi": (0, 2), "fallback": (0, 1), "single": (1 << 40, 0), "rts": (0, 3)}
 
 
 @pytest.mark.parametrize("path", list(PATHS))
