@@ -707,7 +707,7 @@ __device__ __forceinline__ typename Op::elem_t elem_identity()
 // of the lane is chunk c * 64 + lane of the wavefront's share (one 16-byte
 // access per lane and round, like every other type), and the share's tail
 // past n reads as identity words.
-template <class Op, int R, int VEC>
+template <class Op, int R, int VEC, bool LANE_VEC = true>
 __device__ __forceinline__ void issue_loads(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
                                             typename Op::elem_t (&e)[R][VEC], uint32_t (&h4)[R])
 {
@@ -754,7 +754,10 @@ __device__ __forceinline__ void issue_loads(const ScanParams& p, uint64_t wave_b
     for (int r = 0; r < R; ++r) {
         const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
         h4[r] = 0;
-        if (vec || (p.vec_ok && i0 + VEC <= p.n)) {  // whole tile, or this lane's elements all below n
+        if (vec) {
+            load_vec<E, VEC>(in + i0, e[r]);
+            if constexpr (SEG) h4[r] = *reinterpret_cast<const uint32_t*>(p.heads + i0);
+        } else if (LANE_VEC && p.vec_ok && i0 + VEC <= p.n) {  // partial tile, this lane's elements all below n
             load_vec<E, VEC>(in + i0, e[r]);
             if constexpr (SEG) h4[r] = *reinterpret_cast<const uint32_t*>(p.heads + i0);
         } else {
@@ -1202,6 +1205,9 @@ __device__ __forceinline__ void park_blocked(u32x4* tr, int lane, const E (&e)[R
 
 // Head bits of the lane's chunks in blocked order (bit j of hb[r]: element j
 // of chunk lane * R + r starts a segment; element 0 of the input always does).
+// (Packing a waiting tile's flag words into one word when the tile arrives
+// halved the segmented kernel's spills, 48 -> 24 bytes, but made it slower:
+// 214.5 -> 256 us at 2^27.)
 template <class Op, int R, int VEC>
 __device__ __forceinline__ void heads_blocked(uint64_t wave_base, int lane, const uint32_t (&h4)[R],
                                               uint32_t (&hb)[R])
@@ -1246,7 +1252,8 @@ __device__ __forceinline__ typename Op::value_t reduce_blocked(uint64_t wave_bas
 // identical outputs: affine 2^26 187.5 -> 183.8 us, 3x3 matrices 2^24
 // 528.6 -> 505.1 us.  The others keep the plain streaming hint: with the
 // descriptor they spill more at the 128-VGPR limit and were 9-19% slower
-// (segmented, (maximum, count), 2x2 matrices).
+// (segmented, (maximum, count), 2x2 matrices; segmented again with its
+// one-pass tile scan: 214.5 -> 219.5 us at 2^27).
 template <class Op> struct BlockedStorePolicy { static constexpr bool value = false; };
 template <> struct BlockedStorePolicy<OpAffine> { static constexpr bool value = true; };
 template <> struct BlockedStorePolicy<OpMat3> { static constexpr bool value = true; };
@@ -1305,7 +1312,7 @@ __device__ __forceinline__ void store_blocked_tile(const ScanParams& p, uint64_t
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint64_t i0 = wave_base + (uint64_t)(r * 64 + lane) * VEC;
-        if (vec || (p.vec_ok && i0 + VEC <= p.n)) {
+        if (vec) {
             store_vec<E, VEC>(out + i0, y[r]);
         } else {
 #pragma unroll
@@ -1317,7 +1324,7 @@ __device__ __forceinline__ void store_blocked_tile(const ScanParams& p, uint64_t
 
 // Scan of a tile held in blocked order, prefix applied, back to round order
 // through LDS, stored like apply_store.
-template <class Op, bool EXCL, int R, int VEC>
+template <class Op, bool EXCL, int R, int VEC, bool KEPT = false>
 __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
                                                    u32x4* tr, typename Op::carry_t P,
                                                    typename Op::value_t wave_prefix,
@@ -1330,6 +1337,34 @@ __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t
     const auto comb = [](V a, V b) { return Op::combine(a, b); };
     uint32_t hb[R];
     heads_blocked<Op, R, VEC>(wave_base, lane, h4, hb);
+    if constexpr (KEPT) {
+        // the lane prefix was kept from the wavefront scan of the total: one
+        // serial pass applies the prefix as it goes, with no array of in-lane
+        // prefixes held (segmented add at 2^27: 226.6 -> 215.0 us).  The other
+        // operators keep two passes: folding the lane twice instead was slower
+        // for (maximum, count) (437 -> 481 us at 2^27).
+        (void)have_lane_excl;
+        E y[R][VEC];
+        const typename Op::prep_t pc =
+            Op::prepare(Op::combine_carry(P, Op::to_carry(Op::combine(wave_prefix, lane_excl))));
+        V run = ident;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const V v = make_value<Op>(e[r][j], (hb[r] >> j) & 1u);
+                if constexpr (EXCL) {
+                    V o = Op::apply(pc, run);
+                    if constexpr (IsSeg<Op>::value)
+                        if ((hb[r] >> j) & 1u) o = ident;
+                    y[r][j] = elem_of<Op>(o);
+                }
+                run = (r == 0 && j == 0) ? v : Op::combine(run, v);
+                if constexpr (!EXCL) y[r][j] = elem_of<Op>(Op::apply(pc, run));
+            }
+        store_blocked_tile<Op, R, VEC>(p, wave_base, vec, lane, tr, y);
+        return;
+    }
     V x[R][VEC];
     V run = make_value<Op>(e[0][0], hb[0] & 1u);
     x[0][0] = run;
@@ -1416,8 +1451,8 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
     LdsWait lw(p.lb, &s_ids->abort);
     t0.set(p, get_id<counted_lds_waits<Op>()>(lw, s_ids, 0), w);
     t1.set(p, get_id<counted_lds_waits<Op>()>(lw, s_ids, 1), w);
-    if (t0.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t0.base, t0.vec, lane, e0, h0);
-    if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t1.base, t1.vec, lane, e1, h1);
+    if (t0.tile < p.num_tiles) issue_loads<Op, R, VEC, false>(p, t0.base, t0.vec, lane, e0, h0);
+    if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC, false>(p, t1.base, t1.vec, lane, e1, h1);
     if (t1.tile < p.num_tiles)
         hand_over_slot<Op, Slot, ND>(p, t1.tile, 1, w, lane,
                                      tile_wave_total<Op, R, VEC, true>(t1.base, lane, tr, nullptr, e1, h1, lx),
@@ -1438,7 +1473,7 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
                                              &s_slot[k % kPipeSlots]);
             else
                 park_blocked<R, VEC, E>(tr, lane, e0);
-            if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t1.base, t1.vec, lane, e1, h1);
+            if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC, false>(p, t1.base, t1.vec, lane, e1, h1);
         }
         Slot* slot = &s_slot[k % kPipeSlots];
         wait_seq<counted_lds_waits<Op>()>(lw, &slot->prefix_seq, k + 1);
@@ -1515,6 +1550,11 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     // the wavefront scan of its total (for the other blocked operators the
     // extra registers cost more than the second wavefront scan: measured)
     constexpr bool KEEP = BLK && IsSeg<Op>::value;
+    // 16-byte lane loads in the last, partial tile: for the round-order
+    // operators only; in the blocked kernels the extra branch (and the same
+    // one in their stores) moved the register allocation: (maximum, count) at
+    // 2^27 438 -> 471 us, 2x2 matrices at 2^26 476 -> 503-526
+    constexpr bool LANE_VEC = !BLK;
     V lx[kPipeTiles];
     WaveTile<G> t[kPipeTiles];
     LdsWait lw(p.lb, &s_ids.abort);
@@ -1523,7 +1563,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     // the first batch: every tile loaded and its total published up front
 #pragma unroll
     for (int q = 0; q < kPipeTiles; ++q)
-        if (t[q].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[q].base, t[q].vec, lane, e[q], h[q]);
+        if (t[q].tile < p.num_tiles) issue_loads<Op, R, VEC, LANE_VEC>(p, t[q].base, t[q].vec, lane, e[q], h[q]);
 #pragma unroll
     for (int q = 0; q < kPipeTiles; ++q)
         if (t[q].tile < p.num_tiles)
@@ -1537,7 +1577,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
         uint32_t next_id = p.num_tiles;
         if (w == 0) next_id = ask_id(p, exhausted);
         // stages still holding the first batch were loaded and published above
-        if (k >= 1 && t[NEW].tile < p.num_tiles) issue_loads<Op, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], h[NEW]);
+        if (k >= 1 && t[NEW].tile < p.num_tiles) issue_loads<Op, R, VEC, LANE_VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], h[NEW]);
         if (k >= 2 && t[PUB].tile < p.num_tiles)
             hand_over_slot<Op, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane,
                                          tile_wave_total<Op, R, VEC, BLK>(t[PUB].base, lane, tr, trh, e[PUB], h[PUB], lx[PUB]),
@@ -1550,8 +1590,8 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
 #pragma unroll
             for (int q = 0; q < ND; ++q)
                 if (q < w) wave_prefix = Op::combine(wave_prefix, slot->wave_total[q]);
-            scan_store_blocked<Op, EXCL, R, VEC>(p, t[0].base, t[0].vec, lane, tr, slot->prefix, wave_prefix, e[0],
-                                                 h[0], lx[0], KEEP);
+            scan_store_blocked<Op, EXCL, R, VEC, KEEP>(p, t[0].base, t[0].vec, lane, tr, slot->prefix, wave_prefix,
+                                                       e[0], h[0], lx[0], KEEP);
         } else {
             V x[R][VEC], lane_excl[R], round_carry[R + 1];
             uint32_t raw_head[R];
