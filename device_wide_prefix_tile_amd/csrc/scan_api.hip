@@ -77,10 +77,10 @@ namespace {
 #define DWPT_WAIT_SEG 2
 #endif
 #ifndef DWPT_ITEMS_COMPACT     // stream compaction
-#define DWPT_ITEMS_COMPACT 12
+#define DWPT_ITEMS_COMPACT 20
 #endif
 #ifndef DWPT_WAIT_COMPACT
-#define DWPT_WAIT_COMPACT 4
+#define DWPT_WAIT_COMPACT 3
 #endif
 template <class Op>
 struct Shape {

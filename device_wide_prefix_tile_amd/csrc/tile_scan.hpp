@@ -1623,13 +1623,32 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     if (w == 0 && lane == 0) retire_workgroup(p);
 }
 
-// Writes a wavefront's cnt packed elements from LDS to out[dst ...), with
-// the streaming hint (measured: 333 -> 329 us for the float32 compaction at
-// 2^28; 16-byte stores after an element-wise head gave 330).
-template <typename T>
-__device__ __forceinline__ void write_packed(T* __restrict__ out, uint64_t dst, const T* region, uint32_t cnt, int lane)
+// Persistent compaction.  A tile's kept elements leave as one contiguous run:
+// every data wavefront packs its kept elements into a tile buffer in LDS at
+// the wavefront's offset within the tile's run, and once all of them have
+// packed, all write the run out together in 16-byte chunks aligned in global
+// memory, so that partial lines occur only at the two ends of a tile's run
+// (wavefront-by-wavefront runs put 15 seams in every tile, whose lines were
+// written twice: 1.042x the algorithmic bytes).  The buffer is placed so that
+// its chunks line up with the output's 16-byte chunks.  Two tile buffers
+// alternate; LDS counters order their reuse (all waits end: every data
+// wavefront of the workgroup processes the same tiles, and only waits for the
+// others to reach the same point of the same tile).
+//
+// Kept counts: per round, at most 64 * VEC elements of a wavefront are kept,
+// so three rounds' counts fit 10-bit fields of one word, and one wavefront
+// scan of that word gives the lane's exclusive count in each of them and, in
+// lane 63, the wavefront's round totals (in place of one scan per round).
+constexpr int kCountBits = 10, kCountsPerWord = 3;
+template <int R>
+__device__ __forceinline__ uint32_t count_field(const uint32_t (&w)[(R + kCountsPerWord - 1) / kCountsPerWord], int r)
 {
-    for (uint32_t i = lane; i < cnt; i += 64) __builtin_nontemporal_store(region[i], out + dst + i);
+    return (w[r / kCountsPerWord] >> (kCountBits * (r % kCountsPerWord))) & ((1u << kCountBits) - 1u);
+}
+
+__device__ __forceinline__ void wait_at_least(uint32_t* c, uint32_t want)
+{
+    while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < want) __builtin_amdgcn_s_sleep(1);
 }
 
 template <typename T, int BLOCK, int ITEMS, int WAIT>
@@ -1642,14 +1661,22 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
     using G = Geometry<Cnt, BLOCK, ITEMS>;
     using Slot = PipeSlot<uint32_t, uint32_t, G::ND>;
     constexpr int R = G::R, VEC = G::VEC, ND = G::ND;
-    static_assert(sizeof(T) == 4, "4-byte elements");
+    static_assert(sizeof(T) == 4 && VEC == 4, "4-byte elements, 16-byte chunks");
+    static_assert(64 * VEC < (1 << kCountBits), "packed round counts");
+    constexpr int CW = (R + kCountsPerWord - 1) / kCountsPerWord;  // words of packed counts
+    constexpr int RUN = G::TILE + 4;  // a tile's run and up to 3 elements of alignment
 
-    __shared__ T s_keep[G::TILE];  // wavefront w packs into [w * WAVE_ELEMS, ...)
+    __shared__ __align__(16) T s_run[2][RUN];
+    __shared__ uint32_t s_packed[2], s_written[2];  // arrivals per buffer, over all its uses
     __shared__ Slot s_slot[kPipeSlots];
     __shared__ TileIdRing s_ids;
     __shared__ uint32_t s_role;
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
+    if (threadIdx.x < 2) {
+        s_packed[threadIdx.x] = 0u;
+        s_written[threadIdx.x] = 0u;
+    }
     if (start_workgroup(p, s_slot, &s_ids, &s_role) == 0) {
         if (w == 0) {
             const uint32_t total = resolve_stream<Cnt, ResolveSpan<Cnt>::value>(p.lb, p.lb.status, p.lb.groups, p.num_tiles);
@@ -1662,14 +1689,16 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
     }
     bool exhausted = false;
     if (w == 0) exhausted = take_first_ids<kPipeTiles>(p, &s_ids);
-    T* __restrict__ out = static_cast<T*>(p.out);
     if (w == ND) {
         fetch_prefixes<Cnt>(p, &s_ids, s_slot);
         return;
     }
+    T* __restrict__ out = static_cast<T*>(p.out);
+    // the output's offset from a 16-byte boundary, in elements
+    const uint32_t out_mis = (uint32_t)(((uintptr_t)out >> 2) & 3u);
 
     // elements past n were loaded as the lowest value of T, which is never kept
-    const auto kept_bits = [&](const T (&e)[R][VEC], uint64_t, uint32_t (&kept)[R]) {
+    const auto kept_bits = [&](const T (&e)[R][VEC], uint32_t (&kept)[R]) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             uint32_t b = 0;
@@ -1678,18 +1707,31 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
             kept[r] = b;
         }
     };
-    const auto count_wave = [&](const T (&e)[R][VEC], uint64_t base) {
+    // the wavefront's kept count; xcl: the lane's exclusive packed counts, tot: the round totals
+    const auto count_wave = [&](const T (&e)[R][VEC], uint32_t (&xcl)[CW], uint32_t (&tot)[CW]) {
         uint32_t kept[R];
-        kept_bits(e, base, kept);
-        uint32_t c = 0;
+        kept_bits(e, kept);
+        uint32_t c[CW];
 #pragma unroll
-        for (int r = 0; r < R; ++r) c += (uint32_t)__builtin_popcount(kept[r]);
+        for (int q = 0; q < CW; ++q) c[q] = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            c[r / kCountsPerWord] += (uint32_t)__builtin_popcount(kept[r]) << (kCountBits * (r % kCountsPerWord));
         const auto add = [](uint32_t a, uint32_t b) { return a + b; };
-        return read_lane(wave_inclusive_scan(c, 0u, add), 63);
+        uint32_t sum = 0;
+#pragma unroll
+        for (int q = 0; q < CW; ++q) {
+            const uint32_t incl = wave_inclusive_scan(c[q], 0u, add);
+            xcl[q] = incl - c[q];
+            tot[q] = read_lane(incl, 63);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) sum += count_field<R>(tot, r);
+        return sum;
     };
 
-    T* region = s_keep + w * G::WAVE_ELEMS;
     T e[kPipeTiles][R][VEC];
+    uint32_t xcl[kPipeTiles][CW], tot[kPipeTiles][CW];
     uint32_t hu[R];
     WaveTile<G> t[kPipeTiles];
     LdsWait lw(p.lb, &s_ids.abort);
@@ -1701,29 +1743,75 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
 #pragma unroll
     for (int q = 0; q < kPipeWait - 1; ++q)
         if (t[q].tile < p.num_tiles)
-            hand_over_slot<Cnt, Slot, ND>(p, t[q].tile, q, w, lane, count_wave(e[q], t[q].base), &s_slot[q % kPipeSlots]);
+            hand_over_slot<Cnt, Slot, ND>(p, t[q].tile, q, w, lane, count_wave(e[q], xcl[q], tot[q]),
+                                          &s_slot[q % kPipeSlots]);
     for (uint32_t k = 0; t[0].tile < p.num_tiles; ++k) {
         constexpr int NEW = kPipeTiles - 1, PUB = kPipeWait - 1;
         uint32_t next_id = p.num_tiles;
         if (w == 0) next_id = ask_id(p, exhausted);
         if (t[NEW].tile < p.num_tiles) issue_loads<Ld, R, VEC>(p, t[NEW].base, t[NEW].vec, lane, e[NEW], hu);
         if (t[PUB].tile < p.num_tiles)
-            hand_over_slot<Cnt, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane, count_wave(e[PUB], t[PUB].base),
+            hand_over_slot<Cnt, Slot, ND>(p, t[PUB].tile, k + PUB, w, lane, count_wave(e[PUB], xcl[PUB], tot[PUB]),
                                           &s_slot[(k + PUB) % kPipeSlots]);
         Slot* slot = &s_slot[k % kPipeSlots];
-        uint32_t kept[R];
-        kept_bits(e[0], t[0].base, kept);
-        const uint32_t cnt = pack_wave<T, R, VEC>(e[0], kept, region);
         wait_seq<false>(lw, &slot->prefix_seq, k + 1);
-        uint32_t wave_prefix = 0;
+        uint32_t wave_prefix = 0, run_len = 0;
 #pragma unroll
-        for (int q = 0; q < ND; ++q)
-            if (q < w) wave_prefix += slot->wave_total[q];
-        const uint64_t dst = (uint64_t)slot->prefix + wave_prefix;
-        write_packed<T>(out, dst, region, cnt, lane);
+        for (int q = 0; q < ND; ++q) {
+            const uint32_t c = slot->wave_total[q];
+            if (q < w) wave_prefix += c;
+            run_len += c;
+        }
+        const uint64_t g0 = slot->prefix;  // output index of the tile's first kept element
+        const uint32_t shift = (uint32_t)((g0 + out_mis) & 3u);
+        const uint32_t b = k & 1u, use = k >> 1;
+        T* buf = s_run[b];
+        // the buffer's previous tile is out
+        wait_at_least(&s_written[b], (uint32_t)ND * use);
+        {
+            uint32_t kept[R];
+            kept_bits(e[0], kept);
+            uint32_t base = shift + wave_prefix;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                uint32_t rank = base + count_field<R>(xcl[0], r);
+#pragma unroll
+                for (int j = 0; j < VEC; ++j)
+                    if ((kept[r] >> j) & 1u) buf[rank++] = e[0][r][j];
+                base += count_field<R>(tot[0], r);
+            }
+        }
+        if (lane == 0) __hip_atomic_fetch_add(&s_packed[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        wait_at_least(&s_packed[b], (uint32_t)ND * (use + 1));
+        // chunk m of the buffer holds output elements g0 - shift + 4m ... + 3
+        if (run_len > 0) {
+            const uint32_t chunks = (shift + run_len + 3) / 4;
+            T* __restrict__ dst = out + (g0 - shift);
+            for (uint32_t m = (uint32_t)w * 64 + lane; m < chunks; m += ND * 64) {
+                const uint32_t lo = 4 * m, hi = 4 * m + 4;
+                if (lo >= shift && hi <= shift + run_len) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(buf + lo);
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + lo));
+                } else {
+                    // the run's first or last chunk: its elements one by one, read
+                    // from LDS one by one (taking them out of a 16-byte LDS read
+                    // here was compiled into four stores of its first word)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (lo + j >= shift && lo + j < shift + run_len)
+                            __builtin_nontemporal_store(buf[lo + j], dst + lo + j);
+                }
+            }
+        }
+        if (lane == 0) __hip_atomic_fetch_add(&s_written[b], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
         for (int q = 0; q + 1 < kPipeTiles; ++q) {
             t[q] = t[q + 1];
+#pragma unroll
+            for (int c = 0; c < CW; ++c) {
+                xcl[q][c] = xcl[q + 1][c];
+                tot[q][c] = tot[q + 1][c];
+            }
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll

@@ -21,12 +21,12 @@ from parity_helpers import assert_equal, assert_f32_close, from_dev, to_dev
 pytestmark = pytest.mark.gpu
 
 TILE = 15 * 64 * 16   # elements per tile of plain 4-byte scans (15 data wavefronts x 64 lanes x 16)
-TILE12 = 15 * 64 * 12  # elements per tile of compaction
+TILE_C = 15 * 64 * 20  # elements per tile of compaction
 TILE_SEG = 15 * 64 * 16  # elements per tile of segmented scans (16 consecutive elements per lane in the
                          # persistent kernel, 1024 per wavefront)
 TILE8 = 15 * 64 * 8   # pairs per tile of the 8-byte affine type
-SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1000, 4097, TILE8 - 1, TILE8, TILE8 + 1, TILE12 - 1, TILE12,
-         TILE12 + 1, TILE - 1, TILE, TILE + 1, 3 * TILE + 17, 65536 + 1, 250001, 1000003]
+SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1000, 4097, TILE8 - 1, TILE8, TILE8 + 1, TILE_C - 1, TILE_C,
+         TILE_C + 1, TILE - 1, TILE, TILE + 1, 3 * TILE + 17, 65536 + 1, 250001, 1000003]
 NP = {"i32": np.int32, "u32": np.uint32, "f32": np.float32}
 
 
@@ -334,7 +334,7 @@ HEAD_MIXES = {
 @pytest.mark.parametrize("op", ["add", "max", "min"])
 @pytest.mark.parametrize("exclusive", [False, True], ids=["incl", "excl"])
 def test_segmented_parity(op, dt, exclusive):
-    for k, n in enumerate([1, 2, 65, TILE12 - 1, TILE12 + 1, TILE_SEG - 1, TILE_SEG + 1, 3 * TILE_SEG + 17, 250001,
+    for k, n in enumerate([1, 2, 65, TILE_C - 1, TILE_C + 1, TILE_SEG - 1, TILE_SEG + 1, 3 * TILE_SEG + 17, 250001,
                            1000003]):
         x = values(dt, n, 300 + k) if dt != "i32" else si.int32_pm100(300 + k, n)
         for mix, gen in HEAD_MIXES.items():
@@ -397,6 +397,28 @@ def test_compact_special_values():
         ref, rc, _ = oracle.compact(x)
         assert cnt == rc == 3000
         assert_equal(out[:cnt], ref, "special values path=%s" % path)
+
+
+@pytest.mark.parametrize("path", ["multi", "fallback", "single"])
+def test_compact_output_offsets(path):
+    """Outputs that start 4, 8 or 12 bytes past a 16-byte boundary (the persistent kernel
+    writes each tile's run in 16-byte chunks aligned in memory), with inputs aligned and not,
+    over several tiles and a ragged tail; nothing outside [0, count) is written."""
+    n = 5 * TILE_C + 333
+    x = si.float32_normal(71, n)
+    ref, rc, _ = oracle.compact(x)
+    for k, (in_off, out_off) in enumerate([(0, 1), (0, 2), (0, 3), (1, 1), (3, 2)]):
+        xd = to_dev(np.concatenate([np.zeros(in_off, np.float32), x]))[in_off:]
+        buf = torch.full((n + 8,), 5.5, dtype=torch.float32, device="cuda")
+        o = buf[out_off:out_off + n]
+        with Path(path):
+            _, cnt = dw.compact(xd, out=o)
+            cnt = int(from_dev(cnt)[0])
+        b = from_dev(buf)
+        what = "compact offsets in=%d out=%d path=%s" % (in_off, out_off, path)
+        assert cnt == rc, what
+        assert_equal(b[out_off:out_off + cnt], ref, what)
+        assert np.all(b[:out_off] == np.float32(5.5)) and np.all(b[out_off + cnt:] == np.float32(5.5)), what
 
 
 def test_compact_leaves_tail_untouched():
