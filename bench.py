@@ -84,7 +84,7 @@ PROFILE_CMDS = {
     "wl_write": "rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/prof_wl_write -o wl -- "
                 "python3 bench.py --workloads-once 3",
     "wl_trace": "rocprofv3 --kernel-trace -f csv -d $OUT/prof_wl_trace -o wl -- "
-                "python3 bench.py --workloads-once 40",
+                "python3 bench.py --workloads-once 40 --settle-ms 200",
     "latency": "rocprofv3 --kernel-trace -f csv -d $OUT/prof_lat -o lat -- "
                "python3 bench.py --latency $OUT/latency_traced.jsonl",
     "driver": "rocprofv3 --kernel-trace --stats -f csv -d $OUT/prof_drv -o drv -- "
@@ -310,8 +310,8 @@ def summarize_workload_traffic(fetch_dir, write_dir):
 
 def summarize_workload_trace(trace_dir):
     """Kernel durations of every full-size workload's dominant kernel (kernel trace of
-    --workloads-once K: the median over the last half of each kernel's K dispatches, after
-    the clocks have settled) against its algorithmic bytes."""
+    --workloads-once K --settle-ms 200: the median over the last 20 of the kernel's dispatches,
+    which follow 200 ms of untimed ones) against its algorithmic bytes."""
     import numpy as np
     import seeded_inputs as si
     durs = {w[1]: [] for w in WORKLOADS}
@@ -323,7 +323,8 @@ def summarize_workload_trace(trace_dir):
     kept = int(np.count_nonzero(si.float32_normal(3, 1 << 28) > 0))
     out = ["# Kernel duration per launch of each full-size workload's main kernel (rocprofv3 kernel trace)",
            "# command: " + PROFILE_CMDS["wl_trace"],
-           "# median over the last half of the kernel's dispatches; GB/s = algorithmic bytes / duration",
+           "# median over the kernel's last 20 dispatches (after 200 ms of untimed ones); GB/s = algorithmic",
+           "# bytes / duration",
            "source_hash: " + kernel_source_hash(),
            "# workload | kernel | dispatches | median us | algorithmic MB | GB/s | % of 8 TB/s"]
     for label, frag, n, alg in WORKLOADS:
@@ -331,7 +332,7 @@ def summarize_workload_trace(trace_dir):
         if not d:
             out.append("%s | %s | 0 | missing" % (label, frag))
             continue
-        med = statistics.median(d[len(d) // 2:])
+        med = statistics.median(d[-20:])
         a = alg(n, kept)
         out.append("%s | %s | %d | %.2f | %.1f | %.1f | %.1f" % (label, frag, len(d), med, a / 1e6,
                                                                 a / (med * 1e-6) / 1e9,
@@ -537,74 +538,69 @@ def latency(dw, torch, si, out_path, steps=200):
     print(json.dumps({"latency_cases": len(lines), "all_last_ok": all(l["last_ok"] for l in lines)}), flush=True)
 
 
-def workloads_once(dw, torch, si, steps):
-    """Each full-size workload `steps` times, one input resident at a time (for counter runs)."""
+def workloads_once(dw, torch, si, steps, settle_ms=0.0):
+    """Each full-size workload `steps` times, one input resident at a time (for counter runs
+    and kernel traces); with settle_ms, each workload first runs untimed for that long, so
+    that the traced launches are past the clock transient that follows the input's upload."""
     import numpy as np
+
+    def run(fn):
+        if settle_ms > 0:
+            settle_clocks(fn, settle_ms, torch)
+        for _ in range(steps):
+            fn()
     a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1.0)
-    for _ in range(steps):
-        dw.scan_copy_probe(a, b)
+    run(lambda: dw.scan_copy_probe(a, b))
     del a, b
     x = torch.from_numpy(si.float32_01(2, 1 << 28)).cuda()
     y = torch.empty_like(x)
-    for _ in range(steps):
-        dw.scan_inclusive(x, "add", out=y)
+    run(lambda: dw.scan_inclusive(x, "add", out=y))
     del x, y
     x = torch.from_numpy(si.int32_0_15(1, 1 << 28)).cuda()
     y = torch.empty_like(x)
-    for _ in range(steps):
-        dw.scan_exclusive(x, "add", out=y)
-    for _ in range(steps):
-        dw.scan_inclusive(x, "max", out=y)
+    run(lambda: dw.scan_exclusive(x, "add", out=y))
+    run(lambda: dw.scan_inclusive(x, "max", out=y))
     del x, y
     x = torch.from_numpy(si.float32_normal(3, 1 << 28)).cuda()
     y = torch.empty_like(x)
     cnt = torch.zeros(1, dtype=torch.uint32, device="cuda")
-    for _ in range(steps):
-        dw.compact(x, out=y, count=cnt)
+    run(lambda: dw.compact(x, out=y, count=cnt))
     del x, y
     ab = torch.from_numpy(si.affine_pairs(4, 1 << 26)).cuda()
     yab = torch.empty_like(ab)
-    for _ in range(steps):
-        dw.scan_inclusive(ab, "affine", out=yab)
+    run(lambda: dw.scan_inclusive(ab, "affine", out=yab))
     del ab, yab
     xs = torch.from_numpy(si.int32_pm100(5, 1 << 27)).cuda()
     hs = torch.from_numpy(si.segment_heads(5, 1 << 27, 1000.0)).cuda()
     ys = torch.empty_like(xs)
-    for _ in range(steps):
-        dw.segmented_scan(xs, hs, "add", out=ys)
+    run(lambda: dw.segmented_scan(xs, hs, "add", out=ys))
     del xs, hs, ys
     vc = torch.from_numpy(si.maxcount_pairs(8, 1 << 27)).cuda()
     yvc = torch.empty_like(vc)
-    for _ in range(steps):
-        dw.scan_inclusive(vc, "maxcount", out=yvc)
+    run(lambda: dw.scan_inclusive(vc, "maxcount", out=yvc))
     del vc, yvc
     m = torch.from_numpy(si.mat2_elems(9, 1 << 25)).cuda()
     ym = torch.empty_like(m)
-    for _ in range(steps):
-        dw.scan_inclusive(m, "mat2", out=ym)
+    run(lambda: dw.scan_inclusive(m, "mat2", out=ym))
     del m, ym
     m3 = torch.from_numpy(si.mat3_elems(10, 1 << 24)).cuda()
     ym3 = torch.empty_like(m3)
-    for _ in range(steps):
-        dw.scan_inclusive(m3, "mat3", out=ym3)
+    run(lambda: dw.scan_inclusive(m3, "mat3", out=ym3))
     del m3, ym3
     nnz, n_rows = 1 << 27, 1 << 23
     rows = torch.from_numpy(np.sort(si.uint32_full(10, nnz) % n_rows).astype(np.uint32)).cuda()
     rp = torch.empty(n_rows + 1, dtype=torch.uint32, device="cuda")
-    for _ in range(steps):
-        dw.csr_row_offsets(rows, n_rows, out=rp)
+    run(lambda: dw.csr_row_offsets(rows, n_rows, out=rp))
     del rows, rp
     bins = torch.from_numpy((si.uint32_full(11, nnz) % 256).astype(np.uint32)).cuda()
     bp = torch.empty(257, dtype=torch.uint32, device="cuda")
-    for _ in range(steps):
-        dw.csr_row_offsets(bins, 256, out=bp)
+    run(lambda: dw.csr_row_offsets(bins, 256, out=bp))
     del bins, bp
     k = torch.from_numpy(si.uint32_full(11, 1 << 28)).cuda()
     ko = torch.empty_like(k)
-    for _ in range(steps):
-        dw.radix_split(k, 8, keys_out=ko)
+    run(lambda: dw.radix_split(k, 8, keys_out=ko))
     del k, ko
     torch.cuda.synchronize()
     err = dw.scan_get_device_error()
@@ -878,6 +874,7 @@ def main():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the per-workload traffic summary under profiles/ and exit")
     args = ap.parse_args()
+    args.settle_given = "--settle-ms" in sys.argv
     if args.summarize_rocprof:
         summarize_rocprof(*args.summarize_rocprof)
         return
@@ -910,7 +907,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dw.lib()
     if args.workloads_once:
-        workloads_once(dw, torch, si, args.workloads_once)
+        workloads_once(dw, torch, si, args.workloads_once, args.settle_ms if args.settle_given else 0.0)
         return
     if args.latency:
         latency(dw, torch, si, args.latency)
