@@ -682,7 +682,7 @@ scan_status_t radix_split(const uint32_t* keys, const uint32_t* vals, size_t n, 
             if (st != SCAN_OK) return st;
         }
         uint32_t* h = static_cast<uint32_t*>(hist);
-        hipLaunchKernelGGL(radix_hist_kernel, dim3(T), dim3(kRsBlock), 0,
+        hipLaunchKernelGGL(radix_hist_kernel, dim3((T + kHistTiles - 1) / kHistTiles), dim3(kRsBlock), 0,
                            s, keys, (uint64_t)n, shift, T, h, is_aligned(keys, 16) ? 1 : 0);
         if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
         // each (digit, tile) count -> the output position of its first key
