@@ -124,6 +124,7 @@ __global__ __launch_bounds__(kRsBlock) void radix_hist_kernel(const uint32_t* __
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
     const uint32_t G = (T + kHistTiles - 1) / kHistTiles;
+    if (blockIdx.x >= G) return;  // a grid of G workgroups is expected; never index past the tiles
     const uint32_t t0 = rs_tile(blockIdx.x, G) * kHistTiles;
     const uint32_t t1 = t0 + kHistTiles < T ? t0 + kHistTiles : T;
     for (int i = threadIdx.x; i < kRsDigits * kRsCopies; i += kRsBlock) s_cnt[i] = 0u;
