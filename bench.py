@@ -13,10 +13,10 @@ included).
 Before the warm-up steps the step runs untimed, back to back, for about
 --settle-ms (default 200 ms): after the GPU has been idle, launches 6-40 of
 this size run 3-9% slower than the first five and than every later one (a
-clock/power transient of the chip, not of the kernel: a plain copy sees it
-too, and 100 ms of any load before the timed launches removes it).  With 5
-warm-up steps the timed region would otherwise sit inside the transient.
-The JSON line records the settle time and launch count.
+transient of the GPU's clocks or power state: the kernel is the same, and
+100 ms of load before the timed launches removes it).  With 5 warm-up steps
+the timed region would otherwise sit inside the transient.  The JSON line
+records the settle time and launch count.
 
 Prints one JSON line.  value = Gelem/s (n * K / elapsed).  Effective HBM
 traffic counts the minimal 1 read + 1 write per element (8 bytes).
@@ -727,7 +727,7 @@ def suite(dw, torch, si, out_path, steps):
 
     def rec(name, n, bytes_per_elem, fn):
         log("suite: " + name)
-        # the clocks settle over the first ~100 launches; median_us: one call's time,
+        # 100 launches warm the workload up; median_us: one call's time,
         # each launch between its own event pair (latency); the rates: the same number
         # of launches back to back (throughput, gaps between launches included)
         elapsed, ms = time_launches(fn, steps, 100, torch)
@@ -850,8 +850,7 @@ def suite(dw, torch, si, out_path, steps):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU's clocks settle over the first ~100 launches (measured: 360.6 us
-    # median over launches 1-100, 356-357.6 us for every later block of 100)
+    # defaults: 200 warm-up and 200 timed launches (about 0.14 s of GPU time)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--settle-ms", type=float, default=200.0,
