@@ -23,14 +23,18 @@ namespace {
 
 // ------------------------------------------------------------ tile shapes
 // Workgroup size, elements per lane and pipeline depth per class of scan
-// (defaults: 1024 threads = 15 data wavefronts + 1 prefix wavefront; the 3x3
-// matrices take 512).  ITEMS sets the tile ((BLOCK / 64 - 1) * 64 * ITEMS
+// (defaults: 1024 threads = 15 data wavefronts + 1 prefix wavefront; (maximum,
+// count) pairs and 2x2 and 3x3 matrices take 512, whose 8 wavefronts may use
+// 256 registers per lane).  ITEMS sets the tile ((BLOCK / 64 - 1) * 64 * ITEMS
 // elements); WAIT is the number of tiles per data wavefront that wait on
-// their prefix in the persistent kernel.  Each class takes the deepest
-// pipeline that fits in the registers (128 per lane at 1024 threads), then
-// the measured best tile; the matrix classes spill some registers at their
-// fastest measured shape.  Build-time switches, so that shapes can be
-// compared by measurement.
+// their prefix in the persistent kernel.  Each class takes the measured best
+// shape: (maximum, count) at 2^27 436 us with 1024 threads x 6 per lane, WAIT
+// 3, 365 us with 512 x 16, WAIT 4 (512 x 12/20 at WAIT 3-4: 367-399); 2x2
+// matrices at 2^26 474 -> 413 us with 512 x 8, WAIT 4 (512 x 6 or 12: 469
+// and more); affine and segmented scans were slower at 512 threads (affine
+// 354 against 347, segmented 248 against 214 at their best 512 shapes).
+// The 3x3 matrices still spill at their fastest measured shape.
+// Build-time switches, so that shapes can be compared by measurement.
 #ifndef DWPT_BLOCK
 #define DWPT_BLOCK 1024
 #endif
@@ -46,20 +50,23 @@ namespace {
 #ifndef DWPT_WAIT8
 #define DWPT_WAIT8 3
 #endif
-#ifndef DWPT_ITEMS_MC          // (max, count) pairs
-#define DWPT_ITEMS_MC 6
+#ifndef DWPT_BLOCK_MC          // (max, count) pairs: 512 threads, so up to 256 registers per lane
+#define DWPT_BLOCK_MC 512
+#endif
+#ifndef DWPT_ITEMS_MC
+#define DWPT_ITEMS_MC 16
 #endif
 #ifndef DWPT_WAIT_MC
-#define DWPT_WAIT_MC 3
+#define DWPT_WAIT_MC 4
 #endif
 #ifndef DWPT_ITEMS16           // 16-byte values (2x2 matrices)
-#define DWPT_ITEMS16 4
+#define DWPT_ITEMS16 8
 #endif
 #ifndef DWPT_WAIT16
-#define DWPT_WAIT16 3
+#define DWPT_WAIT16 4
 #endif
 #ifndef DWPT_BLOCK16
-#define DWPT_BLOCK16 DWPT_BLOCK
+#define DWPT_BLOCK16 512
 #endif
 #ifndef DWPT_BLOCK36           // 36-byte values (3x3 matrices): 512 threads, so 256 registers per lane
 #define DWPT_BLOCK36 512
@@ -86,8 +93,8 @@ template <class Op>
 struct Shape {
     static constexpr bool SEG = IsSeg<Op>::value, WIDE = sizeof(typename Op::elem_t) == 8,
                           WIDE16 = sizeof(typename Op::elem_t) == 16, WIDE36 = sizeof(typename Op::elem_t) == 36;
-    static constexpr int BLOCK = WIDE36 ? DWPT_BLOCK36 : WIDE16 ? DWPT_BLOCK16 : DWPT_BLOCK;
     static constexpr bool MC = std::is_same<Op, OpMaxCount>::value;
+    static constexpr int BLOCK = MC ? DWPT_BLOCK_MC : WIDE36 ? DWPT_BLOCK36 : WIDE16 ? DWPT_BLOCK16 : DWPT_BLOCK;
     static constexpr int ITEMS = SEG      ? DWPT_ITEMS_SEG
                                  : MC     ? DWPT_ITEMS_MC
                                  : WIDE36 ? DWPT_ITEMS36

@@ -209,7 +209,7 @@ scan_status_t radix_split(const uint32_t* keys, const uint32_t* vals, size_t n, 
  * are rejected with SCAN_ERR_INVALID before anything is launched: tiles *
  * words * 17 * 8 bytes must fit in 16 MiB - 640 bytes, with tiles = ceil(n /
  * tile) and (tile, words) = (15360, 1) for ADD, MAX, MIN, AND, OR over
- * I32, U32 and F32, (7680, 2) AFFINE, (5760, 2) MAX_COUNT, (3840, 4) MAT2,
+ * I32, U32 and F32, (7680, 2) AFFINE, (7168, 2) MAX_COUNT, (3584, 4) MAT2,
  * (3584, 9) MAT3 -- e.g. n up to 1,894,763,520 for the 4-byte types.  Every call on a GPU shares that
  * GPU's array (the last call's contents stay in it): calls that overlap in
  * time on one GPU, e.g. on two streams, race and give wrong results; calls

@@ -168,8 +168,8 @@ def test_affine_parity(exclusive, odd):
 
 
 # ---------------------------------------------------------------- composite and matrix operators
-TILE_MC = 15 * 64 * 6   # (value, count) pairs per tile
-TILE_M2 = 15 * 64 * 4   # 2x2 matrices per tile
+TILE_MC = 7 * 64 * 16  # (value, count) pairs per tile (512-thread workgroups: 7 data wavefronts)
+TILE_M2 = 7 * 64 * 8   # 2x2 matrices per tile
 PAIR_SIZES = [1, 2, 63, 64, 65, 1000, 4097, TILE_M2 - 1, TILE_M2, TILE_M2 + 1, TILE_MC - 1, TILE_MC,
               TILE_MC + 1, 3 * TILE_MC + 17, 65537, 250001]
 
