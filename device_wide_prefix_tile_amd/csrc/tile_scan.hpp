@@ -840,6 +840,9 @@ __device__ __forceinline__ void hand_over_slot(const ScanParams& p, uint32_t til
     if (old != (k / kPipeSlots) * ND + (ND - 1)) return;  // not the last data wavefront of this use
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     V total = Op::identity();
+    // (Folding the exclusive wavefront prefixes here, once, into the slot for the
+    // data wavefronts to read made the float32 add at 2^28 11 us slower and the
+    // 3x3 matrices 1-2% faster: not kept.)
 #pragma unroll
     for (int q = 0; q < ND; ++q) total = Op::combine(total, slot->wave_total[q]);
     if (lane == 0) publish<Op>(p.lb, p.lb.status, (uint64_t)tile * DWPT_AGG_PAD, Op::to_carry(total), kStateAggregate);
@@ -1258,6 +1261,43 @@ template <class Op> struct BlockedStorePolicy { static constexpr bool value = fa
 template <> struct BlockedStorePolicy<OpAffine> { static constexpr bool value = true; };
 template <> struct BlockedStorePolicy<OpMat3> { static constexpr bool value = true; };
 
+// Elements wider than 16 bytes: a wavefront's share in round order, chunk c
+// of this lane being chunk c * 64 + lane of the share (see issue_loads),
+// stored like apply_store.
+template <class Op, int R, int VEC>
+__device__ __forceinline__ void store_round_chunks(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
+                                                   const u32x4 (&v)[R * VecShape<typename Op::elem_t>::K])
+{
+    using E = typename Op::elem_t;
+    constexpr int K = VecShape<E>::K;
+    constexpr int C = R * K, W = (int)sizeof(E) / 4;
+    uint32_t* __restrict__ dst = static_cast<uint32_t*>(p.out) + wave_base * W;
+    if (vec && BlockedStorePolicy<Op>::value) {
+        const __amdgpu_buffer_rsrc_t rsrc = wave_rsrc(dst);
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+            __builtin_amdgcn_raw_buffer_store_b128(v[c], rsrc, (uint32_t)(c * 64 + lane) * 16u, 0, DWPT_STORE_POLICY);
+    } else if (vec) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+#if DWPT_NT_STORES
+            __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4*>(dst) + c * 64 + lane);
+#else
+            reinterpret_cast<u32x4*>(dst)[c * 64 + lane] = v[c];
+#endif
+        }
+    } else {
+        const uint64_t words_in = wave_base < p.n ? (p.n - wave_base) * W : 0;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t wq = (uint32_t)((c * 64 + lane) * 4 + q);
+                if (wq < words_in) dst[wq] = v[c][q];
+            }
+    }
+}
+
 // A scanned tile in blocked order (y, changed in place) back to round order
 // through LDS, stored like apply_store.
 template <class Op, int R, int VEC>
@@ -1267,36 +1307,11 @@ __device__ __forceinline__ void store_blocked_tile(const ScanParams& p, uint64_t
     using E = typename Op::elem_t;
     transpose_chunks<R, VEC, E>(tr, lane, y, false);
     constexpr int K = VecShape<E>::K;
-    if constexpr (K > 1) {  // chunk c goes to chunk c * 64 + lane of the share (see issue_loads)
-        constexpr int C = R * K, W = (int)sizeof(E) / 4;
+    if constexpr (K > 1) {
+        constexpr int C = R * K;
         u32x4 v[C];
         __builtin_memcpy(v, y, 16 * C);
-        uint32_t* __restrict__ dst = static_cast<uint32_t*>(p.out) + wave_base * W;
-        if (vec && BlockedStorePolicy<Op>::value) {
-            const __amdgpu_buffer_rsrc_t rsrc = wave_rsrc(dst);
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-                __builtin_amdgcn_raw_buffer_store_b128(v[c], rsrc, (uint32_t)(c * 64 + lane) * 16u, 0,
-                                                       DWPT_STORE_POLICY);
-        } else if (vec) {
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-#if DWPT_NT_STORES
-                __builtin_nontemporal_store(v[c], reinterpret_cast<u32x4*>(dst) + c * 64 + lane);
-#else
-                reinterpret_cast<u32x4*>(dst)[c * 64 + lane] = v[c];
-#endif
-            }
-        } else {
-            const uint64_t words_in = wave_base < p.n ? (p.n - wave_base) * W : 0;
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t wq = (uint32_t)((c * 64 + lane) * 4 + q);
-                    if (wq < words_in) dst[wq] = v[c][q];
-                }
-        }
+        store_round_chunks<Op, R, VEC>(p, wave_base, vec, lane, v);
         return;
     }
     E* __restrict__ out = static_cast<E*>(p.out);
@@ -1344,10 +1359,41 @@ __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t
         // operators keep two passes: folding the lane twice instead was slower
         // for (maximum, count) (437 -> 481 us at 2^27).
         (void)have_lane_excl;
-        E y[R][VEC];
         const typename Op::prep_t pc =
             Op::prepare(Op::combine_carry(P, Op::to_carry(Op::combine(wave_prefix, lane_excl))));
         V run = ident;
+        constexpr int K = VecShape<E>::K;
+        if constexpr (K > 1) {
+            // elements wider than 16 bytes (3x3 matrices): each round's results go
+            // to the LDS area as they are made, so that only one round of them is
+            // held in registers, then leave in round order
+            constexpr int C = R * K;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                E yr[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const V v = make_value<Op>(e[r][j], (hb[r] >> j) & 1u);
+                    if constexpr (EXCL) yr[j] = elem_of<Op>(Op::apply(pc, run));
+                    run = (r == 0 && j == 0) ? v : Op::combine(run, v);
+                    if constexpr (!EXCL) yr[j] = elem_of<Op>(Op::apply(pc, run));
+                }
+                u32x4 c4[K];
+                __builtin_memcpy(c4, yr, 16 * K);
+#pragma unroll
+                for (int k = 0; k < K; ++k) tr[tr_slot<C>(lane * C + r * K + k)] = c4[k];
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_wave_barrier();
+            u32x4 v[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) v[c] = tr[tr_slot<C>(c * 64 + lane)];
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_wave_barrier();
+            store_round_chunks<Op, R, VEC>(p, wave_base, vec, lane, v);
+            return;
+        }
+        E y[R][VEC];
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -1434,6 +1480,9 @@ constexpr bool counted_lds_waits()
     return !IsSeg<Op>::value && (sizeof(typename Op::value_t) == 4 || sizeof(typename Op::value_t) == 16);
 }
 
+#ifndef DWPT_RELOAD_KEEP
+#define DWPT_RELOAD_KEEP 1
+#endif
 template <class Op> struct ReloadAfterWait { static constexpr bool value = false; };
 template <> struct ReloadAfterWait<OpMat3> { static constexpr bool value = DWPT_RELOAD36; };
 
@@ -1446,7 +1495,7 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
     constexpr int R = G::R, VEC = G::VEC, ND = G::ND;
     E e0[R][VEC], e1[R][VEC];  // the tile to finish (round order, until it is transposed), the next one
     uint32_t h0[R], h1[R];
-    V lx;
+    V lx, lx1;  // lane prefixes from the wavefront scans of the tiles' totals (tile in e0; the second tile)
     WaveTile<G> t0, t1;
     LdsWait lw(p.lb, &s_ids->abort);
     t0.set(p, get_id<counted_lds_waits<Op>()>(lw, s_ids, 0), w);
@@ -1455,7 +1504,7 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
     if (t1.tile < p.num_tiles) issue_loads<Op, R, VEC, false>(p, t1.base, t1.vec, lane, e1, h1);
     if (t1.tile < p.num_tiles)
         hand_over_slot<Op, Slot, ND>(p, t1.tile, 1, w, lane,
-                                     tile_wave_total<Op, R, VEC, true>(t1.base, lane, tr, nullptr, e1, h1, lx),
+                                     tile_wave_total<Op, R, VEC, true>(t1.base, lane, tr, nullptr, e1, h1, lx1),
                                      &s_slot[1]);
     if (t0.tile < p.num_tiles)
         hand_over_slot<Op, Slot, ND>(p, t0.tile, 0, w, lane,
@@ -1482,9 +1531,10 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
         for (int q = 0; q < ND; ++q)
             if (q < w) wave_prefix = Op::combine(wave_prefix, slot->wave_total[q]);
         reload_blocked<R, VEC, E>(tr, lane, e0);
-        scan_store_blocked<Op, EXCL, R, VEC>(p, t0.base, t0.vec, lane, tr, slot->prefix, wave_prefix, e0, h0, lx,
-                                             false);
+        scan_store_blocked<Op, EXCL, R, VEC, DWPT_RELOAD_KEEP>(p, t0.base, t0.vec, lane, tr, slot->prefix,
+                                                               wave_prefix, e0, h0, lx, DWPT_RELOAD_KEEP);
         t0 = t1;
+        lx = lx1;  // the second tile's; every later tile's comes from its own hand-over
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             h0[r] = h1[r];
