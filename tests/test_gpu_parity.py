@@ -60,8 +60,9 @@ class Path:
 
 
 def paths_for(n):
-    # 'auto' picks 'fallback' at these sizes (the persistent kernel starts at
-    # about 1.2e7 elements); the full-size configurations cover 'auto' there
+    # at these sizes 'auto' picks 'single' (at most one tile) or 'fallback' (the
+    # persistent kernel starts at about 1.2e7 elements), both run here forced;
+    # the full-size configurations cover 'auto' above that
     return ["multi", "single", "fallback", "rts"] if n <= 3 * TILE + 17 else ["auto", "multi", "rts"]
 
 

@@ -21,8 +21,8 @@ from parity_helpers import assert_equal, assert_f32_close, from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
-ADD, MAX, AFFINE, MAT3 = 0, 1, 3, 6
-I32, U32, F32, U32X2, U32X9 = 0, 1, 2, 3, 6
+ADD, MAX, AFFINE, MAX_COUNT, MAT2, MAT3 = 0, 1, 3, 4, 5, 6
+I32, U32, F32, U32X2, I32_U32, U32X4, U32X9 = 0, 1, 2, 3, 4, 5, 6
 
 
 def noalloc(x, op, dt, exclusive):
@@ -85,6 +85,15 @@ def test_noalloc_matches_existing_entry_points(path):
             md = to_dev(m)
             y = from_dev(noalloc(md, MAT3, U32X9, True))
             assert_equal(y, from_dev(existing(md, "mat3", True)), "mat3 n=%d" % (n // 64))
+            # the 512-thread classes: (maximum, count) pairs and 2x2 matrices
+            vc = si.maxcount_pairs(950 + seed, n // 4, span=20, unit_counts=False)
+            vd = to_dev(vc)
+            y = from_dev(noalloc(vd, MAX_COUNT, I32_U32, False))
+            assert_equal(y, from_dev(existing(vd, "maxcount", False)), "maxcount n=%d" % (n // 4))
+            m2 = si.mat2_elems(960 + seed, n // 16)
+            m2d = to_dev(m2)
+            y = from_dev(noalloc(m2d, MAT2, U32X4, True))
+            assert_equal(y, from_dev(existing(m2d, "mat2", True)), "mat2 n=%d" % (n // 16))
     assert dw.scan_get_device_error() == 0
 
 
