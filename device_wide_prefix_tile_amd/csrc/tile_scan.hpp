@@ -1717,6 +1717,7 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
     static_assert(64 * VEC < (1 << kCountBits), "packed round counts");
     constexpr int CW = (R + kCountsPerWord - 1) / kCountsPerWord;  // words of packed counts
     constexpr int RUN = G::TILE + 4;  // a tile's run and up to 3 elements of alignment
+    static_assert(RUN * sizeof(T) % 16 == 0, "the second tile buffer starts 16-byte aligned");
 
     __shared__ __align__(16) T s_run[2][RUN];
     __shared__ uint32_t s_packed[2], s_written[2];  // arrivals per buffer, over all its uses
