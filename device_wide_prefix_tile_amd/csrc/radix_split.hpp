@@ -18,7 +18,9 @@
 // Ranking inside a wavefront, one round of 64 keys at a time: every lane
 // sets its bit in an LDS word kept for its digit and reads the word back,
 // which gives the mask of lanes holding the same digit (a round whose keys
-// all share one digit skips this).  A key's rank is the number of those
+// all share one digit skips this).  The bits are set with 32-bit ORs into
+// the word's two halves (a 64-bit OR from every lane moves twice the bytes:
+// 478 -> 470 us for the scatter at 2^28 keys).  A key's rank is the number of those
 // lanes below it plus the wavefront's count of the digit so far, which the
 // lowest lane of the group advances by the group's size with one LDS add.
 //
@@ -26,7 +28,9 @@
 // the same masks with about 40 more vector instructions per round, which
 // made the pass 6% slower; LDS adds from many lanes to one word are slow
 // (all 64 on one word: five times the time of the loads), hence the counter
-// copies of the histogram pass.
+// copies of the histogram pass.  Half-wavefront groups (32-bit masks, two
+// count adds per round, the lower half's first) were slower: 493 against
+// 478 us.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -207,7 +211,7 @@ __device__ __forceinline__ void scatter_tile(RsShared& sh, const uint32_t (&k)[k
     // which the other lanes of the group fetch from it.  The adds of
     // successive rounds need not wait for each other.
     uint32_t rank[kRsItems];
-    const uint64_t my_bit = 1ull << lane;
+    const uint32_t my_bit = 1u << (lane & 31);
 #pragma unroll
     for (int v = 0; v < kRsItems; ++v) {
         const bool valid = FULL || base + (uint64_t)v * 64 + lane < n;
@@ -221,7 +225,8 @@ __device__ __forceinline__ void scatter_tile(RsShared& sh, const uint32_t (&k)[k
         uint64_t m = vm;
         if (wave_ballot(valid && d == d0) != vm) {
             uint64_t* slot = &sh.grp[w][d];
-            if (valid) atomicOr(slot, my_bit);
+            // lanes 0-31 set bits of the low half, lanes 32-63 of the high half
+            if (valid) atomicOr(reinterpret_cast<uint32_t*>(slot) + (lane >> 5), my_bit);
             m = valid ? *slot : 0ull;
             if (valid && lanes_below(m) == 0) *slot = 0ull;
         }
@@ -301,8 +306,14 @@ __device__ __forceinline__ void scatter_tile(RsShared& sh, const uint32_t (&k)[k
 
 // Pass 3: `offs` is the exclusive scan of pass 1's hist.  Writes the tile's
 // keys (and values) to their places in keys_out (vals_out).
+//
+// Registers: the workgroup's LDS (51 KiB) leaves room for three workgroups
+// per CU, which at 512 threads need six wavefronts per SIMD, i.e. at most 80
+// VGPRs.  The keys-only kernel is held to that (82 -> 80 VGPRs, no spills;
+// 2^28 keys 522 -> 478 us); with values it would spill (100 bytes per lane:
+// 440 -> 889 us at 2^27 pairs), so that one keeps two workgroups per CU.
 template <bool VALS>
-__global__ __launch_bounds__(kRsBlock) void radix_scatter_kernel(const uint32_t* __restrict__ keys,
+__global__ __launch_bounds__(kRsBlock) __attribute__((amdgpu_waves_per_eu(VALS ? 1 : 6))) void radix_scatter_kernel(const uint32_t* __restrict__ keys,
                                                                  const uint32_t* __restrict__ vals, uint64_t n,
                                                                  uint32_t shift, uint32_t T,
                                                                  const uint32_t* __restrict__ offs,
