@@ -6,14 +6,19 @@
 // §9.6: the scan of the digit histogram gives each bucket's start).
 //
 // Three launches on the caller's stream:
-//   1. radix_hist_kernel: tile t's count of every digit d, stored digit-major
-//      at hist[d * T + t] (T tiles);
-//   2. the library's exclusive add scan of hist, in place: hist[d * T + t]
-//      becomes the output position of tile t's first key of digit d (all
-//      smaller digits come first, then the same digit in earlier tiles);
+//   1. radix_hist_kernel: counts every digit d in every tile t (T tiles, in
+//      groups of kHistTiles consecutive tiles) and stores, digit-major, the
+//      count of d in the earlier tiles of t's group at local[d * T + t] and
+//      the group's count of d at group[d * G + g] (G groups);
+//   2. the library's exclusive add scan of group, in place: group[d * G + g]
+//      becomes the output position of group g's first key of digit d (all
+//      smaller digits come first, then the same digit in earlier groups);
 //   3. radix_scatter_kernel: every key's rank among the keys of its digit in
 //      its tile, the tile reordered by digit in LDS, and each digit's run
-//      written to its position.
+//      written to its position, group[d * G + g] + local[d * T + t] onward.
+// Only the group totals are scanned: 256 words per kHistTiles tiles instead
+// of 256 per tile (2^28 keys: a scan of 2^20 words instead of 2^23, which
+// took 22 us of the pass).
 //
 // Ranking inside a wavefront, one round of 64 keys at a time: every lane
 // sets its bit in an LDS word kept for its digit and reads the word back,
@@ -107,10 +112,12 @@ __device__ __forceinline__ void load_tile(const uint32_t* __restrict__ src, uint
 // nothing visible), and with 16 copies at most 4 lanes ever share a word.
 constexpr int kRsCopies = 16;
 
-// Pass 1: hist[d * T + t] = number of keys of digit d in tile t.  Each
-// workgroup counts kHistTiles consecutive tiles in turn, loading the next
-// tile's keys while it counts the current one, and writes its counts at the
-// end (kHistTiles consecutive words per digit); measured at 2^28 keys: 225 us
+// Pass 1: local[d * T + t] = number of keys of digit d in the tiles of t's
+// group before t, group[d * G + g] = number of keys of digit d in group g.
+// Each workgroup counts the kHistTiles consecutive tiles of one group in
+// turn, loading the next tile's keys while it counts the current one, and
+// writes its counts at the end (kHistTiles consecutive words per digit);
+// measured at 2^28 keys, when every tile's count was stored: 225 us
 // with one tile per workgroup, 193 with 4 or 8 tiles (16: 200).  The counter
 // copies lie copy-major (copy c of digit d at c * 256 + d), so that the
 // thread that folds a digit's copies reads them from distinct banks.  Groups
@@ -120,8 +127,8 @@ constexpr int kRsCopies = 16;
 constexpr int kHistTiles = 8;
 
 __global__ __launch_bounds__(kRsBlock) void radix_hist_kernel(const uint32_t* __restrict__ keys, uint64_t n,
-                                                              uint32_t shift, uint32_t T, uint32_t* __restrict__ hist,
-                                                              int vec)
+                                                              uint32_t shift, uint32_t T, uint32_t* __restrict__ local,
+                                                              uint32_t* __restrict__ group, int vec)
 {
     __shared__ uint32_t s_cnt[kRsCopies * kRsDigits];
     __shared__ uint32_t s_out[kRsDigits][kHistTiles + 1];
@@ -129,7 +136,8 @@ __global__ __launch_bounds__(kRsBlock) void radix_hist_kernel(const uint32_t* __
     const int w = threadIdx.x >> 6;
     const uint32_t G = (T + kHistTiles - 1) / kHistTiles;
     if (blockIdx.x >= G) return;  // a grid of G workgroups is expected; never index past the tiles
-    const uint32_t t0 = rs_tile(blockIdx.x, G) * kHistTiles;
+    const uint32_t g = rs_tile(blockIdx.x, G);
+    const uint32_t t0 = g * kHistTiles;
     const uint32_t t1 = t0 + kHistTiles < T ? t0 + kHistTiles : T;
     for (int i = threadIdx.x; i < kRsDigits * kRsCopies; i += kRsBlock) s_cnt[i] = 0u;
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -153,6 +161,7 @@ __global__ __launch_bounds__(kRsBlock) void radix_hist_kernel(const uint32_t* __
     load(t0, k);
     __syncthreads();  // counters clear
     uint32_t* my = s_cnt + (lane % kRsCopies) * kRsDigits;
+    uint32_t run = 0;  // thread d < 256: keys of digit d in the group's tiles so far
     for (uint32_t t = t0; t < t1; ++t) {
         if (t + 1 < t1) load(t + 1, k2);
         const uint64_t base = (uint64_t)t * kRsTile + (uint64_t)w * kRsWaveKeys;
@@ -169,16 +178,18 @@ __global__ __launch_bounds__(kRsBlock) void radix_hist_kernel(const uint32_t* __
                 c += s_cnt[i * kRsDigits + threadIdx.x];
                 s_cnt[i * kRsDigits + threadIdx.x] = 0u;
             }
-            s_out[threadIdx.x][t - t0] = c;
+            s_out[threadIdx.x][t - t0] = run;
+            run += c;
         }
         __syncthreads();  // counters clear again
 #pragma unroll
         for (int v = 0; v < kRsItems; ++v) k[v] = k2[v];
     }
+    if (threadIdx.x < kRsDigits) group[(uint64_t)threadIdx.x * G + g] = run;
     const uint32_t nt = t1 - t0;
     for (uint32_t i = threadIdx.x; i < kRsDigits * kHistTiles; i += kRsBlock) {
         const uint32_t d = i / kHistTiles, q = i % kHistTiles;
-        if (q < nt) hist[(uint64_t)d * T + t0 + q] = s_out[d][q];
+        if (q < nt) local[(uint64_t)d * T + t0 + q] = s_out[d][q];
     }
 }
 
@@ -304,8 +315,9 @@ __device__ __forceinline__ void scatter_tile(RsShared& sh, const uint32_t (&k)[k
     }
 }
 
-// Pass 3: `offs` is the exclusive scan of pass 1's hist.  Writes the tile's
-// keys (and values) to their places in keys_out (vals_out).
+// Pass 3: `local` as pass 1 left it, `group` its group counts after the
+// exclusive scan.  Writes the tile's keys (and values) to their places in
+// keys_out (vals_out).
 //
 // Registers: the workgroup's LDS (51 KiB) leaves room for three workgroups
 // per CU, which at 512 threads need six wavefronts per SIMD, i.e. at most 80
@@ -316,7 +328,8 @@ template <bool VALS>
 __global__ __launch_bounds__(kRsBlock) __attribute__((amdgpu_waves_per_eu(VALS ? 1 : 6))) void radix_scatter_kernel(const uint32_t* __restrict__ keys,
                                                                  const uint32_t* __restrict__ vals, uint64_t n,
                                                                  uint32_t shift, uint32_t T,
-                                                                 const uint32_t* __restrict__ offs,
+                                                                 const uint32_t* __restrict__ local,
+                                                                 const uint32_t* __restrict__ group,
                                                                  uint32_t* __restrict__ keys_out,
                                                                  uint32_t* __restrict__ vals_out)
 {
@@ -327,7 +340,10 @@ __global__ __launch_bounds__(kRsBlock) __attribute__((amdgpu_waves_per_eu(VALS ?
     uint32_t k[kRsItems], x[kRsItems];
     load_tile(keys, t, n, w, lane, k);
     if (VALS) load_tile(vals, t, n, w, lane, x);
-    const uint32_t g = threadIdx.x < kRsDigits ? offs[(uint64_t)threadIdx.x * T + t] : 0u;
+    const uint32_t G = (T + kHistTiles - 1) / kHistTiles;
+    const uint32_t g = threadIdx.x < kRsDigits
+                           ? group[(uint64_t)threadIdx.x * G + t / kHistTiles] + local[(uint64_t)threadIdx.x * T + t]
+                           : 0u;
     for (int i = threadIdx.x; i < kRsWaves * kRsDigits; i += kRsBlock) {
         (&sh.cnt[0][0])[i] = 0u;
         (&sh.grp[0][0])[i] = 0ull;

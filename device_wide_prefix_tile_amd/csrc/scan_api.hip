@@ -681,29 +681,35 @@ scan_status_t radix_split(const uint32_t* keys, const uint32_t* vals, size_t n, 
             return SCAN_ERR_INVALID;
         const hipStream_t s = static_cast<hipStream_t>(stream);
         const uint32_t T = (uint32_t)((n + kRsTile - 1) / kRsTile);
-        const size_t nh = (size_t)kRsDigits * T;
+        const uint32_t G = (T + kHistTiles - 1) / kHistTiles;
+        // per (digit, tile): count in the earlier tiles of the tile's group;
+        // then per (digit, group): the group's count
+        const size_t nl = (size_t)kRsDigits * T, ng = (size_t)kRsDigits * G;
         void* hist = nullptr;
         {
             std::lock_guard<std::mutex> lock(g_mu);
-            const scan_status_t st = acquire_hist(s, nh * 4, &hist);
+            const scan_status_t st = acquire_hist(s, (nl + ng) * 4, &hist);
             if (st != SCAN_OK) return st;
         }
-        uint32_t* h = static_cast<uint32_t*>(hist);
-        hipLaunchKernelGGL(radix_hist_kernel, dim3((T + kHistTiles - 1) / kHistTiles), dim3(kRsBlock), 0,
-                           s, keys, (uint64_t)n, shift, T, h, is_aligned(keys, 16) ? 1 : 0);
+        uint32_t* local = static_cast<uint32_t*>(hist);
+        uint32_t* group = local + nl;
+        hipLaunchKernelGGL(radix_hist_kernel, dim3(G), dim3(kRsBlock), 0,
+                           s, keys, (uint64_t)n, shift, T, local, group, is_aligned(keys, 16) ? 1 : 0);
         if (hipGetLastError() != hipSuccess) return SCAN_ERR_HIP;
-        // each (digit, tile) count -> the output position of its first key
-        const Call c{h, h, nullptr, nullptr, nh, s};
+        // each (digit, group) count -> the output position of the group's first key of the digit
+        const Call c{group, group, nullptr, nullptr, ng, s};
         const scan_status_t st = run_scan<OpAdd<uint32_t>, true>(c, true);
         if (st != SCAN_OK) return st;
         if (vals)
             hipLaunchKernelGGL(radix_scatter_kernel<true>,
                                dim3(T), dim3(kRsBlock), 0, s,
-                               keys, vals, (uint64_t)n, shift, T, (const uint32_t*)h, keys_out, vals_out);
+                               keys, vals, (uint64_t)n, shift, T, (const uint32_t*)local, (const uint32_t*)group,
+                               keys_out, vals_out);
         else
             hipLaunchKernelGGL(radix_scatter_kernel<false>,
                                dim3(T), dim3(kRsBlock), 0, s,
-                               keys, vals, (uint64_t)n, shift, T, (const uint32_t*)h, keys_out, vals_out);
+                               keys, vals, (uint64_t)n, shift, T, (const uint32_t*)local, (const uint32_t*)group,
+                               keys_out, vals_out);
         return hipGetLastError() == hipSuccess ? SCAN_OK : SCAN_ERR_HIP;
     } catch (const std::bad_alloc&) {
         return SCAN_ERR_NOMEM;

@@ -191,8 +191,9 @@ scan_status_t csr_row_offsets(const uint32_t* row_idx, size_t nnz, uint32_t n_ro
  * keys, keys_out (and vals, vals_out) are device arrays of n uint32 aligned
  * to 4 bytes; vals and vals_out are both NULL or both non-NULL.  No output
  * may overlap an input or the other output (the split is out of place).
- * shift <= 31; n < 2^32.  n == 0 does nothing.  The digit histogram (256
- * uint32 per 8192 keys) lives in the library's per-stream workspace.
+ * shift <= 31; n < 2^32.  n == 0 does nothing.  The digit histograms (256
+ * uint32 per 8192 keys, and 256 per 65536 keys) live in the library's
+ * per-stream workspace.
  */
 scan_status_t radix_split(const uint32_t* keys, const uint32_t* vals, size_t n, uint32_t shift,
                           uint32_t* keys_out, uint32_t* vals_out, void* stream);
