@@ -105,91 +105,101 @@ __device__ __forceinline__ void load_tile(const uint32_t* __restrict__ src, uint
         load_keys<false>(src, base, n, lane, k);
 }
 
-// Histogram counters: one set per workgroup with kRsCopies copies of each
-// digit's counter; lane l adds to copy l % kRsCopies.  LDS adds
-// to one word from many lanes of an instruction are slow (measured: 64 lanes
-// on one word cost about five times the loads; up to four per word cost
-// nothing visible), and with 16 copies at most 4 lanes ever share a word.
-constexpr int kRsCopies = 16;
+// Histogram counters: every wavefront has its own, kRsCopies copies of each
+// digit's counter; lane l adds to copy l % kRsCopies.  LDS adds to one word
+// from many lanes of an instruction are slow (measured: 64 lanes on one word
+// cost about five times the loads; up to four per word cost nothing
+// visible); with 4 copies, all keys of one digit put 16 lanes on a word.  (On
+// uniform digits the number of copies made no difference: 1, 2 and 4 copies
+// 182.8, 182.8, 182.9 us at 2^28 keys.)
+constexpr int kRsCopies = 4;
+constexpr int kRsCntRow = kRsCopies * kRsDigits + 1;  // one wavefront's counters (+1: rows start in distinct banks)
 
 // Pass 1: local[d * T + t] = number of keys of digit d in the tiles of t's
 // group before t, group[d * G + g] = number of keys of digit d in group g.
-// Each workgroup counts the kHistTiles consecutive tiles of one group in
-// turn, loading the next tile's keys while it counts the current one, and
-// writes its counts at the end (kHistTiles consecutive words per digit);
-// measured at 2^28 keys, when every tile's count was stored: 225 us
-// with one tile per workgroup, 193 with 4 or 8 tiles (16: 200).  The counter
-// copies lie copy-major (copy c of digit d at c * 256 + d), so that the
-// thread that folds a digit's copies reads them from distinct banks.  Groups
-// are dealt to the XCDs as tiles are by rs_tile.  (Counting does not depend
-// on the keys' order, so a tile is read with one 16-byte load per lane and
-// four keys, when the keys are 16-byte aligned.)
-constexpr int kHistTiles = 8;
+// A group is kHistTiles consecutive tiles, one per wavefront of a workgroup:
+// each wavefront reads its whole tile (16-byte loads, four keys each, the
+// next four loads in flight while it counts; counting does not depend on the
+// keys' order) and counts it into its own counters, so the only barrier comes
+// at the end, where the group's counts are turned into prefixes and written,
+// kHistTiles consecutive words per digit.  Measured at 2^28 keys: 182-183 us;
+// a workgroup that counted its tiles one after another, every wavefront an
+// eighth of each, with two barriers per tile, 193 us (one tile per workgroup:
+// 225; two tiles per wavefront 197, four 241: they spill).  Groups are dealt
+// to the XCDs as tiles are by rs_tile (dealt in order: 202 us).
+constexpr int kHistTiles = kRsWaves;
 
 __global__ __launch_bounds__(kRsBlock) void radix_hist_kernel(const uint32_t* __restrict__ keys, uint64_t n,
                                                               uint32_t shift, uint32_t T, uint32_t* __restrict__ local,
                                                               uint32_t* __restrict__ group, int vec)
 {
-    __shared__ uint32_t s_cnt[kRsCopies * kRsDigits];
-    __shared__ uint32_t s_out[kRsDigits][kHistTiles + 1];
+    __shared__ uint32_t s_cnt[kRsWaves][kRsCntRow];
     const int lane = lane_id();
     const int w = threadIdx.x >> 6;
     const uint32_t G = (T + kHistTiles - 1) / kHistTiles;
     if (blockIdx.x >= G) return;  // a grid of G workgroups is expected; never index past the tiles
     const uint32_t g = rs_tile(blockIdx.x, G);
-    const uint32_t t0 = g * kHistTiles;
-    const uint32_t t1 = t0 + kHistTiles < T ? t0 + kHistTiles : T;
-    for (int i = threadIdx.x; i < kRsDigits * kRsCopies; i += kRsBlock) s_cnt[i] = 0u;
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    const auto load = [&](uint32_t t, uint32_t (&k)[kRsItems]) {
+    const uint32_t t = g * kHistTiles + w;  // this wavefront's tile
+    uint32_t* cnt = s_cnt[w];
+    for (int i = lane; i < kRsCntRow; i += 64) cnt[i] = 0u;
+    uint32_t* my = cnt + (lane % kRsCopies) * kRsDigits;
+    if (t < T) {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
         if (vec && (uint64_t)(t + 1) * kRsTile <= n) {
-            const u32x4_t* src =
-                reinterpret_cast<const u32x4_t*>(keys + (uint64_t)t * kRsTile + (uint64_t)w * kRsWaveKeys);
+            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(keys + (uint64_t)t * kRsTile) + lane;
+            constexpr int B = 4, NB = kRsTile / 4 / 64 / B;  // loads per batch, batches
+            u32x4_t q[B], q2[B];
 #pragma unroll
-            for (int v = 0; v < kRsItems / 4; ++v) {
-                const u32x4_t q = __builtin_nontemporal_load(src + v * 64 + lane);
-                k[4 * v] = q.x;
-                k[4 * v + 1] = q.y;
-                k[4 * v + 2] = q.z;
-                k[4 * v + 3] = q.w;
+            for (int j = 0; j < B; ++j) q[j] = __builtin_nontemporal_load(src + j * 64);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (b + 1 < NB) {
+#pragma unroll
+                    for (int j = 0; j < B; ++j) q2[j] = __builtin_nontemporal_load(src + ((b + 1) * B + j) * 64);
+                }
+#pragma unroll
+                for (int j = 0; j < B; ++j) {
+                    atomicAdd(my + ((q[j].x >> shift) & 255u), 1u);
+                    atomicAdd(my + ((q[j].y >> shift) & 255u), 1u);
+                    atomicAdd(my + ((q[j].z >> shift) & 255u), 1u);
+                    atomicAdd(my + ((q[j].w >> shift) & 255u), 1u);
+                }
+#pragma unroll
+                for (int j = 0; j < B; ++j) q[j] = q2[j];
             }
-        } else {
-            load_tile(keys, t, n, w, lane, k);
+        } else {  // the partial last tile, or keys not 16-byte aligned: one key per lane and step
+            const uint64_t base = (uint64_t)t * kRsTile;
+            for (uint32_t i = lane; i < (uint32_t)kRsTile && base + i < n; i += 64)
+                atomicAdd(my + ((keys[base + i] >> shift) & 255u), 1u);
         }
-    };
-    uint32_t k[kRsItems], k2[kRsItems];
-    load(t0, k);
-    __syncthreads();  // counters clear
-    uint32_t* my = s_cnt + (lane % kRsCopies) * kRsDigits;
-    uint32_t run = 0;  // thread d < 256: keys of digit d in the group's tiles so far
-    for (uint32_t t = t0; t < t1; ++t) {
-        if (t + 1 < t1) load(t + 1, k2);
-        const uint64_t base = (uint64_t)t * kRsTile + (uint64_t)w * kRsWaveKeys;
-        const bool full = (uint64_t)(t + 1) * kRsTile <= n;
-        // a partial tile is loaded one key per lane and round (load_tile)
+    }
+    // fold the copies into copy 0 (a wavefront's LDS operations take effect
+    // in order, so its adds are all in)
 #pragma unroll
-        for (int v = 0; v < kRsItems; ++v)
-            if (full || base + (uint64_t)v * 64 + lane < n) atomicAdd(my + ((k[v] >> shift) & 255u), 1u);
-        __syncthreads();
-        if (threadIdx.x < kRsDigits) {
-            uint32_t c = 0;
+    for (int k = 0; k < kRsDigits / 64; ++k) {
+        const int d = lane + 64 * k;
+        uint32_t c = 0;
 #pragma unroll
-            for (int i = 0; i < kRsCopies; ++i) {
-                c += s_cnt[i * kRsDigits + threadIdx.x];
-                s_cnt[i * kRsDigits + threadIdx.x] = 0u;
-            }
-            s_out[threadIdx.x][t - t0] = run;
+        for (int i = 0; i < kRsCopies; ++i) c += cnt[i * kRsDigits + d];
+        cnt[d] = c;
+    }
+    __syncthreads();
+    // thread d: the counts of the group's tiles become prefixes in place
+    if (threadIdx.x < kRsDigits) {
+        const int d = threadIdx.x;
+        uint32_t run = 0;
+#pragma unroll
+        for (int q = 0; q < kHistTiles; ++q) {
+            const uint32_t c = s_cnt[q][d];
+            s_cnt[q][d] = run;
             run += c;
         }
-        __syncthreads();  // counters clear again
-#pragma unroll
-        for (int v = 0; v < kRsItems; ++v) k[v] = k2[v];
+        group[(uint64_t)d * G + g] = run;
     }
-    if (threadIdx.x < kRsDigits) group[(uint64_t)threadIdx.x * G + g] = run;
-    const uint32_t nt = t1 - t0;
+    __syncthreads();
     for (uint32_t i = threadIdx.x; i < kRsDigits * kHistTiles; i += kRsBlock) {
         const uint32_t d = i / kHistTiles, q = i % kHistTiles;
-        if (q < nt) local[(uint64_t)d * T + t0 + q] = s_out[d][q];
+        if (g * kHistTiles + q < T) local[(uint64_t)d * T + g * kHistTiles + q] = s_cnt[q][d];
     }
 }
 
