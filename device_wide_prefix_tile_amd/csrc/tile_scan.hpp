@@ -684,6 +684,7 @@ template <> struct ResolveSpan<OpMat2> { static constexpr int value = 4; };
 #endif
 template <> struct ResolveSpan<OpMat3> { static constexpr int value = DWPT_RESOLVE_SPAN36; };
 
+
 template <class V, class C, int ND>
 struct PipeSlot {
     uint32_t arrived;     // data-wavefront arrivals, counted over all uses of the slot
@@ -1044,6 +1045,44 @@ __device__ __forceinline__ bool take_first_batch(const ScanParams& p, TileIdRing
     return (uint64_t)b + NT >= p.num_tiles;
 }
 
+// The first NT numbers in consecutive pieces: NA numbers, then pieces of NB,
+// each taken once the one before has come back (by then the other
+// workgroups' pieces of the same rank are mostly out), every tile's loads
+// going out as soon as its number is known.  With one batch, the prefix chain
+// cannot pass a workgroup before all NT of its tiles are in, i.e. before
+// nearly the whole first batch of the chip (61 MB for the plain scans) is
+// read, and no tile is stored meanwhile; with a first piece of one tile it
+// passes every workgroup's first tile once those are in.  Every lower number
+// is still held by a running workgroup.  Measured (timing harness, µs):
+// float32 / int32 add at 2^28, pieces (1, 3) 332.1 / 331.5 against one batch
+// 335.5 / 334.5, (2, 2) 332.8 / 332.4, (1, 2, 1) 334.0 / 333.2, (2, 1, 1)
+// 334.8 / 334.4, (1, 1, 1, 1) 336.0 / 335.2; affine 2^27 347 -> 341, 2x2
+// matrices 2^26 474 -> 462; slower for (maximum, count) 2^27 437 -> 464 and
+// segmented add 2^27 214 -> 216.5, which keep one batch.
+template <int NT, int NA, int NB>
+__device__ __forceinline__ bool take_first_pieces(const ScanParams& p, TileIdRing* ids)
+{
+    bool ex = false;
+#pragma unroll
+    for (int q = 0; q < NT;) {
+        const int m = (q == 0 ? NA : NB) < NT - q ? (q == 0 ? NA : NB) : NT - q;
+        uint32_t b = p.num_tiles;
+        if (!ex) {
+            if (lane_id() == 0)
+                b = __hip_atomic_fetch_add(pipe_counter(p, kCtrTiles), (uint32_t)m, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+            b = (uint32_t)__builtin_amdgcn_readfirstlane((int)b);
+        }
+        if (lane_id() == 0)
+#pragma unroll
+            for (int j = 0; j < m; ++j)
+                put_id(ids, (uint32_t)(q + j), !ex && (uint64_t)b + j < p.num_tiles ? b + j : p.num_tiles);
+        ex = ex || (uint64_t)b + m >= p.num_tiles;
+        q += m;
+    }
+    return ex;
+}
+
 // Wavefront 0 asks for a tile number one iteration before it is needed: the
 // request goes out at the top of the iteration (lane 0) and its result is
 // used only at the end, so the counter's round trip overlaps the iteration.
@@ -1127,6 +1166,12 @@ template <class B> struct UseBlocked<OpSeg<B>> { static constexpr bool value = t
 #endif
 #endif
 template <> struct UseBlocked<OpMat3> { static constexpr bool value = true; };  // always (wide elements)
+
+// Operators whose persistent kernel takes its first tile numbers in pieces
+// (take_first_pieces): the round-order scans, affine maps and 2x2 matrices.
+template <class Op> struct FirstPieces { static constexpr bool value = !UseBlocked<Op>::value; };
+template <> struct FirstPieces<OpAffine> { static constexpr bool value = true; };
+template <> struct FirstPieces<OpMat2> { static constexpr bool value = true; };
 
 // LDS chunk slot of chunk c: one chunk of padding after every R, which keeps
 // both orders of access free of bank conflicts.
@@ -1581,7 +1626,13 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
         return;
     }
     bool exhausted = false;
-    if (w == 0) exhausted = take_first_batch<kPipeTiles>(p, &s_ids);
+    constexpr bool PIECES = FirstPieces<Op>::value && !ReloadAfterWait<Op>::value;
+    if (w == 0) {
+        if constexpr (PIECES)
+            exhausted = take_first_pieces<kPipeTiles, 1, 3>(p, &s_ids);
+        else
+            exhausted = take_first_batch<kPipeTiles>(p, &s_ids);
+    }
     if (w == ND) {
         fetch_prefixes<Op>(p, &s_ids, s_slot);
         return;
@@ -1610,12 +1661,21 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     V lx[kPipeTiles];
     WaveTile<G> t[kPipeTiles];
     LdsWait lw(p.lb, &s_ids.abort);
-#pragma unroll
-    for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id<counted_lds_waits<Op>()>(lw, &s_ids, q), w);
     // the first batch: every tile loaded and its total published up front
+    if constexpr (PIECES) {
+        // each tile's loads go out as soon as its number is known
 #pragma unroll
-    for (int q = 0; q < kPipeTiles; ++q)
-        if (t[q].tile < p.num_tiles) issue_loads<Op, R, VEC, LANE_VEC>(p, t[q].base, t[q].vec, lane, e[q], h[q]);
+        for (int q = 0; q < kPipeTiles; ++q) {
+            t[q].set(p, get_id<counted_lds_waits<Op>()>(lw, &s_ids, q), w);
+            if (t[q].tile < p.num_tiles) issue_loads<Op, R, VEC, LANE_VEC>(p, t[q].base, t[q].vec, lane, e[q], h[q]);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < kPipeTiles; ++q) t[q].set(p, get_id<counted_lds_waits<Op>()>(lw, &s_ids, q), w);
+#pragma unroll
+        for (int q = 0; q < kPipeTiles; ++q)
+            if (t[q].tile < p.num_tiles) issue_loads<Op, R, VEC, LANE_VEC>(p, t[q].base, t[q].vec, lane, e[q], h[q]);
+    }
 #pragma unroll
     for (int q = 0; q < kPipeTiles; ++q)
         if (t[q].tile < p.num_tiles)

@@ -10,7 +10,8 @@
 // Modelled, as in the kernel:
 //  * roles from a counter (role 0 resolves), tile numbers from a counter: a
 //    first batch of WAIT + 1 consecutive numbers per workgroup with one
-//    atomic, later numbers one iteration ahead (ask_id / post_id);
+//    atomic, or in consecutive pieces one round trip apart, later numbers
+//    one iteration ahead (ask_id / post_id);
 //  * per workgroup: ND data waves with WAIT + 1 tiles in flight, a prefix
 //    wave, LDS rings of S slots with sequence numbers (tile-number ring,
 //    prefix/arrival ring), the last data wave to hand a tile's total over
@@ -50,6 +51,8 @@ struct Params {
     int wait = 3;          // tiles per data wave waiting for their prefix
     int slots = 16;        // LDS ring slots (the kernel: 16 >= 2 * wait)
     int span = 1;          // resolver window: 64 * span tiles
+    int first_piece = 0;   // first tile numbers: one batch (0), or a piece of this many, then pieces of next_piece
+    int next_piece = 3;
     int wgs = 5;           // workgroups launched (one becomes the resolver)
     int tiles = 300;       // tiles per launch
     int share = 3;         // elements per data wave and tile
@@ -371,11 +374,27 @@ void data_wave(Launch& Lc, Lds& L, int w, uint32_t grid, Noise& nz)
     const uint32_t TE = tile_elems(P);
     LdsWait lw{P.spin * 16, &L.abort};
     bool exhausted = false;
-    if (w == 0) {
+    if (w == 0 && P.first_piece <= 0) {
         const uint32_t b = m.tile_ctr.fetch_add((uint32_t)NT, std::memory_order_relaxed);
         for (int q = 0; q < NT; ++q)
             put_id(L, P, (uint32_t)q, (uint64_t)b + q < Lc.num_tiles ? b + q : Lc.num_tiles);
         exhausted = (uint64_t)b + NT >= Lc.num_tiles;
+    } else if (w == 0) {
+        // the first numbers in consecutive pieces, each taken once the one
+        // before has come back (take_first_pieces)
+        bool ex = false;
+        for (int q = 0; q < NT;) {
+            const int want = q == 0 ? P.first_piece : P.next_piece;
+            const int mq = want < NT - q ? want : NT - q;
+            uint32_t b = Lc.num_tiles;
+            if (!ex) b = m.tile_ctr.fetch_add((uint32_t)mq, std::memory_order_relaxed);
+            for (int j = 0; j < mq; ++j)
+                put_id(L, P, (uint32_t)(q + j), !ex && (uint64_t)b + j < Lc.num_tiles ? b + j : Lc.num_tiles);
+            ex = ex || (uint64_t)b + mq >= Lc.num_tiles;
+            q += mq;
+            nz.step();
+        }
+        exhausted = ex;
     }
     auto load = [&](WaveTile& t) {
         t.e.assign(P.share, identity(P.op));
@@ -664,6 +683,8 @@ int main(int argc, char** argv)
         else if (k == "wait") P.wait = (int)v;
         else if (k == "slots") P.slots = (int)v;
         else if (k == "span") P.span = (int)v;
+        else if (k == "first_piece") P.first_piece = (int)v;
+        else if (k == "next_piece") P.next_piece = (int)v;
         else if (k == "wgs") P.wgs = (int)v;
         else if (k == "tiles") P.tiles = (int)v;
         else if (k == "share") P.share = (int)v;
@@ -679,7 +700,7 @@ int main(int argc, char** argv)
         else if (k == "resident") P.resident = (int)v;
         else if (k == "seed") P.seed = (unsigned)v;
     }
-    if (P.nd < 1 || P.wait < 1 || P.slots < 1 || P.wgs < 2 || P.tiles < 1 || P.share < 1 || P.span < 1) {
+    if (P.nd < 1 || P.wait < 1 || P.slots < 1 || P.wgs < 2 || P.tiles < 1 || P.share < 1 || P.span < 1 || P.next_piece < 1) {
         fprintf(stderr, "bad parameters\n");
         return 2;
     }

@@ -53,9 +53,11 @@ SHIPPED = [(3, 3, 1, 1), (3, 3, 1, 0), (5, 2, 2, 1), (3, 4, 1, 0), (2, 3, 4, 1),
 
 @pytest.mark.parametrize("nd,wait,span,op", SHIPPED)
 def test_persistent_pipeline_random_schedules(model, nd, wait, span, op):
-    for seed in (1, 2, 3):
+    # first tile numbers as one batch, and (the plain scans, affine maps, 2x2
+    # matrices) as a piece of one, then pieces of three
+    for seed, first in ((1, 1), (2, 0), (3, 1)):
         rc, f, err = run(model["plain"], nd=nd, wait=wait, span=span, op=op, seed=seed, tiles=300, wgs=5,
-                         launches=3)
+                         launches=3, first_piece=first)
         assert rc == 0 and f["ok"] == "1", (f, err[-1000:])
         assert f["mismatches"] == "0" and f["err"] == "0"
 
@@ -130,7 +132,8 @@ def test_thread_sanitizer_finds_no_race(model):
     if model["tsan"] is None:
         pytest.skip("ThreadSanitizer build not available")
     for kw in (dict(nd=3, wait=3, span=1, op=1, seed=1), dict(nd=2, wait=1, span=2, op=0, seed=2),
-               dict(nd=4, wait=4, span=4, op=1, seed=3, wgs=6), dict(kernel=1, op=1, seed=4)):
+               dict(nd=4, wait=4, span=4, op=1, seed=3, wgs=6), dict(kernel=1, op=1, seed=4),
+               dict(nd=3, wait=3, span=1, op=0, seed=5, first_piece=1)):
         rc, f, err = run(model["tsan"], tiles=150, launches=2, timeout=300, **kw)
         assert "ThreadSanitizer" not in err, (kw, err[-3000:])
         assert rc == 0 and f["ok"] == "1", (kw, f)
