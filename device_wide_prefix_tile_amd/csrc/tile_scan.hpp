@@ -1056,9 +1056,9 @@ __device__ __forceinline__ bool take_first_batch(const ScanParams& p, TileIdRing
 // is still held by a running workgroup.  Measured (timing harness, µs):
 // float32 / int32 add at 2^28, pieces (1, 3) 332.1 / 331.5 against one batch
 // 335.5 / 334.5, (2, 2) 332.8 / 332.4, (1, 2, 1) 334.0 / 333.2, (2, 1, 1)
-// 334.8 / 334.4, (1, 1, 1, 1) 336.0 / 335.2; affine 2^27 347 -> 341, 2x2
-// matrices 2^26 474 -> 462; slower for (maximum, count) 2^27 437 -> 464 and
-// segmented add 2^27 214 -> 216.5, which keep one batch.
+// 334.8 / 334.4, (1, 1, 1, 1) 336.0 / 335.2.  In the library, same box:
+// float32 add 2^28 335.3 -> 331.5, affine 2^26 184.1 -> 178.5, 2x2 matrices
+// 2^25 219.7 -> 216.9 (which operators take pieces: FirstPieces).
 template <int NT, int NA, int NB>
 __device__ __forceinline__ bool take_first_pieces(const ScanParams& p, TileIdRing* ids)
 {
@@ -1167,11 +1167,13 @@ template <class B> struct UseBlocked<OpSeg<B>> { static constexpr bool value = t
 #endif
 template <> struct UseBlocked<OpMat3> { static constexpr bool value = true; };  // always (wide elements)
 
-// Operators whose persistent kernel takes its first tile numbers in pieces
-// (take_first_pieces): the round-order scans, affine maps and 2x2 matrices.
-template <class Op> struct FirstPieces { static constexpr bool value = !UseBlocked<Op>::value; };
-template <> struct FirstPieces<OpAffine> { static constexpr bool value = true; };
-template <> struct FirstPieces<OpMat2> { static constexpr bool value = true; };
+// How the persistent kernel takes its first tile numbers: in pieces of
+// `first`, then `next` (take_first_pieces), or, with first == 0, as one
+// batch.  Segmented scans keep one batch (pieces of 1 then 2, or 2 then 1:
+// 216 against 214 us at 2^27); (maximum, count) at 2^27 with pieces of 1
+// then 3 / 1 then 4 / 2 then 3: 362.9 / 363.3 / 363.6 against 364.5-365.3.
+template <class Op> struct FirstPieces { static constexpr int first = 1, next = 3; };
+template <class B> struct FirstPieces<OpSeg<B>> { static constexpr int first = 0, next = 0; };
 
 // LDS chunk slot of chunk c: one chunk of padding after every R, which keeps
 // both orders of access free of bank conflicts.
@@ -1626,10 +1628,10 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
         return;
     }
     bool exhausted = false;
-    constexpr bool PIECES = FirstPieces<Op>::value && !ReloadAfterWait<Op>::value;
+    constexpr bool PIECES = FirstPieces<Op>::first > 0 && !ReloadAfterWait<Op>::value;
     if (w == 0) {
         if constexpr (PIECES)
-            exhausted = take_first_pieces<kPipeTiles, 1, 3>(p, &s_ids);
+            exhausted = take_first_pieces<kPipeTiles, FirstPieces<Op>::first, FirstPieces<Op>::next>(p, &s_ids);
         else
             exhausted = take_first_batch<kPipeTiles>(p, &s_ids);
     }
