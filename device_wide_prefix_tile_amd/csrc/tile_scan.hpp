@@ -998,30 +998,6 @@ __device__ __forceinline__ void retire_workgroup(const ScanParams& p)
     }
 }
 
-// Wavefront 0 of a data workgroup takes its first NT tile numbers one round
-// trip after another, so that they interleave with the other workgroups'
-// requests (about one grid apart, like a round-robin deal).  Taking them in
-// one go would hand a workgroup consecutive tiles, and the total of its last
-// one -- published only after the prefix of its first -- would then hold up
-// every later tile: measured, a serial chain seven times slower.  Returns
-// true once a number past the last tile came back.
-template <int NT>
-__device__ __forceinline__ bool take_first_ids(const ScanParams& p, TileIdRing* ids)
-{
-    bool exhausted = false;
-#pragma unroll
-    for (int q = 0; q < NT; ++q) {
-        uint32_t id = p.num_tiles;
-        if (!exhausted) {
-            if (lane_id() == 0)
-                id = __hip_atomic_fetch_add(pipe_counter(p, kCtrTiles), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            id = (uint32_t)__builtin_amdgcn_readfirstlane((int)id);
-            exhausted = id >= p.num_tiles;
-        }
-        if (lane_id() == 0) put_id(ids, (uint32_t)q, id);
-    }
-    return exhausted;
-}
 
 // The scan kernels' start: the first NT numbers as one consecutive batch,
 // with a single atomic (every lower number is then held by a running
@@ -1062,6 +1038,7 @@ __device__ __forceinline__ bool take_first_batch(const ScanParams& p, TileIdRing
 template <int NT, int NA, int NB>
 __device__ __forceinline__ bool take_first_pieces(const ScanParams& p, TileIdRing* ids)
 {
+    static_assert(NA >= 1 && NB >= 1, "pieces of at least one number");
     bool ex = false;
 #pragma unroll
     for (int q = 0; q < NT;) {
@@ -1803,7 +1780,15 @@ __global__ __launch_bounds__(BLOCK) void compact_persistent(ScanParams p)
         return;
     }
     bool exhausted = false;
-    if (w == 0) exhausted = take_first_ids<kPipeTiles>(p, &s_ids);
+    // first tile numbers in pieces of 1, WAIT - 1 and 1 (take_first_pieces):
+    // the totals of stages 0 .. WAIT - 1 go out before the first wait for a
+    // prefix, the newest stage's only after it, so the newest stage must be a
+    // piece of its own -- one that shares a piece with an earlier stage puts
+    // its consecutive numbers behind that stage's prefix: 2^28 pieces of 1 + 3
+    // or 2 + 2 270 us, 1 + 2 + 1 257.0-257.5, 2 + 1 + 1 258.8, single numbers
+    // one round trip apart 259.7-260.1.
+    static_assert(kPipeWait >= 2, "pieces of 1, WAIT - 1 and 1");
+    if (w == 0) exhausted = take_first_pieces<kPipeTiles, 1, kPipeWait - 1>(p, &s_ids);
     if (w == ND) {
         fetch_prefixes<Cnt>(p, &s_ids, s_slot);
         return;
