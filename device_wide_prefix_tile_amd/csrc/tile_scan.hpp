@@ -1152,6 +1152,18 @@ template <> struct UseBlocked<OpMat3> { static constexpr bool value = true; };  
 template <class Op> struct FirstPieces { static constexpr int first = 1, next = 3; };
 template <class B> struct FirstPieces<OpSeg<B>> { static constexpr int first = 0, next = 0; };
 
+// Whether the persistent kernel tells the compiler that the wavefront index
+// is the same in every lane (readfirstlane): the tile bookkeeping derived
+// from it then lives in scalar registers.  Per operator, because the
+// changed schedule helps some and costs others (timing harness, µs, without
+// / with): segmented add 2^27 214.0 / 204.4 (spilled bytes per lane 48 / 8),
+// 2x2 matrices 2^26 411.2 / 408.6; float32 add 2^28 331.2 / 350.0, int32 add
+// 330.6 / 345.4, 3x3 matrices 2^25 966 / 1030, compaction 256.2 / 259.2;
+// affine and (maximum, count) equal.
+template <class Op> struct UniformWaveIndex { static constexpr bool value = false; };
+template <class B> struct UniformWaveIndex<OpSeg<B>> { static constexpr bool value = true; };
+template <> struct UniformWaveIndex<OpMat2> { static constexpr bool value = true; };
+
 // LDS chunk slot of chunk c: one chunk of padding after every R, which keeps
 // both orders of access free of bank conflicts.
 template <int R>
@@ -1594,7 +1606,8 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     __shared__ u32x4 s_tr[BLK ? ND : 1][BLK ? tr_slots<R * G::K>() : 1];
     __shared__ uint32_t s_trh[BLKH ? ND : 1][BLKH ? tr_slots<R>() : 1];
     const int lane = lane_id();
-    const int w = threadIdx.x >> 6;
+    const int w = UniformWaveIndex<Op>::value ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6))
+                                               : (int)(threadIdx.x >> 6);
     u32x4* tr = BLK ? s_tr[w < ND ? w : 0] : nullptr;
     uint32_t* trh = BLKH ? s_trh[w < ND ? w : 0] : nullptr;
     if (start_workgroup(p, s_slot, &s_ids, &s_role) == 0) {
