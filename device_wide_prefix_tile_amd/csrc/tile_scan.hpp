@@ -410,7 +410,12 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_kernel(ScanParams p)
     __shared__ uint32_t s_tile;
 
     const int lane = lane_id();
-    const int w = threadIdx.x >> 6;
+    // one tile per workgroup: the wavefront index through readfirstlane (the
+    // compiler then keeps what derives from it in scalar registers; back to
+    // back at 2^20, same-box A/B: segmented add 8.6 -> 8.3 us, affine 10.3
+    // -> 9.9, int32 add within 0.2 either way; compaction's one-tile kernel
+    // gained nothing); the single workgroup keeps the plain index
+    const int w = SINGLE ? (int)(threadIdx.x >> 6) : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const V ident = Op::identity();
 
     if constexpr (SINGLE) {
