@@ -626,11 +626,16 @@ void one_tile_workgroup(Launch& Lc, unsigned seed)
                 publish(m, m.excl, (size_t)g, P.op, combine(P.op, acc, h.total), kAggregate);
             }
             Val gacc = identity(P.op);
-            for (int64_t top = g - 1; top >= 0; top -= 64) {
-                Val wv;
-                const int rr = fold_window(m, P, m.excl, top, 0, wv, polls);
-                gacc = combine(P.op, wv, gacc);
-                if (rr != kWinNone) break;
+            if (g == 1) {
+                // the second group folds the first group's 64 tile words
+                (void)fold_window(m, P, m.agg, 63, 0, gacc, polls);
+            } else {
+                for (int64_t top = g - 1; top >= 0; top -= 64) {
+                    Val wv;
+                    const int rr = fold_window(m, P, m.excl, top, 0, wv, polls);
+                    gacc = combine(P.op, wv, gacc);
+                    if (rr != kWinNone) break;
+                }
             }
             acc = combine(P.op, gacc, acc);
         }

@@ -79,9 +79,10 @@ def test_epoch_wrap(model):
 
 @pytest.mark.parametrize("op", [0, 1])
 def test_one_tile_kernel_two_level_lookback(model, op):
-    # 300 tiles: within five groups; 4200 tiles: more than 64 groups, so the walk over
-    # the groups takes a second window
-    for seed, tiles in ((1, 300), (2, 300), (3, 4200)):
+    # 100 tiles: the second group folds the first group's tile words; 300 tiles: within
+    # five groups; 4200 tiles: more than 64 groups, so the walk over the groups takes a
+    # second window
+    for seed, tiles in ((4, 100), (1, 300), (2, 300), (3, 4200)):
         rc, f, err = run(model["plain"], kernel=1, op=op, tiles=tiles, seed=seed, launches=2,
                          delay=200 if tiles < 1000 else 20, timeout=300)
         assert rc == 0 and f["ok"] == "1", (f, err[-1000:])
