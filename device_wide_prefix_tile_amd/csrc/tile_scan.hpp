@@ -1294,13 +1294,17 @@ __device__ __forceinline__ typename Op::value_t reduce_blocked(uint64_t wave_bas
 // Blocked-layout operators whose tile stores take the buffer-descriptor path
 // with the streaming + sc1 policy (as apply_store).  Measured per operator,
 // identical outputs: affine 2^26 187.5 -> 183.8 us, 3x3 matrices 2^24
-// 528.6 -> 505.1 us.  The others keep the plain streaming hint: with the
-// descriptor they spill more at the 128-VGPR limit and were 9-19% slower
-// (segmented, (maximum, count), 2x2 matrices; segmented again with its
-// one-pass tile scan: 214.5 -> 219.5 us at 2^27).
+// 528.6 -> 505.1 us; once the tile bookkeeping of the 512-thread kernels sat
+// in scalar registers (2x2: UniformWaveIndex), (maximum, count) 2^27
+// 362.5 -> 355.4 and 2x2 matrices 2^26 409.0 -> 400.0 (timing harness).
+// Segmented scans keep the plain streaming hint: 204.4 -> 212.0 us at 2^27
+// with the descriptor (earlier, when the kernels still spilled at the
+// 128-VGPR limit, all three were 9-19% slower with it).
 template <class Op> struct BlockedStorePolicy { static constexpr bool value = false; };
 template <> struct BlockedStorePolicy<OpAffine> { static constexpr bool value = true; };
 template <> struct BlockedStorePolicy<OpMat3> { static constexpr bool value = true; };
+template <> struct BlockedStorePolicy<OpMaxCount> { static constexpr bool value = true; };
+template <> struct BlockedStorePolicy<OpMat2> { static constexpr bool value = true; };
 
 // Elements wider than 16 bytes: a wavefront's share in round order, chunk c
 // of this lane being chunk c * 64 + lane of the share (see issue_loads),
