@@ -141,7 +141,7 @@ WORKLOADS = [
      lambda n, kept: 72 * n),
     ("CSR row counts, 2^27 sorted COO row indices (indices read once)", "csr_count_kernel", 1 << 27,
      lambda n, kept: 4 * n),
-    ("histogram counts, 2^27 uniform indices over 256 bins (indices read once)", "csr_count_lds_kernel", 1 << 27,
+    ("histogram counts, 2^27 uniform indices over 256 bins (indices read once)", "csr_count_small_kernel", 1 << 27,
      lambda n, kept: 4 * n),
     ("radix split histogram pass, 2^28 uint32 keys (keys read once)", "radix_hist_kernel", 1 << 28,
      lambda n, kept: 4 * n),

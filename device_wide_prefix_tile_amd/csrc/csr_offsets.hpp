@@ -3,8 +3,9 @@
 // of the uses of a prefix sum listed in the introduction of
 // "CUDA编程并行前缀和扫描详解"; the row pointer array has N + 1 entries
 // ("UIUC ECE 408 应用并行编程", L09).  Two steps: count the entries of every
-// row into row_ptr (csr_count_kernel, or csr_count_lds_kernel for few rows,
-// after row_ptr is zeroed), then an exclusive add scan of the n_rows + 1
+// row into row_ptr (csr_count_kernel, csr_count_lds_kernel for up to 16384
+// rows, csr_count_small_kernel for up to 1023 rows and 16-byte aligned
+// indices, after row_ptr is zeroed), then an exclusive add scan of the n_rows + 1
 // counts in place (the library's scan).
 #pragma once
 
@@ -88,6 +89,59 @@ __global__ __launch_bounds__(kCsrLdsBlock) void csr_count_lds_kernel(const uint3
     __syncthreads();
     for (uint32_t i = threadIdx.x; i < n_rows; i += kCsrLdsBlock) {
         const uint32_t c = s_cnt[i];
+        if (c) __hip_atomic_fetch_add(&counts[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Up to kCsrSmallBins rows (a histogram of few bins), indices 16-byte
+// aligned: no run detection, every index is counted with one LDS add into
+// one of kCsrCopies copies of the counts (lane l into copy l mod kCsrCopies,
+// so that at most four lanes of an instruction ever share a word, even when
+// every index names the same bin), four indices per lane and 16-byte load.
+// The workgroups take 16-byte chunks in grid order, so that at any moment
+// the chip reads one contiguous stretch of the indices.  At the end each
+// workgroup folds its copies and adds its nonzero counts to memory.
+constexpr uint32_t kCsrSmallBins = 1023;  // 64 KiB of counts in all
+constexpr int kCsrCopies = 16;
+constexpr int kCsrSmallUnroll = 2;  // 16-byte loads in flight per lane (1 or 3 are slower)
+
+__global__ __launch_bounds__(kCsrLdsBlock) void csr_count_small_kernel(const uint32_t* __restrict__ rows, uint64_t nnz,
+                                                                       uint32_t n_rows, uint32_t* counts)
+{
+    extern __shared__ uint32_t s_cnt[];  // kCsrCopies rows of n_rows + 1 words
+    const uint32_t stride = n_rows + 1;  // copies start in different banks
+    for (uint32_t i = threadIdx.x; i < kCsrCopies * stride; i += kCsrLdsBlock) s_cnt[i] = 0u;
+    __syncthreads();
+    uint32_t* my = s_cnt + (lane_id() % kCsrCopies) * stride;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(rows);
+    const uint64_t n4 = nnz / 4;
+    const uint64_t step = (uint64_t)gridDim.x * kCsrLdsBlock;
+    for (uint64_t c = blockIdx.x * (uint64_t)kCsrLdsBlock + threadIdx.x; c < n4; c += step * kCsrSmallUnroll) {
+        u32x4_t q[kCsrSmallUnroll];
+#pragma unroll
+        for (int u = 0; u < kCsrSmallUnroll; ++u) {
+            const uint64_t j = c + (uint64_t)u * step;
+            q[u] = j < n4 ? __builtin_nontemporal_load(src + j) : u32x4_t{~0u, ~0u, ~0u, ~0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kCsrSmallUnroll; ++u) {
+            if (q[u].x < n_rows) atomicAdd(my + q[u].x, 1u);
+            if (q[u].y < n_rows) atomicAdd(my + q[u].y, 1u);
+            if (q[u].z < n_rows) atomicAdd(my + q[u].z, 1u);
+            if (q[u].w < n_rows) atomicAdd(my + q[u].w, 1u);
+        }
+    }
+    // the last nnz mod 4 indices
+    if (blockIdx.x == 0 && threadIdx.x < (uint32_t)(nnz % 4)) {
+        const uint32_t r = rows[n4 * 4 + threadIdx.x];
+        if (r < n_rows) atomicAdd(my + r, 1u);
+    }
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < n_rows; i += kCsrLdsBlock) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < kCsrCopies; ++k) c += s_cnt[k * stride + i];
         if (c) __hip_atomic_fetch_add(&counts[i], c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }

@@ -634,13 +634,19 @@ scan_status_t csr_row_offsets(const uint32_t* row_idx, size_t nnz, uint32_t n_ro
         hipLaunchKernelGGL(zero_u32_kernel, dim3(zgrid), dim3(kCsrBlock), 0, s, row_ptr, (uint64_t)np);
         if (nnz > 0) {
             const size_t chunks = (nnz + 64 * kCsrSteps - 1) / (64 * kCsrSteps);  // one per wavefront
-            if (n_rows <= kCsrLdsBins) {
+            int cus = 1;
+            {
+                std::lock_guard<std::mutex> lock(g_mu);
+                cus = device_cus();
+            }
+            if (n_rows <= kCsrSmallBins && is_aligned(row_idx, 16)) {
+                // one workgroup per CU, every index counted in LDS
+                const size_t c4 = (nnz / 4 + kCsrLdsBlock - 1) / kCsrLdsBlock;
+                const unsigned grid = (unsigned)std::max<size_t>(1, std::min<size_t>(c4, (size_t)cus));
+                hipLaunchKernelGGL(csr_count_small_kernel, dim3(grid), dim3(kCsrLdsBlock),
+                                   (size_t)kCsrCopies * (n_rows + 1) * 4, s, row_idx, (uint64_t)nnz, n_rows, row_ptr);
+            } else if (n_rows <= kCsrLdsBins) {
                 // at most one workgroup per CU: each adds its n_rows counts to memory once
-                int cus = 1;
-                {
-                    std::lock_guard<std::mutex> lock(g_mu);
-                    cus = device_cus();
-                }
                 const unsigned grid = (unsigned)std::min<size_t>((chunks + kCsrLdsBlock / 64 - 1) / (kCsrLdsBlock / 64),
                                                                  (size_t)cus);
                 hipLaunchKernelGGL(csr_count_lds_kernel, dim3(grid), dim3(kCsrLdsBlock), (size_t)n_rows * 4, s,

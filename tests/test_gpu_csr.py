@@ -41,16 +41,32 @@ def test_unsorted(n_rows, nnz):
     check(rows, n_rows, "unsorted n_rows=%d nnz=%d" % (n_rows, nnz))
 
 
-@pytest.mark.parametrize("n_rows", [1, 2, 16, 256, 4096, 16383, 16384, 16385])
+@pytest.mark.parametrize("n_rows", [1, 2, 16, 256, 1023, 1024, 4096, 16383, 16384, 16385])
 def test_few_bins(n_rows):
-    """Histogram offsets of few bins (at most 16384 take the per-workgroup LDS counts):
-    uniform bin indices, sorted ones, and a skewed mix with most entries in one bin."""
+    """Histogram offsets of few bins (up to 1023 bins every index is counted in LDS, up
+    to 16384 runs are, each workgroup with its own counts): uniform bin indices, sorted
+    ones, and a skewed mix with most entries in one bin."""
     nnz = (1 << 22) + 77
     rows = (si.uint32_full(950 + n_rows % 83, nnz) % n_rows).astype(np.uint32)
     check(rows, n_rows, "uniform bins n_rows=%d" % n_rows)
     check(np.sort(rows), n_rows, "sorted bins n_rows=%d" % n_rows)
     skew = np.where(si.uint32_full(960, nnz) % 10 == 0, rows, np.uint32(n_rows - 1)).astype(np.uint32)
     check(skew, n_rows, "skewed bins n_rows=%d" % n_rows)
+
+
+@pytest.mark.parametrize("nnz", [1, 2, 3, 4, 5, 4099, 1 << 20])
+def test_few_bins_tails_and_alignment(nnz):
+    """Counts of few bins from 16-byte loads: index counts that are not a multiple of
+    four, and indices that start 4, 8 or 12 bytes past a 16-byte boundary (read one
+    index at a time instead); indices past the last bin are not counted."""
+    rows = (si.uint32_full(970 + nnz % 61, nnz + 3) % 300).astype(np.uint32)
+    ref_all = {}
+    dev = to_dev(rows)
+    for off in range(4):
+        part = rows[off:off + nnz]
+        ref_all[off] = oracle.csr_offsets(part, 257)
+        got = from_dev(dw.csr_row_offsets(dev[off:off + nnz], 257))
+        assert_equal(got, ref_all[off], "nnz=%d starting %d bytes in" % (nnz, 4 * off))
 
 
 def test_few_bins_full_size():
