@@ -1382,6 +1382,28 @@ __device__ __forceinline__ void store_blocked_tile(const ScanParams& p, uint64_t
     }
 }
 
+// Operators whose combine is exactly associative and whose carry is a value
+// of the same type (integer arithmetic mod 2^32, comparisons): the lane's
+// running value can start from the prefix, so each output is one combine
+// instead of a combine and an apply -- the same words, as
+// carry (+) (x_0 (+) .. (+) x_i) == (..(carry (+) x_0) (+) ..) (+) x_i holds
+// exactly for them (not for float add, whose carry is a double).
+template <class Op> struct FoldCarry { static constexpr bool value = false; };
+template <> struct FoldCarry<OpAffine> { static constexpr bool value = true; };
+template <> struct FoldCarry<OpMaxCount> { static constexpr bool value = true; };
+template <> struct FoldCarry<OpMat2> { static constexpr bool value = true; };
+template <> struct FoldCarry<OpMat3> { static constexpr bool value = true; };
+
+// Blocked-layout operators that keep each waiting tile's lane prefix (from
+// the wavefront scan of its total) until the tile's prefix is in, so that the
+// scan after the wait is one serial pass with no second wavefront scan:
+// segmented pairs, and 2x2 matrices, whose pass then needs one combine per
+// element (FoldCarry).  Measured with identical outputs (same-box A/B, us):
+// 2x2 matrices 2^25 211.4 -> 209.1; affine maps 2^26 179.0 -> 179.9 and
+// (maximum, count) 2^27 356.5 -> 365.5, where the kept prefixes spill.
+template <class Op> struct KeepLanePrefix { static constexpr bool value = IsSeg<Op>::value; };
+template <> struct KeepLanePrefix<OpMat2> { static constexpr bool value = FoldCarry<OpMat2>::value; };
+
 // Scan of a tile held in blocked order, prefix applied, back to round order
 // through LDS, stored like apply_store.
 template <class Op, bool EXCL, int R, int VEC, bool KEPT = false>
@@ -1400,50 +1422,30 @@ __device__ __forceinline__ void scan_store_blocked(const ScanParams& p, uint64_t
     if constexpr (KEPT) {
         // the lane prefix was kept from the wavefront scan of the total: one
         // serial pass applies the prefix as it goes, with no array of in-lane
-        // prefixes held (segmented add at 2^27: 226.6 -> 215.0 us).  The other
-        // operators keep two passes: folding the lane twice instead was slower
-        // for (maximum, count) (437 -> 481 us at 2^27).
+        // prefixes held (segmented add at 2^27: 226.6 -> 215.0 us); for 2x2
+        // matrices the pass starts from the prefix (FoldCarry), one combine
+        // per element.  Affine maps and (maximum, count) keep two passes (see
+        // KeepLanePrefix).
         (void)have_lane_excl;
         const typename Op::prep_t pc =
             Op::prepare(Op::combine_carry(P, Op::to_carry(Op::combine(wave_prefix, lane_excl))));
+        constexpr bool FOLD = FoldCarry<Op>::value;
         V run = ident;
-        constexpr int K = VecShape<E>::K;
-        if constexpr (K > 1) {
-            // elements wider than 16 bytes (3x3 matrices): each round's results go
-            // to the LDS area as they are made, so that only one round of them is
-            // held in registers, then leave in round order
-            constexpr int C = R * K;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                E yr[VEC];
-#pragma unroll
-                for (int j = 0; j < VEC; ++j) {
-                    const V v = make_value<Op>(e[r][j], (hb[r] >> j) & 1u);
-                    if constexpr (EXCL) yr[j] = elem_of<Op>(Op::apply(pc, run));
-                    run = (r == 0 && j == 0) ? v : Op::combine(run, v);
-                    if constexpr (!EXCL) yr[j] = elem_of<Op>(Op::apply(pc, run));
-                }
-                u32x4 c4[K];
-                __builtin_memcpy(c4, yr, 16 * K);
-#pragma unroll
-                for (int k = 0; k < K; ++k) tr[tr_slot<C>(lane * C + r * K + k)] = c4[k];
-            }
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_wave_barrier();
-            u32x4 v[C];
-#pragma unroll
-            for (int c = 0; c < C; ++c) v[c] = tr[tr_slot<C>(c * 64 + lane)];
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_wave_barrier();
-            store_round_chunks<Op, R, VEC>(p, wave_base, vec, lane, v);
-            return;
-        }
+        if constexpr (FOLD) run = pc;
+        static_assert(VecShape<E>::K == 1, "wide elements take scan_store_parked");
         E y[R][VEC];
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
                 const V v = make_value<Op>(e[r][j], (hb[r] >> j) & 1u);
+                if constexpr (FOLD) {
+                    static_assert(!IsSeg<Op>::value, "segmented pairs apply their carry");
+                    if constexpr (EXCL) y[r][j] = elem_of<Op>(run);
+                    run = Op::combine(run, v);
+                    if constexpr (!EXCL) y[r][j] = elem_of<Op>(run);
+                    continue;
+                }
                 if constexpr (EXCL) {
                     V o = Op::apply(pc, run);
                     if constexpr (IsSeg<Op>::value)
@@ -1508,11 +1510,66 @@ __device__ __forceinline__ typename Op::value_t tile_wave_total(uint64_t wave_ba
     }
 }
 
+// The scan after the wait of persistent_reload_loop, read from the LDS area
+// where the tile is parked (blocked order: this lane's chunk c in slot
+// lane * C + c) one round of VEC elements at a time: each round's results
+// replace its chunks in place, then the area leaves in round order as in the
+// kept-prefix form of scan_store_blocked.  Only one round of elements and of
+// results is held in registers, not the whole tile.
+template <class Op, bool EXCL, int R, int VEC>
+__device__ __forceinline__ void scan_store_parked(const ScanParams& p, uint64_t wave_base, bool vec, int lane,
+                                                  u32x4* tr, typename Op::carry_t P, typename Op::value_t wave_prefix,
+                                                  typename Op::value_t lane_excl)
+{
+    using E = typename Op::elem_t;
+    using V = typename Op::value_t;
+    constexpr int K = VecShape<E>::K, C = R * K;
+    static_assert(!IsSeg<Op>::value && K > 1, "wide elements without head flags");
+    const typename Op::prep_t pc =
+        Op::prepare(Op::combine_carry(P, Op::to_carry(Op::combine(wave_prefix, lane_excl))));
+    constexpr bool FOLD = FoldCarry<Op>::value;
+    V run = Op::identity();
+    if constexpr (FOLD) run = pc;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        u32x4 c4[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) c4[k] = tr[tr_slot<C>(lane * C + r * K + k)];
+        E er[VEC], yr[VEC];
+        __builtin_memcpy(er, c4, 16 * K);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            const V v = make_value<Op>(er[j], 0u);
+            if constexpr (FOLD) {
+                if constexpr (EXCL) yr[j] = elem_of<Op>(run);
+                run = Op::combine(run, v);
+                if constexpr (!EXCL) yr[j] = elem_of<Op>(run);
+            } else {
+                if constexpr (EXCL) yr[j] = elem_of<Op>(Op::apply(pc, run));
+                run = (r == 0 && j == 0) ? v : Op::combine(run, v);
+                if constexpr (!EXCL) yr[j] = elem_of<Op>(Op::apply(pc, run));
+            }
+        }
+        __builtin_memcpy(c4, yr, 16 * K);
+#pragma unroll
+        for (int k = 0; k < K; ++k) tr[tr_slot<C>(lane * C + r * K + k)] = c4[k];
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+    u32x4 v[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) v[c] = tr[tr_slot<C>(c * 64 + lane)];
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+    store_round_chunks<Op, R, VEC>(p, wave_base, vec, lane, v);
+}
+
 // Elements wider than 16 bytes with one tile waiting (3x3 matrices): a
 // data wavefront holds only its newest tile in registers.  The waiting
 // tile's data stay in the wavefront's LDS transposition area from its
-// hand-over until its prefix is in, and are read back from there for the
-// scan -- instead of keeping a second tile in registers across the wait,
+// hand-over until its prefix is in, and are read back from there, one round
+// at a time, for the scan (scan_store_parked) -- instead of keeping a second
+// tile in registers across the wait,
 // which at 72 words per tile spilled.  The first two tiles' totals are both
 // published before any wait (the second one's first, so that the LDS area
 // then holds the first tile); the second tile is written back to the area in
@@ -1575,9 +1632,13 @@ __device__ __forceinline__ void persistent_reload_loop(const ScanParams& p, Slot
 #pragma unroll
         for (int q = 0; q < ND; ++q)
             if (q < w) wave_prefix = Op::combine(wave_prefix, slot->wave_total[q]);
-        reload_blocked<R, VEC, E>(tr, lane, e0);
-        scan_store_blocked<Op, EXCL, R, VEC, DWPT_RELOAD_KEEP>(p, t0.base, t0.vec, lane, tr, slot->prefix,
-                                                               wave_prefix, e0, h0, lx, DWPT_RELOAD_KEEP);
+        if constexpr (DWPT_RELOAD_KEEP) {
+            scan_store_parked<Op, EXCL, R, VEC>(p, t0.base, t0.vec, lane, tr, slot->prefix, wave_prefix, lx);
+        } else {
+            reload_blocked<R, VEC, E>(tr, lane, e0);
+            scan_store_blocked<Op, EXCL, R, VEC, DWPT_RELOAD_KEEP>(p, t0.base, t0.vec, lane, tr, slot->prefix,
+                                                                   wave_prefix, e0, h0, lx, DWPT_RELOAD_KEEP);
+        }
         t0 = t1;
         lx = lx1;  // the second tile's; every later tile's comes from its own hand-over
 #pragma unroll
@@ -1653,7 +1714,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     // extra registers cost more than the second wavefront scan: (maximum,
     // count) at 2^27 435 -> 682 us, 2x2 matrices at 2^26 473 -> 905, affine
     // unchanged)
-    constexpr bool KEEP = BLK && IsSeg<Op>::value;
+    constexpr bool KEEP = BLK && KeepLanePrefix<Op>::value;
     // 16-byte lane loads in the last, partial tile: for the round-order
     // operators only; in the blocked kernels the extra branch (and the same
     // one in their stores) moved the register allocation: (maximum, count) at
