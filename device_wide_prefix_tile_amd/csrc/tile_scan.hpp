@@ -1164,10 +1164,14 @@ template <class B> struct FirstPieces<OpSeg<B>> { static constexpr int first = 0
 // / with): segmented add 2^27 214.0 / 204.4 (spilled bytes per lane 48 / 8),
 // 2x2 matrices 2^26 411.2 / 408.6; float32 add 2^28 331.2 / 350.0, int32 add
 // 330.6 / 345.4, 3x3 matrices 2^25 966 / 1030, compaction 256.2 / 259.2;
-// affine and (maximum, count) equal.
+// affine and (maximum, count) equal by themselves (128 -> 119 and 246 -> 229
+// VGPRs), and the registers freed hold their kept lane prefixes
+// (KeepLanePrefix).
 template <class Op> struct UniformWaveIndex { static constexpr bool value = false; };
 template <class B> struct UniformWaveIndex<OpSeg<B>> { static constexpr bool value = true; };
 template <> struct UniformWaveIndex<OpMat2> { static constexpr bool value = true; };
+template <> struct UniformWaveIndex<OpAffine> { static constexpr bool value = true; };
+template <> struct UniformWaveIndex<OpMaxCount> { static constexpr bool value = true; };
 
 // LDS chunk slot of chunk c: one chunk of padding after every R, which keeps
 // both orders of access free of bank conflicts.
@@ -1397,12 +1401,16 @@ template <> struct FoldCarry<OpMat3> { static constexpr bool value = true; };
 // Blocked-layout operators that keep each waiting tile's lane prefix (from
 // the wavefront scan of its total) until the tile's prefix is in, so that the
 // scan after the wait is one serial pass with no second wavefront scan:
-// segmented pairs, and 2x2 matrices, whose pass then needs one combine per
-// element (FoldCarry).  Measured with identical outputs (same-box A/B, us):
-// 2x2 matrices 2^25 211.4 -> 209.1; affine maps 2^26 179.0 -> 179.9 and
-// (maximum, count) 2^27 356.5 -> 365.5, where the kept prefixes spill.
+// segmented pairs, and the FoldCarry operators, whose pass then needs one
+// combine per element.  Measured with identical outputs (same-box A/B, us):
+// 2x2 matrices 2^25 211.4 -> 209.1; affine maps 2^26 and (maximum, count)
+// 2^27 179.0 -> 177.6 and 356.3 -> 354.5 with their tile bookkeeping in
+// scalar registers (UniformWaveIndex), which makes room for the kept
+// prefixes (without it they spill: 179.9 and 365.5).
 template <class Op> struct KeepLanePrefix { static constexpr bool value = IsSeg<Op>::value; };
 template <> struct KeepLanePrefix<OpMat2> { static constexpr bool value = FoldCarry<OpMat2>::value; };
+template <> struct KeepLanePrefix<OpAffine> { static constexpr bool value = FoldCarry<OpAffine>::value; };
+template <> struct KeepLanePrefix<OpMaxCount> { static constexpr bool value = FoldCarry<OpMaxCount>::value; };
 
 // Scan of a tile held in blocked order, prefix applied, back to round order
 // through LDS, stored like apply_store.
