@@ -1733,11 +1733,11 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_persistent(ScanParams p)
     // prefix, stages 1 .. WAIT-1 have their totals out, the newest loads.
     E e[kPipeTiles][R][VEC];
     uint32_t h[kPipeTiles][R];
-    // segmented scans in the blocked layout keep each stage's lane prefix from
-    // the wavefront scan of its total (for the other blocked operators the
-    // extra registers cost more than the second wavefront scan: (maximum,
-    // count) at 2^27 435 -> 682 us, 2x2 matrices at 2^26 473 -> 905, affine
-    // unchanged)
+    // each stage's lane prefix from the wavefront scan of its total, kept
+    // across the wait by the operators that KeepLanePrefix names (before the
+    // one-pass scan from the prefix, FoldCarry, the extra registers cost more
+    // than the second wavefront scan: (maximum, count) at 2^27 435 -> 682 us,
+    // 2x2 matrices at 2^26 473 -> 905)
     constexpr bool KEEP = BLK && KeepLanePrefix<Op>::value;
     // 16-byte lane loads in the last, partial tile: for the round-order
     // operators only; in the blocked kernels the extra branch (and the same
