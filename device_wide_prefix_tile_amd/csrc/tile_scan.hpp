@@ -676,10 +676,13 @@ constexpr int kPipeSlots = 16;  // >= 2 * WAIT + 1 (see the ring note above)
 // float32 add 349.5 / 352 / 354.5 us, int32 exclusive add 346.8 / 349.5 /
 // 349, affine 190.2 / 191.6 / 197, compaction 332.5 / 334 / 334; segmented
 // scans 246.7 / 227.3 / 227; (maximum, count) 423 (64 and 128) / 421 (256)
-// and 2x2 matrices 254 (128) / 252 (256).
+// and 2x2 matrices 254 (128) / 252 (256).  Re-measured with the one-pass
+// scans after the wait (same-box A/B of library builds, us; 64 / 128 / 256 /
+// 512 tiles): (maximum, count) 2^27 355.8 / 348.4 / 354.0 / -, 2x2 matrices
+// 2^25 208.7 / 211.4 / 208.7 / 226.2; affine 2^26 177.2 / 180.0 / 191.4.
 template <class Op> struct ResolveSpan { static constexpr int value = 1; };
 template <class B> struct ResolveSpan<OpSeg<B>> { static constexpr int value = 2; };
-template <> struct ResolveSpan<OpMaxCount> { static constexpr int value = 4; };
+template <> struct ResolveSpan<OpMaxCount> { static constexpr int value = 2; };
 template <> struct ResolveSpan<OpMat2> { static constexpr int value = 4; };
 #ifndef DWPT_RELOAD36
 #define DWPT_RELOAD36 1
