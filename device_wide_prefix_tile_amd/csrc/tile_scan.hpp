@@ -679,7 +679,9 @@ constexpr int kPipeSlots = 16;  // >= 2 * WAIT + 1 (see the ring note above)
 // and 2x2 matrices 254 (128) / 252 (256).  Re-measured with the one-pass
 // scans after the wait (same-box A/B of library builds, us; 64 / 128 / 256 /
 // 512 tiles): (maximum, count) 2^27 355.8 / 348.4 / 354.0 / -, 2x2 matrices
-// 2^25 208.7 / 211.4 / 208.7 / 226.2; affine 2^26 177.2 / 180.0 / 191.4.
+// 2^25 208.7 / 211.4 / 208.7 / 226.2; affine 2^26 177.2 / 180.0 / 191.4;
+// segmented add 2^27 241.2 / 202.3 / 210.5; 3x3 matrices 2^24 464.3 / 448.2
+// / 498.4.
 template <class Op> struct ResolveSpan { static constexpr int value = 1; };
 template <class B> struct ResolveSpan<OpSeg<B>> { static constexpr int value = 2; };
 template <> struct ResolveSpan<OpMaxCount> { static constexpr int value = 2; };
