@@ -29,11 +29,14 @@ namespace {
 // elements); WAIT is the number of tiles per data wavefront that wait on
 // their prefix in the persistent kernel.  Each class takes the measured best
 // shape: (maximum, count) at 2^27 436 us with 1024 threads x 6 per lane, WAIT
-// 3, 365 us with 512 x 16, WAIT 4 (512 x 12/20 at WAIT 3-4: 367-399); 2x2
-// matrices at 2^26 474 -> 413 us with 512 x 8, WAIT 4 (512 x 6 or 12: 469
-// and more); affine and segmented scans were slower at 512 threads (affine
-// 354 against 347, segmented 248 against 214 at their best 512 shapes).
-// The 3x3 matrices still spill at their fastest measured shape.
+// 3, 365 us with 512 x 16, WAIT 4 (512 x 12/20 at WAIT 3-4: 367-399), and
+// since its one-pass scan after the wait 346.4 us with 512 x 16, WAIT 3
+// (WAIT 4 348.7, 20/3 350.0, 12/5 395.4; same-box A/B); 2x2 matrices at 2^26
+// 474 -> 413 us with 512 x 8, WAIT 4 (512 x 6 or 12: 469 and more; at 2^25
+// with the one-pass scan 8/4 208.7, 10/3 208.5, 8/3 225.0, 6/5 230.5);
+// affine and segmented scans were slower at 512 threads (affine 354 against
+// 347, segmented 248 against 214 at their best 512 shapes).  The 3x3
+// matrices still spill at their fastest measured shape.
 // Build-time switches, so that shapes can be compared by measurement.
 #ifndef DWPT_BLOCK
 #define DWPT_BLOCK 1024
@@ -57,7 +60,7 @@ namespace {
 #define DWPT_ITEMS_MC 16
 #endif
 #ifndef DWPT_WAIT_MC
-#define DWPT_WAIT_MC 4
+#define DWPT_WAIT_MC 3
 #endif
 #ifndef DWPT_ITEMS16           // 16-byte values (2x2 matrices)
 #define DWPT_ITEMS16 8

@@ -45,10 +45,12 @@ def run(binary, timeout=120, **kw):
 
 
 # (data waves, tiles waiting per wave, resolver span, operator 0 add / 1 affine): the
-# pipeline depths and resolver windows of the shipped classes -- plain scans 3/1,
-# segmented 2/2, compaction 4/1, (maximum, count) and 2x2 matrices 3/4 -- with
-# one-word and two-word carries
-SHIPPED = [(3, 3, 1, 1), (3, 3, 1, 0), (5, 2, 2, 1), (3, 4, 1, 0), (2, 3, 4, 1), (1, 2, 2, 0), (4, 1, 1, 1)]
+# pipeline depths and resolver windows (tiles waiting / tiles per lane of a window)
+# of the shipped classes -- plain scans and affine maps 3/1, segmented 2/2,
+# compaction 3/1, (maximum, count) 3/2, 2x2 matrices 4/4,
+# 3x3 matrices 1/2 -- with one-word and two-word carries
+SHIPPED = [(3, 3, 1, 1), (3, 3, 1, 0), (5, 2, 2, 1), (3, 4, 1, 0), (2, 3, 4, 1), (1, 2, 2, 0), (4, 1, 1, 1),
+           (2, 3, 2, 1), (3, 4, 4, 1), (2, 1, 2, 1)]
 
 
 @pytest.mark.parametrize("nd,wait,span,op", SHIPPED)
