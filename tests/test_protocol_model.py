@@ -3,8 +3,9 @@ look-back, run on the CPU (tests/protocol_model/pipeline_model.cpp: one thread p
 wavefront, random pauses at every step, workgroups starting late and in any order),
 also under ThreadSanitizer.
 
-The lecture warns that a single-kernel scan across blocks needs careful memory
-ordering and spinning, and that a race gives results that change from run to run
+The lecture points out that a scan whose blocks pass carries to each other inside
+one kernel depends on how their memory accesses are ordered and on blocks busy-waiting
+for one another, and that a race there shows up as results that differ between runs
 ([L7] concept 6 "层次化扫描（Hierarchical Scan）"; "常见陷阱与注意事项").  These tests
 run thousands of schedules the GPU cannot be made to show on demand and check, on
 every run, the outputs against a sequential scan, that no wait gave up, that the
