@@ -31,7 +31,7 @@ namespace {
 // shape: (maximum, count) at 2^27 436 us with 1024 threads x 6 per lane, WAIT
 // 3, 365 us with 512 x 16, WAIT 4 (512 x 12/20 at WAIT 3-4: 367-399), and
 // since its one-pass scan after the wait 346.4 us with 512 x 16, WAIT 3
-// (WAIT 4 348.7, 20/3 350.0, 12/5 395.4; same-box A/B); 2x2 matrices at 2^26
+// (WAIT 4 348.7, 20/3 350.0, 12/5 395.4; A/B on one machine); 2x2 matrices at 2^26
 // 474 -> 413 us with 512 x 8, WAIT 4 (512 x 6 or 12: 469 and more; at 2^25
 // with the one-pass scan 8/4 208.7, 10/3 208.5, 8/3 225.0, 6/5 230.5);
 // affine and segmented scans were slower at 512 threads (affine 354 against

@@ -412,7 +412,7 @@ __global__ __launch_bounds__(BLOCK) void tile_scan_kernel(ScanParams p)
     const int lane = lane_id();
     // one tile per workgroup: the wavefront index through readfirstlane (the
     // compiler then keeps what derives from it in scalar registers; back to
-    // back at 2^20, same-box A/B: segmented add 8.6 -> 8.3 us, affine 10.3
+    // back at 2^20, A/B on one machine: segmented add 8.6 -> 8.3 us, affine 10.3
     // -> 9.9, int32 add within 0.2 either way; compaction's one-tile kernel
     // gained nothing); the single workgroup keeps the plain index
     const int w = SINGLE ? (int)(threadIdx.x >> 6) : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -677,7 +677,7 @@ constexpr int kPipeSlots = 16;  // >= 2 * WAIT + 1 (see the ring note above)
 // 349, affine 190.2 / 191.6 / 197, compaction 332.5 / 334 / 334; segmented
 // scans 246.7 / 227.3 / 227; (maximum, count) 423 (64 and 128) / 421 (256)
 // and 2x2 matrices 254 (128) / 252 (256).  Re-measured with the one-pass
-// scans after the wait (same-box A/B of library builds, us; 64 / 128 / 256 /
+// scans after the wait (A/B of library builds on one machine, us; 64 / 128 / 256 /
 // 512 tiles): (maximum, count) 2^27 355.8 / 348.4 / 354.0 / -, 2x2 matrices
 // 2^25 208.7 / 211.4 / 208.7 / 226.2; affine 2^26 177.2 / 180.0 / 191.4;
 // segmented add 2^27 241.2 / 202.3 / 210.5; 3x3 matrices 2^24 464.3 / 448.2
@@ -1042,7 +1042,7 @@ __device__ __forceinline__ bool take_first_batch(const ScanParams& p, TileIdRing
 // is still held by a running workgroup.  Measured (timing harness, µs):
 // float32 / int32 add at 2^28, pieces (1, 3) 332.1 / 331.5 against one batch
 // 335.5 / 334.5, (2, 2) 332.8 / 332.4, (1, 2, 1) 334.0 / 333.2, (2, 1, 1)
-// 334.8 / 334.4, (1, 1, 1, 1) 336.0 / 335.2.  In the library, same box:
+// 334.8 / 334.4, (1, 1, 1, 1) 336.0 / 335.2.  In the library, on one machine:
 // float32 add 2^28 335.3 -> 331.5, affine 2^26 184.1 -> 178.5, 2x2 matrices
 // 2^25 219.7 -> 216.9 (which operators take pieces: FirstPieces).
 template <int NT, int NA, int NB>
@@ -1404,8 +1404,8 @@ template <> struct FoldCarry<OpMat2> { static constexpr bool value = true; };
 template <> struct FoldCarry<OpMat3> { static constexpr bool value = true; };
 // Segmented pairs over an exact integer operator: the running pair starts as
 // (no head, prefix); a head inside the lane then discards the prefix exactly
-// as applying it to the lane's fold would (segmented add at 2^27, same-box
-// A/B, identical outputs: 204.1 -> 201.7 us).
+// as applying it to the lane's fold would (segmented add at 2^27, A/B on one
+// machine, identical outputs: 204.1 -> 201.7 us).
 template <class B> struct FoldCarry<OpSeg<B>> {
     static constexpr bool value =
         std::is_same<typename B::prep_t, typename B::value_t>::value && std::is_integral<typename B::value_t>::value;
@@ -1415,7 +1415,7 @@ template <class B> struct FoldCarry<OpSeg<B>> {
 // the wavefront scan of its total) until the tile's prefix is in, so that the
 // scan after the wait is one serial pass with no second wavefront scan:
 // segmented pairs, and the FoldCarry operators, whose pass then needs one
-// combine per element.  Measured with identical outputs (same-box A/B, us):
+// combine per element.  Measured with identical outputs (A/B on one machine, us):
 // 2x2 matrices 2^25 211.4 -> 209.1; affine maps 2^26 and (maximum, count)
 // 2^27 179.0 -> 177.6 and 356.3 -> 354.5 with their tile bookkeeping in
 // scalar registers (UniformWaveIndex), which makes room for the kept
